@@ -1,0 +1,171 @@
+// The C ABI of libhk: host-side argument checks, workspace sizing and dispatch.
+// Every entry point validates on the host before enqueueing anything, launches only on
+// the caller's stream, allocates nothing and keeps no state between calls.
+#include "hk_internal.h"
+
+using namespace hk;
+
+namespace {
+
+inline hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+inline hk_status from_hip(hipError_t e) { return e == hipSuccess ? HK_OK : HK_ERR_HIP; }
+
+hk_status check_hash(const hk_hash *h) {
+  if (!h) return HK_ERR_INVALID_ARGUMENT;
+  if (h->dtype != HK_F32 && h->dtype != HK_BF16) return HK_ERR_UNSUPPORTED;
+  if (h->d != kHeadDim) return HK_ERR_UNSUPPORTED;
+  if (h->bits != 64 && h->bits != 128) return HK_ERR_UNSUPPORTED;
+  if (h->kind == HK_HASH_LSH) {
+    if (!h->R) return HK_ERR_INVALID_ARGUMENT;
+  } else if (h->kind == HK_HASH_MLP) {
+    if (h->hidden != kHidden) return HK_ERR_UNSUPPORTED;
+    if (!h->W1 || !h->W2) return HK_ERR_INVALID_ARGUMENT;
+  } else {
+    return HK_ERR_UNSUPPORTED;
+  }
+  return HK_OK;
+}
+
+hk_status check_retrieve(int bits, int B, int Hkv, int64_t cap, int64_t n_ctx, int n_sink,
+                         int n_local, int k) {
+  if (bits != 64 && bits != 128) return HK_ERR_UNSUPPORTED;
+  if (B < 0 || Hkv < 0 || cap < 0 || n_ctx < 0 || n_sink < 0 || n_local < 0 || k < 0)
+    return HK_ERR_INVALID_ARGUMENT;
+  if (n_ctx > cap) return HK_ERR_INVALID_ARGUMENT;
+  if (n_ctx > INT32_MAX) return HK_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hkv > 65535) return HK_ERR_UNSUPPORTED;
+  return HK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hk_strerror(hk_status s) {
+  switch (s) {
+    case HK_OK: return "success";
+    case HK_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case HK_ERR_UNSUPPORTED: return "unsupported shape, dtype or code width";
+    case HK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case HK_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+hk_status hk_encode_keys(const hk_hash *h, const void *k, int B, int Hkv, int64_t cap,
+                         int64_t t0, int64_t t1, uint32_t *codes, void *stream) {
+  hk_status s = check_hash(h);
+  if (s != HK_OK) return s;
+  if (B < 0 || Hkv < 0 || cap < 0 || t0 < 0 || t1 < t0 || t1 > cap) return HK_ERR_INVALID_ARGUMENT;
+  if ((int64_t)B * Hkv * (t1 - t0) == 0) return HK_OK;
+  if (!k || !codes) return HK_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_encode_keys(*h, k, B, Hkv, cap, t0, t1, codes, as_stream(stream)));
+}
+
+hk_status hk_encode_query(const hk_hash *h, const void *q, int B, int Hq, int Hkv,
+                          uint32_t *qcodes, void *stream) {
+  hk_status s = check_hash(h);
+  if (s != HK_OK) return s;
+  if (B < 0 || Hq < 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq < Hkv) return HK_ERR_INVALID_ARGUMENT;
+  if ((int64_t)B * Hkv == 0) return HK_OK;
+  if (!q || !qcodes) return HK_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_encode_query(*h, q, B, Hq, Hkv, qcodes, as_stream(stream)));
+}
+
+size_t hk_retrieve_topk_workspace(int bits, int B, int Hkv, int64_t n_ctx, int n_sink,
+                                  int n_local, int k) {
+  if (check_retrieve(bits, B, Hkv, n_ctx, n_ctx, n_sink, n_local, k) != HK_OK) return 0;
+  return plan_retrieve(bits, B, Hkv, n_ctx, n_sink, n_local, k).total;
+}
+
+hk_status hk_hamming_scan(const uint32_t *codes, const uint32_t *qcodes, int bits, int B,
+                          int Hkv, int64_t cap, int64_t n_ctx, int n_sink, int n_local,
+                          int k, void *ws, size_t ws_bytes, void *stream) {
+  hk_status s = check_retrieve(bits, B, Hkv, cap, n_ctx, n_sink, n_local, k);
+  if (s != HK_OK) return s;
+  const RetrievePlan p = plan_retrieve(bits, B, Hkv, n_ctx, n_sink, n_local, k);
+  if (p.BH == 0 || p.S == 0) return HK_OK;
+  if (!codes || !qcodes || !ws) return HK_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(launch_hamming_scan(p, codes, qcodes, cap, ws, as_stream(stream)));
+}
+
+hk_status hk_topk_select(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, int n_local,
+                         int k, int32_t *idx, int32_t *count, void *ws, size_t ws_bytes,
+                         void *stream) {
+  hk_status s = check_retrieve(bits, B, Hkv, n_ctx, n_ctx, n_sink, n_local, k);
+  if (s != HK_OK) return s;
+  const RetrievePlan p = plan_retrieve(bits, B, Hkv, n_ctx, n_sink, n_local, k);
+  if (p.BH == 0) return HK_OK;
+  if (!count || !ws || (p.keff > 0 && !idx)) return HK_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(launch_topk_select(p, k, idx, count, ws, as_stream(stream)));
+}
+
+hk_status hk_retrieve_topk(const uint32_t *codes, const uint32_t *qcodes, int bits, int B,
+                           int Hkv, int64_t cap, int64_t n_ctx, int n_sink, int n_local,
+                           int k, int32_t *idx, int32_t *count, void *ws, size_t ws_bytes,
+                           void *stream) {
+  hk_status s = check_retrieve(bits, B, Hkv, cap, n_ctx, n_sink, n_local, k);
+  if (s != HK_OK) return s;
+  const RetrievePlan p = plan_retrieve(bits, B, Hkv, n_ctx, n_sink, n_local, k);
+  if (p.BH == 0) return HK_OK;
+  if (!count || !ws || (p.keff > 0 && !idx)) return HK_ERR_INVALID_ARGUMENT;
+  if (p.S > 0 && (!codes || !qcodes)) return HK_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
+  hipError_t e = launch_hamming_scan(p, codes, qcodes, cap, ws, as_stream(stream));
+  if (e != hipSuccess) return HK_ERR_HIP;
+  return from_hip(launch_topk_select(p, k, idx, count, ws, as_stream(stream)));
+}
+
+hk_status hk_window_indices(int64_t n_ctx, int n_sink, int n_local, int32_t *idx,
+                            int32_t *n_out, void *stream) {
+  if (n_ctx < 0 || n_sink < 0 || n_local < 0 || !n_out) return HK_ERR_INVALID_ARGUMENT;
+  if (n_ctx > INT32_MAX) return HK_ERR_UNSUPPORTED;
+  const int64_t sinks = n_sink < n_ctx ? n_sink : n_ctx;
+  const int64_t local0 = (n_ctx - n_local) > n_sink ? (n_ctx - n_local) : n_sink;
+  const int64_t n = sinks + (n_ctx > local0 ? n_ctx - local0 : 0);
+  *n_out = (int32_t)n;
+  if (n == 0 || !idx) return HK_OK;   // idx == NULL: size query only
+  return from_hip(launch_window_indices(n_ctx, n_sink, n_local, idx, as_stream(stream)));
+}
+
+size_t hk_sparse_decode_workspace(int B, int Hq, int Hkv, int d, int max_count) {
+  if (B < 0 || Hq < 0 || Hkv <= 0 || max_count < 0 || d != kHeadDim) return 0;
+  return plan_decode(B, Hq, Hkv, max_count).total;
+}
+
+hk_status hk_sparse_decode(const void *q, const void *k, const void *v, int dtype, int B,
+                           int Hq, int Hkv, int d, int64_t cap, const int32_t *idx,
+                           int64_t idx_stride, const int32_t *count, int max_count,
+                           float scale, float *o, float *lse, void *ws, size_t ws_bytes,
+                           void *stream) {
+  if (dtype != HK_F32 && dtype != HK_BF16) return HK_ERR_UNSUPPORTED;
+  if (d != kHeadDim) return HK_ERR_UNSUPPORTED;
+  if (B < 0 || Hq < 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq < Hkv || cap < 0 || max_count < 0 ||
+      idx_stride < 0)
+    return HK_ERR_INVALID_ARGUMENT;
+  if (Hq / Hkv > kMaxGroup) return HK_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hkv > 65535) return HK_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq == 0) return HK_OK;
+  if (!q || !o || !lse) return HK_ERR_INVALID_ARGUMENT;
+  if (max_count > 0 && (!k || !v || !idx)) return HK_ERR_INVALID_ARGUMENT;
+  const DecodePlan p = plan_decode(B, Hq, Hkv, max_count);
+  if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
+  if (p.total > 0 && !ws) return HK_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_sparse_decode(p, q, k, v, dtype, B, Hq, Hkv, cap, idx, idx_stride,
+                                       count, max_count, scale, o, lse, ws,
+                                       as_stream(stream)));
+}
+
+hk_status hk_lse_merge(const float *o_parts, const float *lse_parts, int P, int64_t rows,
+                       int d, float *o, float *lse, void *stream) {
+  if (P < 1 || d < 1 || rows < 0) return HK_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return HK_OK;
+  if (!o_parts || !lse_parts || !o || !lse) return HK_ERR_INVALID_ARGUMENT;
+  if (rows > (int64_t)4 * INT32_MAX) return HK_ERR_UNSUPPORTED;
+  return from_hip(launch_lse_merge(o_parts, lse_parts, P, rows, d, o, lse, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Internal declarations shared by the HIP translation units of libhk.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hk.h"
+
+namespace hk {
+
+constexpr int kHeadDim = 128;
+constexpr int kHidden = 256;
+constexpr int kMaxGroup = 8;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- retrieval plan
+// Candidate tokens of each (b, KV head) are cut into S chunks of `ch` tokens; one
+// workgroup scans one chunk.  The workspace holds
+//   stash  [BH][S*ch] uint8   per-token Hamming distance (255 past the last candidate)
+//   cum    [BH][S][NB] uint32 per-chunk inclusive cumulative distance histogram
+//   meta   [BH][S] int4      (#dist<T before chunk, #dist==T before chunk, #<T, #==T)
+//   params [BH] int2         (threshold T or -1, tie quota)
+struct RetrievePlan {
+  int W = 0, NB = 0, lpt = 0, ch = 0, S = 0, BH = 0, keff = 0;
+  int64_t lo = 0, C = 0;
+  size_t off_stash = 0, off_cum = 0, off_meta = 0, off_params = 0, total = 0;
+};
+RetrievePlan plan_retrieve(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, int n_local,
+                           int k);
+hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
+                               const uint32_t *qcodes, int64_t cap, void *ws,
+                               hipStream_t st);
+hipError_t launch_topk_select(const RetrievePlan &p, int k, int32_t *idx, int32_t *count,
+                              void *ws, hipStream_t st);
+hipError_t launch_window_indices(int64_t n_ctx, int n_sink, int n_local, int32_t *idx,
+                                 hipStream_t st);
+
+// ---------------------------------------------------------------- attention plan
+// The token list of each (b, KV head) is split into P slices; one workgroup gathers a
+// slice for all G query heads of the group.  With P > 1 the workspace holds normalised
+// partials o [P][B*Hq][d] and lse [P][B*Hq], merged by the log-sum-exp kernel.
+struct DecodePlan {
+  int P = 1, rows_per_split = 0, G = 1;
+  size_t off_o = 0, off_lse = 0, total = 0;
+};
+DecodePlan plan_decode(int B, int Hq, int Hkv, int max_count);
+hipError_t launch_sparse_decode(const DecodePlan &p, const void *q, const void *k,
+                                const void *v, int dtype, int B, int Hq, int Hkv,
+                                int64_t cap, const int32_t *idx, int64_t idx_stride,
+                                const int32_t *count, int max_count, float scale, float *o,
+                                float *lse, void *ws, hipStream_t st);
+hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int P,
+                            int64_t rows, int d, float *o, float *lse, hipStream_t st);
+
+// ---------------------------------------------------------------- encoders
+hipError_t launch_encode_keys(const hk_hash &h, const void *k, int B, int Hkv, int64_t cap,
+                              int64_t t0, int64_t t1, uint32_t *codes, hipStream_t st);
+hipError_t launch_encode_query(const hk_hash &h, const void *q, int B, int Hq, int Hkv,
+                               uint32_t *qcodes, hipStream_t st);
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t n = __shfl_up(v, o, 64);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Exclusive scan over a workgroup of NT threads (NT multiple of 64).  `lds` holds
+// NT/64 entries.  Returns this thread's exclusive prefix and sets `total`.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t *lds,
+                                                        uint32_t &total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t inc = wave_incl_scan_u32(v);
+  if (lane == 63) lds[wave] = inc;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    uint32_t x = lds[w];
+    off += (w < wave) ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();
+  total = tot;
+  return off + inc - v;
+}
+
+}  // namespace hk

@@ -1,0 +1,345 @@
+// Per-head top-k retrieval by Hamming distance between packed sign-bit codes.
+//
+// The query code of a (batch, KV head) is compared with every cached key code of that
+// head (HashEvict: Abstract; Spotlight Attention: Key results, "bitwise hashing
+// retrieval"), and the k nearest candidates are kept with ties broken by token index.
+//
+// Three kernels, all of them deterministic (no result depends on the order of atomics):
+//   hamming_scan   reads each candidate code once with 16-byte (or 8-byte) loads,
+//                  XOR + popcount against the query code, stores the distance as one
+//                  byte, and builds the chunk's distance histogram in LDS (one private
+//                  histogram per wavefront).  The chunk's cumulative histogram goes to
+//                  the workspace.  This kernel is bound by HBM bandwidth.
+//   topk_threshold one workgroup per head: sums the chunk histograms, finds the
+//                  threshold T = min{t : #(D <= t) >= k_eff} and the tie quota
+//                  k_eff - #(D < T), and an exclusive prefix over chunks of the counts
+//                  below and at T.  No sort is needed: the histogram select replaces it.
+//   topk_emit      re-reads the one-byte distances of a chunk and writes the selected
+//                  tokens (all with D < T, and the first `quota` with D == T in index
+//                  order) at their final positions, so the output is ascending.
+#include "hk_internal.h"
+
+namespace hk {
+namespace {
+
+constexpr int kScanThreads = 256;
+constexpr int kSelThreads = 1024;
+
+template <int W> struct CodeVec;
+template <> struct CodeVec<4> {
+  using T = uint4;
+  __device__ static T zero() { return make_uint4(0u, 0u, 0u, 0u); }
+  __device__ static uint32_t dist(const T &v, const uint32_t *q) {
+    return __builtin_popcount(v.x ^ q[0]) + __builtin_popcount(v.y ^ q[1]) +
+           __builtin_popcount(v.z ^ q[2]) + __builtin_popcount(v.w ^ q[3]);
+  }
+};
+template <> struct CodeVec<2> {
+  using T = uint2;
+  __device__ static T zero() { return make_uint2(0u, 0u); }
+  __device__ static uint32_t dist(const T &v, const uint32_t *q) {
+    return __builtin_popcount(v.x ^ q[0]) + __builtin_popcount(v.y ^ q[1]);
+  }
+};
+
+// grid (S, BH); chunk c of head bh covers candidate offsets [c*CH, (c+1)*CH).
+template <int W, int LPT>
+__global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
+    const uint32_t *__restrict__ codes, const uint32_t *__restrict__ qcodes, int64_t cap,
+    int64_t lo, int64_t C, int S, uint8_t *__restrict__ stash, uint32_t *__restrict__ cum) {
+  constexpr int NB = 32 * W + 1;
+  constexpr int NBP = (NB + 3) & ~3;
+  constexpr int CH = kScanThreads * LPT;
+  using CV = CodeVec<W>;
+  using V = typename CV::T;
+  __shared__ uint32_t hist[kScanThreads / 64][NBP];
+  __shared__ uint32_t tot[NBP];
+
+  const int c = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+
+  for (int i = t; i < (kScanThreads / 64) * NBP; i += kScanThreads) (&hist[0][0])[i] = 0u;
+
+  uint32_t q[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) q[w] = qcodes[(int64_t)bh * W + w];
+
+  const int64_t p0 = (int64_t)c * CH;
+  const V *base = reinterpret_cast<const V *>(codes + ((int64_t)bh * cap + lo) * W);
+  V v[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int64_t p = p0 + i * kScanThreads + t;
+    v[i] = (p < C) ? base[p] : CV::zero();
+  }
+  __syncthreads();
+
+  uint8_t *st = stash + (int64_t)bh * S * CH + p0;
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int64_t p = p0 + i * kScanThreads + t;
+    const uint32_t d = CV::dist(v[i], q);
+    if (p < C) {
+      atomicAdd(&hist[wave][d], 1u);
+      st[i * kScanThreads + t] = (uint8_t)d;
+    } else {
+      st[i * kScanThreads + t] = 0xFF;  // never selected: T <= 128
+    }
+  }
+  __syncthreads();
+  if (t < NB) {
+    uint32_t s = 0;
+#pragma unroll
+    for (int w = 0; w < kScanThreads / 64; ++w) s += hist[w][t];
+    tot[t] = s;
+  }
+  __syncthreads();
+  if (t < NB) {
+    uint32_t s = 0;
+    for (int j = 0; j <= t; ++j) s += tot[j];
+    cum[((int64_t)bh * S + c) * NB + t] = s;
+  }
+}
+
+// grid (BH); one workgroup per head.
+template <int NB>
+__global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
+    const uint32_t *__restrict__ cum, int S, int keff, int4 *__restrict__ meta,
+    int2 *__restrict__ params, int32_t *__restrict__ count) {
+  constexpr int NG = kSelThreads / NB;
+  __shared__ uint32_t part[NG][NB];
+  __shared__ uint32_t gcum[NB];
+  __shared__ uint32_t scan_lds[2][kSelThreads / 64];
+  __shared__ int sT, sQ;
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint32_t *cb = cum + (int64_t)bh * S * NB;
+
+  if (tid == 0) {
+    sT = -1;
+    sQ = 0;
+  }
+  if (keff > 0) {
+    for (int e = tid; e < NG * NB; e += kSelThreads) {
+      const int g = e / NB, tb = e - g * NB;
+      uint32_t s = 0;
+      for (int c = g; c < S; c += NG) s += cb[(int64_t)c * NB + tb];
+      part[g][tb] = s;
+    }
+    __syncthreads();
+    if (tid < NB) {
+      uint32_t s = 0;
+      for (int g = 0; g < NG; ++g) s += part[g][tid];
+      gcum[tid] = s;
+    }
+    __syncthreads();
+    if (tid < NB) {
+      const uint32_t below = tid ? gcum[tid - 1] : 0u;
+      if (gcum[tid] >= (uint32_t)keff && below < (uint32_t)keff) {
+        sT = tid;
+        sQ = keff - (int)below;
+      }
+    }
+  }
+  __syncthreads();
+  const int T = sT;
+  const int quota = sQ;
+  uint32_t carry_lt = 0, carry_eq = 0;
+  for (int base = 0; base < S; base += kSelThreads) {
+    const int c = base + tid;
+    uint32_t lt = 0, eq = 0;
+    if (c < S && T >= 0) {
+      const uint32_t a = T > 0 ? cb[(int64_t)c * NB + T - 1] : 0u;
+      const uint32_t b = cb[(int64_t)c * NB + T];
+      lt = a;
+      eq = b - a;
+    }
+    uint32_t tl, te;
+    const uint32_t lt_ex = block_excl_scan_u32<kSelThreads>(lt, scan_lds[0], tl);
+    const uint32_t eq_ex = block_excl_scan_u32<kSelThreads>(eq, scan_lds[1], te);
+    if (c < S)
+      meta[(int64_t)bh * S + c] =
+          make_int4((int)(carry_lt + lt_ex), (int)(carry_eq + eq_ex), (int)lt, (int)eq);
+    carry_lt += tl;
+    carry_eq += te;
+  }
+  if (tid == 0) {
+    params[bh] = make_int2(T, quota);
+    count[bh] = keff;
+  }
+}
+
+template <int LPT> struct ByteVec;
+template <> struct ByteVec<16> {
+  __device__ static void load(const uint8_t *p, uint32_t *w) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+};
+template <> struct ByteVec<8> {
+  __device__ static void load(const uint8_t *p, uint32_t *w) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+    w[0] = v.x; w[1] = v.y;
+  }
+};
+template <> struct ByteVec<4> {
+  __device__ static void load(const uint8_t *p, uint32_t *w) {
+    w[0] = *reinterpret_cast<const uint32_t *>(p);
+  }
+};
+
+// grid (S, BH); thread t owns the LPT consecutive candidates t*LPT .. t*LPT+LPT-1.
+template <int LPT>
+__global__ __launch_bounds__(kScanThreads) void topk_emit_kernel(
+    const uint8_t *__restrict__ stash, const int4 *__restrict__ meta,
+    const int2 *__restrict__ params, int S, int64_t lo, int k, int32_t *__restrict__ idx) {
+  constexpr int CH = kScanThreads * LPT;
+  __shared__ uint32_t scan_lds[kScanThreads / 64];
+  const int c = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int t = threadIdx.x;
+  const int2 pr = params[bh];
+  const int T = pr.x;
+  const int quota = pr.y;
+  if (T < 0) return;
+  const int4 mt = meta[(int64_t)bh * S + c];
+  const int lt_before = mt.x, eq_before = mt.y;
+  if (mt.z == 0 && (mt.w == 0 || eq_before >= quota)) return;  // nothing selected here
+
+  uint32_t w[LPT / 4];
+  ByteVec<LPT>::load(stash + ((int64_t)bh * S + c) * CH + (int64_t)t * LPT, w);
+  uint32_t lt = 0, eq = 0;
+#pragma unroll
+  for (int e = 0; e < LPT; ++e) {
+    const int d = (w[e >> 2] >> (8 * (e & 3))) & 0xFF;
+    lt += d < T;
+    eq += d == T;
+  }
+  uint32_t total;
+  const uint32_t ex = block_excl_scan_u32<kScanThreads>(lt | (eq << 16), scan_lds, total);
+  int lt_run = (int)(ex & 0xFFFFu);
+  int eq_run = (int)(ex >> 16);
+  int32_t *out = idx + (int64_t)bh * k;
+  const int64_t tok0 = lo + (int64_t)c * CH + (int64_t)t * LPT;
+#pragma unroll
+  for (int e = 0; e < LPT; ++e) {
+    const int d = (w[e >> 2] >> (8 * (e & 3))) & 0xFF;
+    if (d < T) {
+      out[lt_before + lt_run + min(eq_before + eq_run, quota)] = (int32_t)(tok0 + e);
+      ++lt_run;
+    } else if (d == T) {
+      if (eq_before + eq_run < quota)
+        out[lt_before + lt_run + eq_before + eq_run] = (int32_t)(tok0 + e);
+      ++eq_run;
+    }
+  }
+}
+
+__global__ void window_indices_kernel(int32_t n_sinks, int64_t local0, int32_t n,
+                                      int32_t *__restrict__ idx) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) idx[i] = (i < n_sinks) ? i : (int32_t)(local0 + (i - n_sinks));
+}
+
+template <int W, int LPT>
+void scan_launch(const RetrievePlan &p, const uint32_t *codes, const uint32_t *qcodes,
+                 int64_t cap, uint8_t *stash, uint32_t *cum, hipStream_t st) {
+  hipLaunchKernelGGL((hamming_scan_kernel<W, LPT>), dim3(p.S, p.BH), dim3(kScanThreads), 0,
+                     st, codes, qcodes, cap, p.lo, p.C, p.S, stash, cum);
+}
+
+}  // namespace
+
+RetrievePlan plan_retrieve(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, int n_local,
+                           int k) {
+  RetrievePlan p;
+  p.W = bits / 32;
+  p.NB = bits + 1;
+  p.BH = B * Hkv;
+  p.lo = n_sink;
+  const int64_t hi = n_ctx - n_local;
+  p.C = hi > p.lo ? hi - p.lo : 0;
+  p.keff = (int)(k < p.C ? k : p.C);
+  if (p.keff < 0) p.keff = 0;
+  // Chunk size: the largest of 16/8/4 codes per thread that still gives >= 1024
+  // workgroups, so that 256 CUs each see several.
+  const int64_t tok = (int64_t)p.BH * p.C;
+  p.lpt = 16;
+  if ((tok + 4095) / 4096 < 1024) p.lpt = 8;
+  if (p.lpt == 8 && (tok + 2047) / 2048 < 1024) p.lpt = 4;
+  p.ch = kScanThreads * p.lpt;
+  p.S = (int)((p.C + p.ch - 1) / p.ch);
+  size_t off = 0;
+  p.off_stash = off;
+  off = align_up(off + (size_t)p.BH * p.S * p.ch, 256);
+  p.off_cum = off;
+  off = align_up(off + (size_t)p.BH * p.S * p.NB * sizeof(uint32_t), 256);
+  p.off_meta = off;
+  off = align_up(off + (size_t)p.BH * p.S * sizeof(int4), 256);
+  p.off_params = off;
+  off = align_up(off + (size_t)p.BH * sizeof(int2), 256);
+  p.total = off;
+  return p;
+}
+
+hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
+                               const uint32_t *qcodes, int64_t cap, void *ws,
+                               hipStream_t st) {
+  if (p.BH == 0 || p.S == 0) return hipSuccess;
+  uint8_t *w8 = static_cast<uint8_t *>(ws);
+  uint8_t *stash = w8 + p.off_stash;
+  uint32_t *cum = reinterpret_cast<uint32_t *>(w8 + p.off_cum);
+  if (p.W == 4) {
+    if (p.lpt == 16) scan_launch<4, 16>(p, codes, qcodes, cap, stash, cum, st);
+    else if (p.lpt == 8) scan_launch<4, 8>(p, codes, qcodes, cap, stash, cum, st);
+    else scan_launch<4, 4>(p, codes, qcodes, cap, stash, cum, st);
+  } else {
+    if (p.lpt == 16) scan_launch<2, 16>(p, codes, qcodes, cap, stash, cum, st);
+    else if (p.lpt == 8) scan_launch<2, 8>(p, codes, qcodes, cap, stash, cum, st);
+    else scan_launch<2, 4>(p, codes, qcodes, cap, stash, cum, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_select(const RetrievePlan &p, int k, int32_t *idx, int32_t *count,
+                              void *ws, hipStream_t st) {
+  if (p.BH == 0) return hipSuccess;
+  uint8_t *w8 = static_cast<uint8_t *>(ws);
+  const uint8_t *stash = w8 + p.off_stash;
+  const uint32_t *cum = reinterpret_cast<const uint32_t *>(w8 + p.off_cum);
+  int4 *meta = reinterpret_cast<int4 *>(w8 + p.off_meta);
+  int2 *params = reinterpret_cast<int2 *>(w8 + p.off_params);
+  if (p.NB == 129)
+    hipLaunchKernelGGL((topk_threshold_kernel<129>), dim3(p.BH), dim3(kSelThreads), 0, st,
+                       cum, p.S, p.keff, meta, params, count);
+  else
+    hipLaunchKernelGGL((topk_threshold_kernel<65>), dim3(p.BH), dim3(kSelThreads), 0, st,
+                       cum, p.S, p.keff, meta, params, count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.S == 0 || p.keff == 0) return e;
+  if (p.lpt == 16)
+    hipLaunchKernelGGL((topk_emit_kernel<16>), dim3(p.S, p.BH), dim3(kScanThreads), 0, st,
+                       stash, meta, params, p.S, p.lo, k, idx);
+  else if (p.lpt == 8)
+    hipLaunchKernelGGL((topk_emit_kernel<8>), dim3(p.S, p.BH), dim3(kScanThreads), 0, st,
+                       stash, meta, params, p.S, p.lo, k, idx);
+  else
+    hipLaunchKernelGGL((topk_emit_kernel<4>), dim3(p.S, p.BH), dim3(kScanThreads), 0, st,
+                       stash, meta, params, p.S, p.lo, k, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_indices(int64_t n_ctx, int n_sink, int n_local, int32_t *idx,
+                                 hipStream_t st) {
+  const int64_t sinks = n_sink < n_ctx ? n_sink : n_ctx;
+  const int64_t local0 = (n_ctx - n_local) > n_sink ? (n_ctx - n_local) : n_sink;
+  const int64_t n = sinks + (n_ctx > local0 ? n_ctx - local0 : 0);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(window_indices_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     st, (int32_t)sinks, local0, (int32_t)n, idx);
+  return hipGetLastError();
+}
+
+}  // namespace hk

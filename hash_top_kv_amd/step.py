@@ -1,0 +1,69 @@
+"""One decode step of binary-hash retrieval attention over a resident KV cache.
+
+Sequences the C entry points with preallocated buffers (no allocation per step, so a
+step can be captured in a HIP graph):
+
+    hk_encode_query -> hk_retrieve_topk -> hk_sparse_decode (top-k list)
+                    -> hk_sparse_decode (sink + local window) -> hk_lse_merge
+
+Spotlight Attention (summary, Approach): query hashed, Hamming top-k over the cached
+key codes, attention over the selected tokens only.  RetrievalAttention (elamur
+summary: Summary; atlas summary: Approach): static window attended separately and
+merged by exact log-sum-exp rescaling.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import (Hash, encode_query, lse_merge, retrieve_topk_workspace, sparse_decode,
+               sparse_decode_workspace, window_indices, _check, _ptr, _stream, lib)
+
+
+class DecodeStep:
+    def __init__(self, K: torch.Tensor, V: torch.Tensor, codes: torch.Tensor, bits: int,
+                 n_ctx: int, n_sink: int, n_local: int, k: int, Hq: int,
+                 hash: Hash | None = None):
+        self.K, self.V, self.codes, self.bits, self.hash = K, V, codes, bits, hash
+        B, Hkv, cap, d = K.shape
+        self.B, self.Hkv, self.cap, self.d, self.Hq = B, Hkv, cap, d, Hq
+        self.n_ctx, self.n_sink, self.n_local, self.k = n_ctx, n_sink, n_local, k
+        dev = K.device
+        self.keff = max(0, min(k, n_ctx - n_sink - n_local))
+        self.idx = torch.zeros((B, Hkv, max(k, 1)), dtype=torch.int32, device=dev)
+        self.count = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+        self.win = window_indices(n_ctx, n_sink, n_local, dev)
+        self.n_win = int(self.win.numel())
+        self.ws_r = torch.empty(max(1, retrieve_topk_workspace(bits, B, Hkv, n_ctx, n_sink,
+                                                               n_local, k)),
+                                dtype=torch.uint8, device=dev)
+        wd = max(sparse_decode_workspace(B, Hq, Hkv, self.keff, d),
+                 sparse_decode_workspace(B, Hq, Hkv, self.n_win, d))
+        self.ws_d = torch.empty(max(1, wd), dtype=torch.uint8, device=dev)
+        self.o_parts = torch.empty((2, B, Hq, d), dtype=torch.float32, device=dev)
+        self.lse_parts = torch.empty((2, B, Hq), dtype=torch.float32, device=dev)
+        self.o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        self.qcodes = torch.empty((B, Hkv, bits // 32), dtype=torch.int32, device=dev)
+        self.scale = 1.0 / math.sqrt(d)
+
+    def retrieve(self, qcodes: torch.Tensor):
+        L = lib()
+        _check(L.hk_retrieve_topk(_ptr(self.codes), _ptr(qcodes), self.bits, self.B, self.Hkv,
+                                  self.cap, self.n_ctx, self.n_sink, self.n_local, self.k,
+                                  _ptr(self.idx), _ptr(self.count), _ptr(self.ws_r),
+                                  self.ws_r.numel(), _stream()), "hk_retrieve_topk")
+
+    def __call__(self, q: torch.Tensor, qcodes: torch.Tensor | None = None):
+        """Returns (o [B, Hq, d], lse [B, Hq]); with qcodes given the query is not hashed."""
+        if qcodes is None:
+            qcodes = encode_query(self.hash, q, self.Hkv, self.qcodes)
+        self.retrieve(qcodes)
+        sparse_decode(q, self.K, self.V, self.idx, self.keff, count=self.count,
+                      scale=self.scale, o=self.o_parts[0], lse=self.lse_parts[0], ws=self.ws_d)
+        if self.n_win == 0:
+            return self.o_parts[0], self.lse_parts[0]
+        sparse_decode(q, self.K, self.V, self.win, self.n_win, idx_stride=0, scale=self.scale,
+                      o=self.o_parts[1], lse=self.lse_parts[1], ws=self.ws_d)
+        return lse_merge(self.o_parts, self.lse_parts, self.o, self.lse)

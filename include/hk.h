@@ -1,0 +1,184 @@
+/*
+ * hk.h -- C ABI of the binary-hash KV-cache retrieval decode path for MI355X (gfx950).
+ *
+ * One decode step of binary-hash retrieval attention:
+ *   1. keys and the current query are hashed to packed sign-bit codes, by a Gaussian
+ *      random projection (HashEvict: Abstract, "binarized Gaussian projections") or by
+ *      the sign of a two-layer MLP (Spotlight Attention: Approach);
+ *   2. the cached key codes are compared with the query code by Hamming distance
+ *      (HashEvict: Abstract; Spotlight Attention: Key results, "bitwise hashing
+ *      retrieval");
+ *   3. the top-k tokens per head are kept (Spotlight Attention: summary, top-2%);
+ *   4. exact softmax attention runs over those tokens only, and over a static
+ *      sink + local window (RetrievalAttention, elamur summary: Summary);
+ *   5. the partial results are combined by exact log-sum-exp rescaling
+ *      (RetrievalAttention, atlas summary: Approach).
+ *
+ * Conventions shared by every call:
+ *  - Pointers named as device pointers are caller-owned device memory; the library
+ *    allocates no device memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call only
+ *    enqueues kernels on it and returns; nothing synchronises and nothing reads device
+ *    memory from the host.  Device faults surface at the caller's next synchronisation.
+ *  - Arguments are checked on the host before anything is enqueued.  A bad argument
+ *    returns HK_ERR_INVALID_ARGUMENT or HK_ERR_UNSUPPORTED and enqueues nothing.  A
+ *    failed launch returns HK_ERR_HIP.
+ *  - Head dimension d is 128.  Code widths are 64 or 128 bits, stored as bits/32
+ *    uint32 words per token: bit j is bit (j mod 32) of word j/32 (least significant
+ *    first), words in increasing order.  A bit is 1 iff its pre-sign value is > 0.
+ *  - GQA: query head h belongs to KV head h / G with G = Hq / Hkv (contiguous groups).
+ *  - Token indices are int32; contexts are limited to 2^31 - 1 tokens.
+ */
+#ifndef HK_H
+#define HK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hk_status {
+  HK_OK = 0,
+  HK_ERR_INVALID_ARGUMENT = 1,
+  HK_ERR_UNSUPPORTED = 2,
+  HK_ERR_WORKSPACE_TOO_SMALL = 3,
+  HK_ERR_HIP = 4
+} hk_status;
+
+typedef enum hk_dtype { HK_F32 = 0, HK_BF16 = 1 } hk_dtype;
+
+typedef enum hk_hash_kind { HK_HASH_LSH = 0, HK_HASH_MLP = 1 } hk_hash_kind;
+
+/* Hash parameters: a host struct that points at caller-owned device tensors.
+ * LSH  (HashEvict: Abstract): y = R x, R [bits][d] row-major, row j gives bit j.
+ * MLP  (Spotlight Attention: Approach): y = W2 rho(GELU(W1 x + b1)) + b2 with
+ *      W1 [hidden][d], W2 [bits][hidden] ([out][in], row-major), optional biases
+ *      b1 [hidden] and b2 [bits] (NULL = zero), GELU in its exact erf form, and rho the
+ *      rounding of the hidden activation to bf16 (nearest-even) when dtype is HK_BF16.
+ * All tensors have element type `dtype`, which is also the element type of the keys and
+ * queries the hash encodes.  d must be 128, bits 64 or 128, hidden 256 (MLP) or 0. */
+typedef struct hk_hash {
+  int32_t kind;    /* hk_hash_kind */
+  int32_t dtype;   /* hk_dtype */
+  int32_t d;
+  int32_t bits;
+  int32_t hidden;
+  const void *R;
+  const void *W1;
+  const void *b1;
+  const void *W2;
+  const void *b2;
+} hk_hash;
+
+/* Static string describing a status; never NULL. */
+const char *hk_strerror(hk_status s);
+
+/* Encode cached keys into codes (prefill: t0 = 0, t1 = n; append: t1 = t0 + 1).
+ * Spotlight Attention (Approach) hashes keys with the sign of an MLP; HashEvict
+ * (Abstract) with a binarized Gaussian projection kept in a GPU-resident structure.
+ *   k      device [B][Hkv][cap][d], element type h->dtype.
+ *   codes  device [B][Hkv][cap][bits/32] uint32; tokens t0 <= t < t1 of every (b, head)
+ *          are written, nothing else.
+ * Errors: t0 < 0, t1 < t0, t1 > cap, negative B/Hkv, NULL pointers -> INVALID_ARGUMENT;
+ * unsupported hash shape -> UNSUPPORTED.  t0 == t1 or B*Hkv == 0 enqueues nothing. */
+hk_status hk_encode_keys(const hk_hash *h, const void *k, int B, int Hkv, int64_t cap,
+                         int64_t t0, int64_t t1, uint32_t *codes, void *stream);
+
+/* Encode the query of one decode step, one code per KV head: the code of the mean of
+ * the G query vectors of the head's group (the mean ranks keys by the group's summed
+ * logit), computed in fp32 without rounding the mean.
+ *   q       device [B][Hq][d], element type h->dtype.
+ *   qcodes  device [B][Hkv][bits/32] uint32 (written).
+ * Errors: Hq % Hkv != 0, NULL pointers -> INVALID_ARGUMENT. */
+hk_status hk_encode_query(const hk_hash *h, const void *q, int B, int Hq, int Hkv,
+                          uint32_t *qcodes, void *stream);
+
+/* Workspace bytes needed by hk_retrieve_topk / hk_hamming_scan / hk_topk_select. */
+size_t hk_retrieve_topk_workspace(int bits, int B, int Hkv, int64_t n_ctx, int n_sink,
+                                  int n_local, int k);
+
+/* Per-head top-k retrieval by Hamming distance (HashEvict: Abstract; Spotlight
+ * Attention: Key results).  Candidates of every (b, head) are tokens
+ * n_sink <= t < n_ctx - n_local (sink and local tokens are attended separately);
+ * k_eff = min(k, max(0, n_ctx - n_sink - n_local)) of them are selected by
+ * (distance ascending, token index ascending), a unique set.
+ *   codes   device [B][Hkv][cap][bits/32]; qcodes device [B][Hkv][bits/32].
+ *   idx     device [B][Hkv][k] int32: the first k_eff entries of each row are the
+ *           selected tokens in ascending order; later entries are left untouched.
+ *   count   device [B][Hkv] int32, set to k_eff.
+ *   ws      device workspace of at least hk_retrieve_topk_workspace(...) bytes, 256-byte
+ *           aligned; its contents on entry do not matter.
+ * Errors: bits not 64/128 -> UNSUPPORTED; n_ctx > cap, negative sizes, NULL pointers ->
+ * INVALID_ARGUMENT; small ws -> WORKSPACE_TOO_SMALL. */
+hk_status hk_retrieve_topk(const uint32_t *codes, const uint32_t *qcodes, int bits, int B,
+                           int Hkv, int64_t cap, int64_t n_ctx, int n_sink, int n_local,
+                           int k, int32_t *idx, int32_t *count, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* The two halves of hk_retrieve_topk, for callers that time or overlap them
+ * separately; called in this order with the same arguments and workspace they produce
+ * exactly what hk_retrieve_topk produces.  hk_hamming_scan reads every candidate code
+ * once and leaves per-token distances and per-chunk distance histograms in ws;
+ * hk_topk_select derives the distance threshold and the tie quota from them and writes
+ * idx and count. */
+hk_status hk_hamming_scan(const uint32_t *codes, const uint32_t *qcodes, int bits, int B,
+                          int Hkv, int64_t cap, int64_t n_ctx, int n_sink, int n_local,
+                          int k, void *ws, size_t ws_bytes, void *stream);
+hk_status hk_topk_select(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, int n_local,
+                         int k, int32_t *idx, int32_t *count, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* Write the static window [0, min(s, n)) U [max(s, n - w), n) in ascending order
+ * (tokens kept by fixed patterns: RetrievalAttention, elamur summary: Summary).
+ *   idx    device int32 array of at least *n_out entries (written), or NULL to
+ *          only query the size (nothing is enqueued then).
+ *   n_out  host int32: receives the window size, computed on the host.
+ * Errors: negative sizes, NULL n_out -> INVALID_ARGUMENT. */
+hk_status hk_window_indices(int64_t n_ctx, int n_sink, int n_local, int32_t *idx,
+                            int32_t *n_out, void *stream);
+
+/* Workspace bytes needed by hk_sparse_decode. */
+size_t hk_sparse_decode_workspace(int B, int Hq, int Hkv, int d, int max_count);
+
+/* Exact softmax attention of every query head over its KV head's token list
+ * ("partial attention" over retrieved tokens: RetrievalAttention, elamur summary:
+ * Summary; Spotlight Attention: summary).  For query head h of batch b with KV head
+ * g = h / G: l_j = scale * q . K[b][g][j] over j in the list, o = sum softmax(l)_j V_j,
+ * lse = ln sum exp(l_j).  The K/V rows of a list are read once and shared by the G query
+ * heads of the group; accumulation is fp32.
+ *   q, k, v     device; q [B][Hq][d], k and v [B][Hkv][cap][d], element type dtype.
+ *   idx         device int32; list of (b, g) starts at idx + (b*Hkv + g) * idx_stride
+ *               (idx_stride 0 = one list shared by all heads); entries must be in
+ *               [0, cap).
+ *   count       device int32 [B][Hkv], entries clamped to [0, max_count]; NULL = every
+ *               list has max_count entries.
+ *   max_count   host upper bound of the list lengths (sizes the launch).
+ *   o, lse      device float [B][Hq][d] and [B][Hq] (written).  An empty list gives
+ *               o = 0 and lse = -inf.
+ *   ws          device workspace of hk_sparse_decode_workspace(...) bytes (split-K
+ *               partials), 256-byte aligned.
+ * Errors: d != 128 or G > 8 -> UNSUPPORTED; Hq % Hkv != 0, NULL pointers, negative
+ * sizes -> INVALID_ARGUMENT; small ws -> WORKSPACE_TOO_SMALL. */
+hk_status hk_sparse_decode(const void *q, const void *k, const void *v, int dtype, int B,
+                           int Hq, int Hkv, int d, int64_t cap, const int32_t *idx,
+                           int64_t idx_stride, const int32_t *count, int max_count,
+                           float scale, float *o, float *lse, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* Exact log-sum-exp merge of P partial attentions of disjoint token sets
+ * (RetrievalAttention, atlas summary: Approach):  m = max_p lse_p,
+ * o = sum_p e^(lse_p - m) o_p / sum_p e^(lse_p - m),  lse = m + ln sum_p e^(lse_p - m).
+ * Parts with lse = -inf are ignored; if all are, o = 0 and lse = -inf.
+ *   o_parts [P][rows][d], lse_parts [P][rows] device float; o [rows][d], lse [rows]
+ *   device float (written; may not alias the parts).
+ * Errors: P < 1, d < 1, rows < 0, NULL pointers -> INVALID_ARGUMENT. */
+hk_status hk_lse_merge(const float *o_parts, const float *lse_parts, int P, int64_t rows,
+                       int d, float *o, float *lse, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HK_H */

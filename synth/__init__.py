@@ -265,3 +265,21 @@ def describe(wl: Workload) -> dict:
             "d": wl.d, "dtype": wl.dtype, "k": wl.k, "n_sink": wl.n_sink,
             "n_local": wl.n_local,
             "hashes": [f"{h.kind}-{h.bits}" for h in wl.hashes] or ["given-128"]}
+
+
+def to_device(arr: np.ndarray, dtype: str, device="cuda"):
+    """Upload a generated array: float32 as is, bf16 bit patterns as torch.bfloat16,
+    uint32 codes as int32 (same bits)."""
+    import torch
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32)).to(device)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a.astype(np.float32, copy=False)).to(device)
+
+
+def hash_to_device(h: dict, device="cuda") -> dict:
+    """Hash parameter tensors of make_hash() on the device (keys R / W1 / W2)."""
+    return {k: to_device(h[k], h["dtype"], device) for k in ("R", "W1", "W2", "b1", "b2")
+            if h.get(k) is not None}

@@ -1,0 +1,104 @@
+"""The C ABI without a GPU: libhk.so loads, exports every function include/hk.h
+declares, and rejects bad arguments on the host before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hk.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hk_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def hk():
+    import hash_top_kv_amd
+    return hash_top_kv_amd
+
+
+def test_header_declares_the_five_calls():
+    names = _declared()
+    for n in ("hk_encode_keys", "hk_encode_query", "hk_retrieve_topk", "hk_sparse_decode",
+              "hk_lse_merge"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(hk):
+    L = ctypes.CDLL(hk.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(_declared()) <= set(hk._SIGNATURES), "binding lacks a declared call"
+
+
+def test_strerror_covers_every_status(hk):
+    msgs = {hk.strerror(s) for s in range(5)}
+    assert len(msgs) == 5 and "unknown status" not in msgs
+    assert hk.strerror(99) == "unknown status"
+
+
+def test_host_validation_without_gpu(hk):
+    L = hk.lib()
+    P = None
+    # unsupported code width, negative sizes, context beyond capacity
+    assert L.hk_retrieve_topk(P, P, 96, 1, 1, 10, 10, 0, 0, 3, P, P, P, 0, P) == hk.HK_ERR_UNSUPPORTED
+    assert L.hk_retrieve_topk(P, P, 128, -1, 1, 10, 10, 0, 0, 3, P, P, P, 0, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_retrieve_topk(P, P, 128, 1, 1, 10, 11, 0, 0, 3, P, P, P, 0, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_retrieve_topk(P, P, 128, 1, 1, 10, 10, 0, 0, -3, P, P, P, 0, P) == hk.HK_ERR_INVALID_ARGUMENT
+    # missing buffers, then a workspace that is too small (dummy non-null pointers)
+    assert L.hk_retrieve_topk(P, P, 128, 1, 1, 10, 10, 0, 0, 3, P, P, P, 0, P) == hk.HK_ERR_INVALID_ARGUMENT
+    dummy = ctypes.c_void_p(0x1000)
+    assert L.hk_retrieve_topk(dummy, dummy, 128, 1, 1, 10, 10, 0, 0, 3, dummy, dummy, dummy, 1, P) \
+        == hk.HK_ERR_WORKSPACE_TOO_SMALL
+    # empty problems are successful no-ops
+    assert L.hk_retrieve_topk(P, P, 128, 0, 8, 10, 10, 0, 0, 3, P, P, P, 0, P) == hk.HK_OK
+    # hashes
+    assert L.hk_encode_keys(None, P, 1, 1, 10, 0, 10, P, P) == hk.HK_ERR_INVALID_ARGUMENT
+    h = hk._Hash(hk.HK_HASH_LSH, hk.HK_BF16, 128, 96, 0, dummy, P, P, P, P)
+    assert L.hk_encode_keys(ctypes.byref(h), dummy, 1, 1, 10, 0, 10, dummy, P) == hk.HK_ERR_UNSUPPORTED
+    h = hk._Hash(hk.HK_HASH_MLP, hk.HK_BF16, 128, 128, 128, P, dummy, P, dummy, P)
+    assert L.hk_encode_keys(ctypes.byref(h), dummy, 1, 1, 10, 0, 10, dummy, P) == hk.HK_ERR_UNSUPPORTED
+    h = hk._Hash(hk.HK_HASH_LSH, hk.HK_BF16, 64, 128, 0, dummy, P, P, P, P)
+    assert L.hk_encode_keys(ctypes.byref(h), dummy, 1, 1, 10, 0, 10, dummy, P) == hk.HK_ERR_UNSUPPORTED
+    h = hk._Hash(hk.HK_HASH_LSH, hk.HK_BF16, 128, 128, 0, P, P, P, P, P)
+    assert L.hk_encode_keys(ctypes.byref(h), dummy, 1, 1, 10, 0, 10, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
+    h = hk._Hash(hk.HK_HASH_LSH, hk.HK_BF16, 128, 128, 0, dummy, P, P, P, P)
+    assert L.hk_encode_keys(ctypes.byref(h), dummy, 1, 1, 10, 5, 11, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_encode_keys(ctypes.byref(h), dummy, 1, 1, 10, 5, 4, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_encode_keys(ctypes.byref(h), dummy, 1, 1, 10, 5, 5, dummy, P) == hk.HK_OK
+    assert L.hk_encode_query(ctypes.byref(h), dummy, 1, 30, 4, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
+    # attention
+    f = ctypes.c_float(0.1)
+    assert L.hk_sparse_decode(dummy, dummy, dummy, hk.HK_BF16, 1, 36, 4, 128, 10, dummy, 4, P, 4, f,
+                              dummy, dummy, dummy, 1 << 30, P) == hk.HK_ERR_UNSUPPORTED   # G = 9
+    assert L.hk_sparse_decode(dummy, dummy, dummy, hk.HK_BF16, 1, 30, 4, 128, 10, dummy, 4, P, 4, f,
+                              dummy, dummy, dummy, 1 << 30, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_sparse_decode(dummy, dummy, dummy, hk.HK_BF16, 1, 8, 4, 64, 10, dummy, 4, P, 4, f,
+                              dummy, dummy, dummy, 1 << 30, P) == hk.HK_ERR_UNSUPPORTED   # d = 64
+    assert L.hk_sparse_decode(dummy, dummy, dummy, 7, 1, 8, 4, 128, 10, dummy, 4, P, 4, f,
+                              dummy, dummy, dummy, 1 << 30, P) == hk.HK_ERR_UNSUPPORTED
+    need = L.hk_sparse_decode_workspace(64, 32, 8, 128, 4000)
+    assert need > 0
+    assert L.hk_sparse_decode(dummy, dummy, dummy, hk.HK_BF16, 64, 32, 8, 128, 10, dummy, 4, P, 4000,
+                              f, dummy, dummy, dummy, need - 1, P) == hk.HK_ERR_WORKSPACE_TOO_SMALL
+    assert L.hk_lse_merge(dummy, dummy, 0, 4, 128, dummy, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_lse_merge(dummy, dummy, 2, -1, 128, dummy, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_lse_merge(P, P, 2, 0, 128, P, P, P) == hk.HK_OK
+    n = ctypes.c_int32(-1)
+    assert L.hk_window_indices(100, 4, 64, P, ctypes.byref(n), P) == hk.HK_OK and n.value == 68
+    assert L.hk_window_indices(-1, 4, 64, P, ctypes.byref(n), P) == hk.HK_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_sizes_grow_with_the_problem(hk):
+    a = hk.retrieve_topk_workspace(128, 1, 8, 100000, 4, 64, 100)
+    b = hk.retrieve_topk_workspace(128, 1, 8, 200000, 4, 64, 100)
+    c = hk.retrieve_topk_workspace(128, 2, 8, 200000, 4, 64, 100)
+    assert 0 < a < b < c
+    assert hk.retrieve_topk_workspace(128, 1, 8, 100000, 4, 64, 100) >= 8 * 99932   # a byte per candidate
+    assert hk.sparse_decode_workspace(1, 1, 1, 0) == 0 or hk.sparse_decode_workspace(1, 1, 1, 0) >= 0
+    assert hk.sparse_decode_workspace(16, 32, 8, 2622) >= hk.sparse_decode_workspace(16, 32, 8, 100)

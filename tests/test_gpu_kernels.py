@@ -1,0 +1,318 @@
+"""Parity of each HIP entry point with the CPU oracle at small sizes that still span
+several workgroup tiles and ragged tails, plus the degenerate cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import codes_tensor, compare_codes, np_u32, say
+
+pytestmark = pytest.mark.gpu
+
+hk = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global hk
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import hash_top_kv_amd
+    hk = hash_top_kv_amd
+
+
+# ----------------------------------------------------------------- retrieval
+RETRIEVE_CASES = [
+    # bits, B, Hkv, N, s, w, k, pool (number of distinct codes -> ties)
+    (128, 1, 1, 4096, 4, 64, 82, 0),
+    (128, 2, 3, 5000, 4, 64, 100, 6),       # heavy ties
+    (64, 2, 2, 9001, 4, 512, 181, 0),
+    (64, 1, 4, 3333, 0, 0, 77, 3),
+    (128, 3, 2, 70000, 4, 64, 1400, 0),     # many chunks per head
+    (128, 1, 2, 100, 4, 64, 82, 0),         # k >= candidates
+    (128, 1, 2, 60, 4, 64, 82, 0),          # n_ctx < s + w: no candidates
+    (128, 1, 2, 1000, 4, 64, 0, 0),         # k = 0
+    (64, 1, 1, 1, 0, 0, 5, 0),              # single token
+    (128, 2, 2, 4100, 4, 0, 4096, 2),       # k = C, two distinct codes
+]
+
+
+@pytest.mark.parametrize("case", RETRIEVE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_retrieve_topk_bit_exact(case):
+    bits, B, Hkv, N, s, w, k, pool = case
+    say(f"retrieve {case}")
+    W = bits // 32
+    rng = np.random.default_rng(N * 31 + k)
+    cap = N + 37                                           # capacity beyond the context
+    if pool:
+        table = rng.integers(0, 2 ** 32, size=(pool, W), dtype=np.uint32)
+        codes = table[rng.integers(0, pool, size=(B, Hkv, cap))]
+    else:
+        codes = rng.integers(0, 2 ** 32, size=(B, Hkv, cap, W), dtype=np.uint32)
+    qc = rng.integers(0, 2 ** 32, size=(B, Hkv, W), dtype=np.uint32)
+    idx, count = hk.retrieve_topk(codes_tensor(codes), codes_tensor(qc), bits, N, s, w, k)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    count = count.cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            want = oracle.select_topk(codes[b, h], qc[b, h], N, s, w, k)
+            assert count[b, h] == want.size
+            assert np.array_equal(idx[b, h, :want.size], want), (b, h)
+
+
+def test_retrieve_split_halves_equal_whole():
+    rng = np.random.default_rng(2)
+    codes = rng.integers(0, 2 ** 32, size=(2, 2, 20000, 4), dtype=np.uint32)
+    qc = rng.integers(0, 2 ** 32, size=(2, 2, 4), dtype=np.uint32)
+    c, q = codes_tensor(codes), codes_tensor(qc)
+    idx1, cnt1 = hk.retrieve_topk(c, q, 128, 20000, 4, 64, 400)
+    wsb = hk.retrieve_topk_workspace(128, 2, 2, 20000, 4, 64, 400)
+    ws = torch.full((wsb,), 0xAB, dtype=torch.uint8, device="cuda")   # poisoned workspace
+    idx2 = torch.full((2, 2, 400), -7, dtype=torch.int32, device="cuda")
+    cnt2 = torch.zeros((2, 2), dtype=torch.int32, device="cuda")
+    hk.hamming_scan(c, q, 128, 20000, 4, 64, 400, ws)
+    hk.topk_select(128, 2, 2, 20000, 4, 64, 400, idx2, cnt2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2)
+    assert (idx2 >= 0).all()                                 # every slot written
+
+
+def test_retrieve_is_deterministic():
+    rng = np.random.default_rng(3)
+    table = rng.integers(0, 2 ** 32, size=(5, 4), dtype=np.uint32)
+    codes = table[rng.integers(0, 5, size=(1, 4, 50000))]
+    qc = rng.integers(0, 2 ** 32, size=(1, 4, 4), dtype=np.uint32)
+    c, q = codes_tensor(codes), codes_tensor(qc)
+    a = hk.retrieve_topk(c, q, 128, 50000, 4, 64, 1000)[0].clone()
+    b = hk.retrieve_topk(c, q, 128, 50000, 4, 64, 1000)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_retrieve_planted_closed_form():
+    wl = synth.scaled(synth.WORKLOADS[2], N=100000, Hkv=2, Hq=2, k=300)
+    g = synth.make_given_codes(wl)
+    idx, count = hk.retrieve_topk(codes_tensor(g["codes"]), codes_tensor(g["qcodes"]), 128,
+                                  wl.N, 0, 0, wl.k)
+    idx = idx.cpu().numpy()
+    for h in range(2):
+        pos, dl = g["planted_pos"][0, h], g["planted_delta"][0, h]
+        want = sorted(int(pos[i]) for i in sorted(range(len(pos)), key=lambda i: (dl[i], pos[i]))[:wl.k])
+        assert idx[0, h].tolist() == want
+
+
+def test_window_indices():
+    for n, s, w in [(4096, 4, 64), (60, 4, 64), (131072, 4, 512), (3, 4, 64), (10, 0, 0)]:
+        got = hk.window_indices(n, s, w, "cuda").cpu().numpy()
+        assert np.array_equal(got, oracle.window_indices(n, s, w)), (n, s, w)
+
+
+# ----------------------------------------------------------------- attention
+def _attention_case(dtype, B, Hq, Hkv, cap, counts, seed, stride0=False):
+    rng = np.random.default_rng(seed)
+    d = 128
+    Kf = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32) * 1.5
+    Vf = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+    Qf = rng.standard_normal((B, Hq, d)).astype(np.float32) * 1.5
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    K = torch.from_numpy(Kf).to(tdt).cuda()
+    V = torch.from_numpy(Vf).to(tdt).cuda()
+    Q = torch.from_numpy(Qf).to(tdt).cuda()
+    maxc = max(counts)
+    if stride0:
+        lst = np.sort(rng.choice(cap, size=maxc, replace=False)).astype(np.int32)
+        idx_np = np.broadcast_to(lst, (B, Hkv, maxc))
+        idx = torch.from_numpy(lst).cuda()
+        cnt = None
+    else:
+        idx_np = np.zeros((B, Hkv, max(maxc, 1)), dtype=np.int32)
+        cnt_np = np.zeros((B, Hkv), dtype=np.int32)
+        for b in range(B):
+            for h in range(Hkv):
+                c = counts[(b * Hkv + h) % len(counts)]
+                idx_np[b, h, :c] = np.sort(rng.choice(cap, size=c, replace=False))
+                cnt_np[b, h] = c
+        idx = torch.from_numpy(idx_np).cuda()
+        cnt = torch.from_numpy(cnt_np).cuda()
+    return K, V, Q, idx, cnt, idx_np, (cnt.cpu().numpy() if cnt is not None else None), maxc
+
+
+ATT_CASES = [
+    # dtype, B, Hq, Hkv, cap, counts
+    ("f32", 1, 1, 1, 4096, [82]),
+    ("f32", 2, 8, 2, 3000, [1, 0, 700, 2000]),
+    ("bf16", 1, 32, 8, 5000, [656, 1, 300, 0, 1999, 17, 64, 655]),
+    ("bf16", 2, 28, 4, 9000, [5243, 100, 3, 4000]),
+    ("bf16", 3, 8, 8, 2000, [1024]),
+    ("bf16", 1, 16, 8, 500, [0]),
+    ("f32", 1, 6, 2, 9000, [8000, 33]),
+    ("bf16", 2, 5, 1, 800, [130, 129]),
+]
+
+
+@pytest.mark.parametrize("case", ATT_CASES, ids=lambda c: f"{c[0]}-B{c[1]}-Hq{c[2]}-Hkv{c[3]}")
+def test_sparse_decode_matches_oracle(case):
+    dtype, B, Hq, Hkv, cap, counts = case
+    say(f"sparse_decode {case}")
+    K, V, Q, idx, cnt, idx_np, cnt_np, maxc = _attention_case(dtype, B, Hq, Hkv, cap, counts, 7)
+    o, lse = hk.sparse_decode(Q, K, V, idx, maxc, count=cnt)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    Kd, Vd, Qd = (x.cpu().to(torch.float64).numpy() for x in (K, V, Q))
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    scale = 1 / math.sqrt(128)
+    for b in range(B):
+        lists = [idx_np[b, h, :cnt_np[b, h]] for h in range(Hkv)]
+        ro, rl = oracle.sparse_attention(Qd[b], Kd[b], Vd[b], lists, scale)
+        assert np.max(np.abs(o[b] - ro)) <= tol
+        fin = np.isfinite(rl)
+        assert np.array_equal(fin, np.isfinite(lse[b]))
+        assert np.all(lse[b][~fin] == -np.inf)
+        if fin.any():
+            assert np.max(np.abs(lse[b][fin] - rl[fin])) <= tol
+
+
+def test_sparse_decode_shared_list_stride0():
+    K, V, Q, idx, cnt, idx_np, _, maxc = _attention_case("bf16", 2, 8, 4, 3000, [68], 9, stride0=True)
+    o, lse = hk.sparse_decode(Q, K, V, idx, maxc, idx_stride=0)
+    torch.cuda.synchronize()
+    Kd, Vd, Qd = (x.cpu().to(torch.float64).numpy() for x in (K, V, Q))
+    for b in range(2):
+        ro, rl = oracle.sparse_attention(Qd[b], Kd[b], Vd[b], [idx_np[b, h] for h in range(4)],
+                                         1 / math.sqrt(128))
+        assert np.max(np.abs(o[b].cpu().numpy() - ro)) <= 2e-2
+        assert np.max(np.abs(lse[b].cpu().numpy() - rl)) <= 2e-2
+
+
+def test_lse_merge_matches_oracle():
+    rng = np.random.default_rng(11)
+    P, rows, d = 5, 300, 128
+    o_parts = rng.standard_normal((P, rows, d)).astype(np.float32)
+    lse_parts = (rng.standard_normal((P, rows)) * 4).astype(np.float32)
+    lse_parts[rng.random((P, rows)) < 0.3] = -np.inf
+    lse_parts[:, 7] = -np.inf                                # an all-empty row
+    o, lse = hk.lse_merge(torch.from_numpy(o_parts).cuda(), torch.from_numpy(lse_parts).cuda())
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    for r in range(rows):
+        ro, rl = oracle.lse_merge(o_parts[:, r].astype(np.float64), lse_parts[:, r].astype(np.float64))
+        assert np.max(np.abs(o[r] - ro)) <= 1e-5
+        assert (rl == -np.inf and lse[r] == -np.inf) or abs(lse[r] - rl) <= 1e-5
+
+
+# ----------------------------------------------------------------- encoders
+def _hash_case(kind, bits, dtype, seed, identity=False):
+    rng = np.random.default_rng(seed)
+    d = 128
+    if kind == "lsh":
+        if identity:
+            R = np.zeros((bits, d), np.float32)
+            R[np.arange(bits), rng.permutation(d)[:bits]] = 1.0
+        else:
+            R = rng.standard_normal((bits, d)).astype(np.float32)
+        h = {"kind": "lsh", "bits": bits, "dtype": dtype,
+             "R": R if dtype == "f32" else synth.to_bf16_bits(R)}
+    else:
+        if identity:
+            W1 = np.zeros((256, d), np.float32)
+            W1[np.arange(128), rng.permutation(d)] = 1.0
+            W2 = np.zeros((bits, 256), np.float32)
+            W2[np.arange(bits), rng.permutation(128)[:bits]] = 1.0
+        else:
+            W1 = (rng.standard_normal((256, d)) / math.sqrt(d)).astype(np.float32)
+            W2 = (rng.standard_normal((bits, 256)) / 16).astype(np.float32)
+        cv = (lambda a: a) if dtype == "f32" else synth.to_bf16_bits
+        h = {"kind": "mlp", "bits": bits, "dtype": dtype, "W1": cv(W1), "W2": cv(W2)}
+    return h
+
+
+ENC_CASES = [
+    ("lsh", 128, "f32", False), ("lsh", 64, "f32", False), ("mlp", 128, "f32", False),
+    ("lsh", 128, "bf16", True), ("lsh", 64, "bf16", True), ("mlp", 128, "bf16", True),
+    ("mlp", 64, "bf16", True),
+    ("lsh", 128, "bf16", False), ("lsh", 64, "bf16", False), ("mlp", 128, "bf16", False),
+    ("mlp", 64, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("case", ENC_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_encode_keys_matches_oracle(case):
+    kind, bits, dtype, identity = case
+    say(f"encode_keys {case}")
+    B, Hkv, cap = 2, 3, 1111
+    t0, t1 = 5, 1071                                         # ragged range inside the cache
+    wl = synth.scaled(synth.WORKLOADS[1], B=B, Hkv=Hkv, Hq=Hkv, N=cap, dtype=dtype)
+    kv = synth.make_kv(wl, "k")
+    hnp = _hash_case(kind, bits, dtype, 5, identity)
+    h = hk.Hash(kind, bits, **synth.hash_to_device(hnp))
+    K = synth.to_device(kv["K"], dtype)
+    sentinel = 0x5A5A5A5A
+    codes = torch.full((B, Hkv, cap, bits // 32), sentinel, dtype=torch.int32, device="cuda")
+    hk.encode_keys(h, K, codes, t0, t1)
+    torch.cuda.synchronize()
+    got = np_u32(codes)
+    hp = oracle.prepare_hash(hnp)
+    flips = 0
+    for b in range(B):
+        for g in range(Hkv):
+            ref, y = oracle.encode(oracle.widen(kv["K"][b, g, t0:t1], dtype), hp)
+            n = compare_codes(got[b, g, t0:t1], ref, y)
+            if identity:
+                assert n == 0
+            flips += n
+            assert np.all(got[b, g, :t0] == sentinel) and np.all(got[b, g, t1:] == sentinel)
+    say(f"  exempt bits that differ: {flips}")
+
+
+@pytest.mark.parametrize("case", [("lsh", 128, "f32"), ("mlp", 128, "bf16"), ("lsh", 64, "bf16"),
+                                  ("mlp", 64, "f32")], ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("G", [1, 4, 7])
+def test_encode_query_matches_oracle(case, G):
+    kind, bits, dtype = case
+    Hkv, B = 4, 3
+    wl = synth.scaled(synth.WORKLOADS[1], B=B, Hkv=Hkv, Hq=Hkv * G, dtype=dtype)
+    q = synth.make_q(wl)
+    hnp = _hash_case(kind, bits, dtype, 6)
+    h = hk.Hash(kind, bits, **synth.hash_to_device(hnp))
+    qc = hk.encode_query(h, synth.to_device(q, dtype), Hkv)
+    torch.cuda.synchronize()
+    ref, y = oracle.encode_query(oracle.widen(q, dtype), oracle.prepare_hash(hnp), Hkv)
+    compare_codes(np_u32(qc), ref, y)
+
+
+def test_encode_keys_append_one_token():
+    dtype, bits = "bf16", 128
+    wl = synth.scaled(synth.WORKLOADS[1], B=2, Hkv=2, Hq=2, N=300, dtype=dtype)
+    kv = synth.make_kv(wl, "k")
+    hnp = _hash_case("mlp", bits, dtype, 8)
+    h = hk.Hash("mlp", bits, **synth.hash_to_device(hnp))
+    K = synth.to_device(kv["K"], dtype)
+    codes = torch.zeros((2, 2, 300, 4), dtype=torch.int32, device="cuda")
+    hk.encode_keys(h, K, codes, 0, 299)
+    hk.encode_keys(h, K, codes, 299, 300)
+    torch.cuda.synchronize()
+    got = np_u32(codes)
+    hp = oracle.prepare_hash(hnp)
+    for b in range(2):
+        for g in range(2):
+            ref, y = oracle.encode(oracle.widen(kv["K"][b, g], dtype), hp)
+            compare_codes(got[b, g], ref, y)
+
+
+def test_invalid_arguments_enqueue_nothing():
+    c = torch.zeros((1, 1, 10, 4), dtype=torch.int32, device="cuda")
+    q = torch.zeros((1, 1, 4), dtype=torch.int32, device="cuda")
+    with pytest.raises(hk.HkError) as e:
+        hk.retrieve_topk(c, q, 96, 10, 0, 0, 3)
+    assert e.value.status == hk.HK_ERR_UNSUPPORTED
+    with pytest.raises(hk.HkError) as e:
+        hk.retrieve_topk(c, q, 128, 11, 0, 0, 3)              # n_ctx > cap
+    assert e.value.status == hk.HK_ERR_INVALID_ARGUMENT
+    ws = torch.empty(1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(hk.HkError) as e:
+        hk.retrieve_topk(c, q, 128, 10, 0, 0, 3, ws=ws)
+    assert e.value.status == hk.HK_ERR_WORKSPACE_TOO_SMALL
