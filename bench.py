@@ -1,0 +1,342 @@
+"""Benchmark of the binary-hash KV retrieval decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--hash i]
+                    [--replicas R] [--no-cpu] [--graph] [--prefill]
+
+Default workload: retrieval at 512K tokens -- 8 KV heads x 524,288 cached 128-bit codes
+(uniform random bits plus 1% planted near neighbours of the query code), top-1024 per
+head, then exact attention over the 1024 selected bf16 K/V rows of each head.  One step
+is hk_hamming_scan + hk_topk_select (= hk_retrieve_topk) + hk_sparse_decode.  Other
+workloads (--workload 0/1/3/4) run the whole step: hk_encode_query, hk_retrieve_topk,
+hk_sparse_decode over the top-k list and over the sink + local window, hk_lse_merge.
+
+Inputs are resident in HBM before timing.  R replicas of the per-step inputs (codes,
+query codes, queries) rotate so that the bytes a step reads are not left in the 256 MB
+Infinity Cache or the L2 by the previous steps (R * code bytes >> 256 MB).
+
+Prints ONE JSON line.  `value` is microseconds per decode step (lower is better).
+`roofline` describes the dominant kernel (the Hamming scan): algorithmic bytes per
+launch over its average duration, timed with HIP events on the launch stream.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "retrieve+sparse-attn µs/decode step @512K tok; achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = ["include/hk.h", "hash_top_kv_amd/csrc/hk_internal.h",
+                  "hash_top_kv_amd/csrc/retrieve.hip", "hash_top_kv_amd/csrc/attend.hip",
+                  "hash_top_kv_amd/csrc/encode.hip", "hash_top_kv_amd/csrc/api.hip"]
+
+
+def source_digest(files=KERNEL_SOURCES) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name: str):
+    """HBM bytes per launch of a kernel from a committed counter summary, if the kernel
+    sources have not changed since it was taken (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{name}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_info():
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return cores, model
+
+
+class Timer:
+    """Pairs of HIP events on the current (launch) stream."""
+
+    def __init__(self, torch, n):
+        self.torch = torch
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        self.i = 0
+
+    def start(self):
+        self.ev[self.i][0].record()
+
+    def stop(self):
+        self.ev[self.i][1].record()
+        self.i += 1
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.ev[:self.i]]))
+
+
+def build_retrieval_case(args, torch, hk, synth):
+    """Workload 2: given codes, per-step hk_hamming_scan + hk_topk_select + hk_sparse_decode."""
+    wl = synth.WORKLOADS[2]
+    R = args.replicas
+    kv = synth.make_kv(wl)
+    K = synth.to_device(kv["K"], wl.dtype)
+    V = synth.to_device(kv["V"], wl.dtype)
+    reps = []
+    for r in range(R):
+        g = synth.make_given_codes(wl, replica=r)
+        reps.append({"codes": synth.to_device(g["codes"], wl.dtype),
+                     "qcodes": synth.to_device(g["qcodes"], wl.dtype),
+                     "Q": synth.to_device(synth.make_q(wl, replica=r), wl.dtype),
+                     "planted": (g["planted_pos"], g["planted_delta"]) if r == 0 else None})
+    B, Hkv, N, k = wl.B, wl.Hkv, wl.N, wl.k
+    wsb = hk.retrieve_topk_workspace(128, B, Hkv, N, 0, 0, k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, Hkv, k), dtype=torch.int32, device="cuda")
+    count = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
+    wsd = torch.empty(max(1, hk.sparse_decode_workspace(B, wl.Hq, Hkv, k)), dtype=torch.uint8,
+                      device="cuda")
+    o = torch.empty((B, wl.Hq, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, wl.Hq), dtype=torch.float32, device="cuda")
+
+    def step(i, timers=None):
+        rp = reps[i % R]
+        if timers:
+            timers[0].start()
+        hk.hamming_scan(rp["codes"], rp["qcodes"], 128, N, 0, 0, k, ws)
+        if timers:
+            timers[0].stop()
+            timers[1].start()
+        hk.topk_select(128, B, Hkv, N, 0, 0, k, idx, count, ws)
+        if timers:
+            timers[1].stop()
+            timers[2].start()
+        hk.sparse_decode(rp["Q"], K, V, idx, k, count=count, o=o, lse=lse, ws=wsd)
+        if timers:
+            timers[2].stop()
+
+    def check():
+        step(0)
+        torch.cuda.synchronize()
+        pos, dl = reps[0]["planted"]
+        got = idx.cpu().numpy()
+        for h in range(Hkv):
+            order = np.lexsort((pos[0, h], dl[0, h]))
+            want = np.sort(pos[0, h][order[:k]])
+            assert np.array_equal(got[0, h], want), f"head {h}: top-k differs from the planted set"
+
+    scan_bytes = B * Hkv * N * 16
+    gather_bytes = B * Hkv * k * 2 * 128 * 2 + B * wl.Hq * 128 * 2
+    names = ["hamming_scan", "topk_select", "sparse_decode"]
+    info = {"workload": wl.name, "B": B, "Hq": wl.Hq, "Hkv": Hkv, "N": N, "k": k,
+            "code_bits": 128, "kv_dtype": "bf16", "replicas": R,
+            "rotating_code_bytes": R * scan_bytes}
+    return step, check, names, {"hamming_scan": scan_bytes, "sparse_decode": gather_bytes}, info, \
+        {"wl": wl, "reps": reps, "kv": kv}
+
+
+def build_full_case(args, torch, hk, synth):
+    """Workloads 0, 1, 3, 4: the whole step through DecodeStep, keys encoded beforehand."""
+    from hash_top_kv_amd.step import DecodeStep
+    wl = synth.WORKLOADS[args.workload]
+    spec = wl.hashes[args.hash]
+    R = args.replicas
+    kv = synth.make_kv(wl)
+    K = synth.to_device(kv["K"], wl.dtype)
+    V = synth.to_device(kv["V"], wl.dtype)
+    del kv
+    hnp = synth.make_hash(wl, spec, args.hash)
+    h = hk.Hash(spec.kind, spec.bits, **synth.hash_to_device(hnp))
+    codes = torch.empty((wl.B, wl.Hkv, wl.N, spec.words), dtype=torch.int32, device="cuda")
+    hk.encode_keys(h, K, codes)
+    torch.cuda.synchronize()
+    step_obj = DecodeStep(K, V, codes, spec.bits, wl.N, wl.n_sink, wl.n_local, wl.k, wl.Hq, h)
+    Qs = [synth.to_device(synth.make_q(wl, replica=r), wl.dtype) for r in range(R)]
+
+    def step(i, timers=None):
+        if timers:
+            timers[0].start()
+        step_obj(Qs[i % R])
+        if timers:
+            timers[0].stop()
+
+    def check():
+        step(0)
+        torch.cuda.synchronize()
+        assert bool((step_obj.count == step_obj.keff).all())
+
+    C = wl.N - wl.n_sink - wl.n_local
+    esz = 4 if wl.dtype == "f32" else 2
+    scan_bytes = wl.B * wl.Hkv * C * spec.bits // 8
+    gather_bytes = wl.B * wl.Hkv * (step_obj.keff + step_obj.n_win) * 2 * 128 * esz
+    info = {"workload": wl.name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "N": wl.N, "k": wl.k,
+            "n_sink": wl.n_sink, "n_local": wl.n_local, "hash": f"{spec.kind}-{spec.bits}",
+            "kv_dtype": wl.dtype, "replicas": R}
+    return step, check, ["decode_step"], {"hamming_scan": scan_bytes, "sparse_decode": gather_bytes}, \
+        info, {"wl": wl, "K": K, "h": h, "codes": codes, "spec": spec}
+
+
+def time_prefill(torch, hk, ctx, steps):
+    """MFMA key encode of the whole cache (prefill), bf16: flops per launch / duration."""
+    wl, K, h, codes, spec = ctx["wl"], ctx["K"], ctx["h"], ctx["codes"], ctx["spec"]
+    for _ in range(2):
+        hk.encode_keys(h, K, codes)
+    t = Timer(torch, steps)
+    for _ in range(steps):
+        t.start()
+        hk.encode_keys(h, K, codes)
+        t.stop()
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    M = wl.B * wl.Hkv * wl.N
+    flops = 2 * M * (128 * 256 + 256 * spec.bits) if spec.kind == "mlp" else 2 * M * 128 * spec.bits
+    bytes_ = M * 128 * 2 + M * spec.bits // 8
+    return {"kernel": f"encode_keys_mfma ({spec.kind}-{spec.bits})", "rows": M, "us": ms * 1e3,
+            "tflops": flops / ms / 1e9, "mfma_frac": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+            "hbm_gbs": bytes_ / ms / 1e6}
+
+
+def cpu_baseline(args, ctx, synth):
+    """The CPU oracle on a bounded sample: whole decode steps of the same workload."""
+    import oracle
+    cores, model = cpu_info()
+    if args.workload != 2:
+        return {"value": None, "unit": "us/step", "cores": cores, "kind": "oracle",
+                "sample": "not run for this workload"}
+    wl = ctx["wl"]
+    g = synth.make_given_codes(wl, replica=0)
+    kv = ctx["kv"]
+    q = oracle.widen(synth.make_q(wl, replica=0), wl.dtype)
+    scale = 1 / math.sqrt(128)
+    times = []
+    t_end = time.perf_counter() + args.cpu_seconds
+    while time.perf_counter() < t_end or not times:
+        t0 = time.perf_counter()
+        for h in range(wl.Hkv):
+            idx = oracle.select_topk(g["codes"][0, h], g["qcodes"][0, h], wl.N, 0, 0, wl.k)
+            kr = oracle.widen(kv["K"][0, h][idx], wl.dtype)
+            vr = oracle.widen(kv["V"][0, h][idx], wl.dtype)
+            oracle.attend(q[0, h], kr, vr, scale)
+        times.append(time.perf_counter() - t0)
+    us = float(np.median(times)) * 1e6
+    return {"value": round(us, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
+            "sample": f"{len(times)} whole decode steps (8 heads x 524288 codes, top-1024, "
+                      f"attention over the selected rows), median; NumPy popcount and stable "
+                      f"argsort run on one thread; host has {cores} cores ({model})"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--hash", type=int, default=0, help="index of the workload's hash (workload 4: 0 = LSH-64, 1 = MLP-128)")
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--prefill", action="store_true", help="also time the key encode of the whole cache")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the step shards by (batch, KV head) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hash_top_kv_amd as hk
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    build = build_retrieval_case if args.workload == 2 else build_full_case
+    step, check, names, alg_bytes, info, ctx = build(args, torch, hk, synth)
+    check()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps, synchronised on both sides.
+    t0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # Per-call durations, live, with events on the launch stream around each call.
+    kern = {}
+    if not args.no_kernel_timing:
+        timers = [Timer(torch, args.steps) for _ in names]
+        for i in range(args.steps):
+            step(i, timers)
+        torch.cuda.synchronize()
+        for n, t in zip(names, timers):
+            ms = t.mean_ms()
+            ent = {"us": round(ms * 1e3, 3)}
+            if n in alg_bytes:
+                ent["alg_bytes"] = alg_bytes[n]
+                ent["gbs"] = round(alg_bytes[n] / ms / 1e6, 1)
+                ent["frac_of_peak"] = round(alg_bytes[n] / ms / 1e6 / HBM_PEAK_GBS, 4)
+            kern[n] = ent
+
+    roofline = None
+    if "hamming_scan" in kern:
+        a = kern["hamming_scan"]["gbs"]
+        roofline = {"kernel": "hamming_scan", "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4),
+                    "traffic": read_traffic(f"hamming_scan_w{args.workload}"),
+                    "alg_bytes_per_launch": alg_bytes["hamming_scan"],
+                    "us_per_launch": kern["hamming_scan"]["us"]}
+    out = {"metric": METRIC, "value": round(ms_step * 1e3, 3), "unit": "us/step", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+           "dtype": "u32+f32", "data": "synthetic",
+           "config": info, "roofline": roofline, "kernels": kern,
+           "wall_ms_timed_region": round(wall_ms, 3)}
+    if args.prefill and args.workload != 2:
+        out["prefill"] = time_prefill(torch, hk, ctx, 10)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(args, ctx, synth)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

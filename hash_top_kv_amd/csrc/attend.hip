@@ -113,32 +113,54 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
   }
 
+  // Rows of this quarter-wave: r0 + qw + 16*j.  Lane col of the quarter-wave fetches the
+  // token index of row j = 16*blk + col for a block of 16 rows at a time, and the rows'
+  // indices are then broadcast within the quarter-wave.  K/V rows are loaded four at a
+  // time, one group ahead of the group being reduced.
   const int32_t *ilist = idx + (int64_t)bh * idx_stride;
   const size_t head_row0 = (size_t)bh * (size_t)cap;
-  for (int r = r0 + qw; r < r1; r += kQuarterWaves * kDecUnroll) {
-    typename RL::Raw kr[kDecUnroll], vr[kDecUnroll];
-    bool ok[kDecUnroll];
+  const int nrows = r1 > r0 + qw ? (r1 - r0 - qw + kQuarterWaves - 1) / kQuarterWaves : 0;
+  const int qlane0 = lane & ~15;
+  auto fetch_tokens = [&](int blk) -> int {
+    const int j = blk * 16 + col;
+    return j < nrows ? ilist[r0 + qw + kQuarterWaves * j] : 0;
+  };
+  auto load_group = [&](int grp, int toks, typename RL::Raw *kr, typename RL::Raw *vr) {
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
-      const int rr = r + u * kQuarterWaves;
-      ok[u] = rr < r1;
-      const int tok = ok[u] ? ilist[rr] : 0;
-      const size_t e0 = (head_row0 + (size_t)tok) * D + col * 8;
-      kr[u] = ok[u] ? RL::load(kc, e0) : RL::zero();
-      vr[u] = ok[u] ? RL::load(vc, e0) : RL::zero();
+      const int j = grp * kDecUnroll + u;
+      const int tok = __shfl(toks, qlane0 + (j & 15));
+      const bool ok = j < nrows;
+      const size_t e0 = (head_row0 + (size_t)(ok ? tok : 0)) * D + col * 8;
+      kr[u] = ok ? RL::load(kc, e0) : RL::zero();
+      vr[u] = ok ? RL::load(vc, e0) : RL::zero();
     }
+  };
+  const int ngroups = (nrows + kDecUnroll - 1) / kDecUnroll;
+  int toks = fetch_tokens(0);
+  typename RL::Raw kr[kDecUnroll], vr[kDecUnroll];
+  if (ngroups > 0) load_group(0, toks, kr, vr);
+  for (int grp = 0; grp < ngroups; ++grp) {
+    // Prefetch the next group (and the next 16 indices when this block of 16 is used up).
+    typename RL::Raw kn[kDecUnroll], vn[kDecUnroll];
+    const int ngrp = grp + 1;
+    int toks_n = toks;
+    if ((ngrp & 3) == 0 && ngrp < ngroups) toks_n = fetch_tokens(ngrp >> 2);
+    if (ngrp < ngroups) load_group(ngrp, toks_n, kn, vn);
+
     float s[G][kDecUnroll];
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
       float kf[8];
       RL::widen(kr[u], kf);
+      const bool ok = grp * kDecUnroll + u < nrows;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float a = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) a = fmaf(qf[g][e], kf[e], a);
         a = row16_sum(a);
-        s[g][u] = ok[u] ? a : -INFINITY;
+        s[g][u] = ok ? a : -INFINITY;
       }
     }
 #pragma unroll
@@ -146,7 +168,7 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
       float mx = s[g][0];
 #pragma unroll
       for (int u = 1; u < kDecUnroll; ++u) mx = fmaxf(mx, s[g][u]);
-      const float mn = fmaxf(m[g], mx);        // finite: row u = 0 is always valid
+      const float mn = fmaxf(m[g], mx);        // finite: row 0 of a group is always valid
       const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);
       float psum = 0.f;
 #pragma unroll
@@ -169,6 +191,12 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
         for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(s[g][u], vf[e], acc[g][e]);
       }
     }
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      kr[u] = kn[u];
+      vr[u] = vn[u];
+    }
+    toks = toks_n;
   }
 
   // Combine the four quarter-waves of this wave (lanes col, col+16, col+32, col+48).
@@ -221,7 +249,20 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
   }
 }
 
-// One wavefront per row.
+// One wavefront per row.  Phase 1: the lanes read the P log-sum-exps at once (max and
+// normaliser by wavefront reductions).  Phase 2: each lane accumulates its output
+// elements over the parts, eight parts of loads in flight at a time.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 __global__ __launch_bounds__(256) void lse_merge_kernel(
     const float *__restrict__ o_parts, const float *__restrict__ lse_parts, int P,
     int64_t rows, int d, float *__restrict__ o, float *__restrict__ lse) {
@@ -229,22 +270,41 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
   float m = -INFINITY;
-  for (int p = 0; p < P; ++p) m = fmaxf(m, lse_parts[(int64_t)p * rows + row]);
+  for (int p = lane; p < P; p += 64) m = fmaxf(m, lse_parts[(int64_t)p * rows + row]);
+  m = wave_max(m);
   if (m == -INFINITY) {
     for (int e = lane; e < d; e += 64) o[row * d + e] = 0.f;
     if (lane == 0) lse[row] = -INFINITY;
     return;
   }
   float ssum = 0.f;
-  for (int p = 0; p < P; ++p) ssum += expf(lse_parts[(int64_t)p * rows + row] - m);
+  for (int p = lane; p < P; p += 64) ssum += expf(lse_parts[(int64_t)p * rows + row] - m);
+  ssum = wave_sum(ssum);
   const float inv = 1.f / ssum;
-  for (int e = lane; e < d; e += 64) {
-    float a = 0.f;
-    for (int p = 0; p < P; ++p) {
-      const float w = expf(lse_parts[(int64_t)p * rows + row] - m);
-      a = fmaf(w, o_parts[((int64_t)p * rows + row) * d + e], a);
+  constexpr int PB = 8;
+  for (int e0 = 0; e0 < d; e0 += 128) {
+    const int ea = e0 + lane, eb = e0 + 64 + lane;
+    float acc_a = 0.f, acc_b = 0.f;
+    for (int p0 = 0; p0 < P; p0 += PB) {
+      float la[PB], va[PB], vb[PB];
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        const int p = p0 + j;
+        const bool ok = p < P;
+        const float *op = o_parts + ((int64_t)(ok ? p : 0) * rows + row) * d;
+        la[j] = ok ? lse_parts[(int64_t)p * rows + row] : -INFINITY;
+        va[j] = (ok && ea < d) ? op[ea] : 0.f;
+        vb[j] = (ok && eb < d) ? op[eb] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        const float w = expf(la[j] - m);
+        acc_a = fmaf(w, va[j], acc_a);
+        acc_b = fmaf(w, vb[j], acc_b);
+      }
     }
-    o[row * d + e] = a * inv;
+    if (ea < d) o[row * d + ea] = acc_a * inv;
+    if (eb < d) o[row * d + eb] = acc_b * inv;
   }
   if (lane == 0) lse[row] = m + logf(ssum);
 }
@@ -284,17 +344,18 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int max_count) {
   p.G = Hkv > 0 ? Hq / Hkv : 1;
   const int64_t BH = (int64_t)B * Hkv;
   const int mc = max_count > 0 ? max_count : 1;
-  // Aim for about 2048 workgroups, but keep >= 128 rows per slice (>= 32 when the
-  // whole problem is small) so that the partials stay a few percent of the gathered
-  // bytes.
-  const int min_rows = (BH * ((mc + 127) / 128) >= 512) ? 128 : 32;
-  int64_t want = BH > 0 ? (2048 + BH - 1) / BH : 1;
-  int64_t pmax = (mc + min_rows - 1) / min_rows;
-  int64_t P = want < pmax ? want : pmax;
-  if (P < 1) P = 1;
-  if (P > 1024) P = 1024;
-  p.rows_per_split = (int)((mc + P - 1) / P);
-  p.P = (int)((mc + p.rows_per_split - 1) / p.rows_per_split);
+  // Slices of 64, 128 or 256 rows: the smallest that keeps the grid near 1024
+  // workgroups.  Short slices finish in two memory round trips (indices, then rows);
+  // long ones amortise the (G x d) partial each slice writes.
+  int rps = 256;
+  for (int cand : {64, 128, 256}) {
+    if (BH * ((mc + cand - 1) / cand) <= 1024) {
+      rps = cand;
+      break;
+    }
+  }
+  p.rows_per_split = rps < mc ? rps : mc;
+  p.P = (mc + p.rows_per_split - 1) / p.rows_per_split;
   size_t off = 0;
   if (p.P > 1) {
     const size_t rows = (size_t)B * Hq;

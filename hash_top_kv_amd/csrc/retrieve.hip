@@ -25,91 +25,118 @@ namespace {
 constexpr int kScanThreads = 256;
 constexpr int kSelThreads = 1024;
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
 template <int W> struct CodeVec;
 template <> struct CodeVec<4> {
-  using T = uint4;
-  __device__ static T zero() { return make_uint4(0u, 0u, 0u, 0u); }
+  using T = u32x4;
+  __device__ static T zero() { return T{0u, 0u, 0u, 0u}; }
   __device__ static uint32_t dist(const T &v, const uint32_t *q) {
     return __builtin_popcount(v.x ^ q[0]) + __builtin_popcount(v.y ^ q[1]) +
            __builtin_popcount(v.z ^ q[2]) + __builtin_popcount(v.w ^ q[3]);
   }
 };
 template <> struct CodeVec<2> {
-  using T = uint2;
-  __device__ static T zero() { return make_uint2(0u, 0u); }
+  using T = u32x2;
+  __device__ static T zero() { return T{0u, 0u}; }
   __device__ static uint32_t dist(const T &v, const uint32_t *q) {
     return __builtin_popcount(v.x ^ q[0]) + __builtin_popcount(v.y ^ q[1]);
   }
 };
 
+// Token p of a chunk is handled by thread p % 256 as its item p / 256, so every load
+// instruction of a wavefront reads one contiguous run of codes.  A thread's distances
+// are stored four to a 32-bit word: word (i/4)*256 + t of the chunk holds items
+// i..i+3 of thread t (one dword store per four tokens, coalesced).
+template <int LPT>
+__device__ __forceinline__ int64_t stash_words_per_chunk() { return (int64_t)LPT / 4 * kScanThreads; }
+
 // grid (S, BH); chunk c of head bh covers candidate offsets [c*CH, (c+1)*CH).
 template <int W, int LPT>
 __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
     const uint32_t *__restrict__ codes, const uint32_t *__restrict__ qcodes, int64_t cap,
-    int64_t lo, int64_t C, int S, uint8_t *__restrict__ stash, uint32_t *__restrict__ cum) {
+    int64_t lo, int64_t C, int S, uint32_t *__restrict__ stash, uint32_t *__restrict__ cum) {
   constexpr int NB = 32 * W + 1;
   constexpr int NBP = (NB + 3) & ~3;
   constexpr int CH = kScanThreads * LPT;
   using CV = CodeVec<W>;
   using V = typename CV::T;
   __shared__ uint32_t hist[kScanThreads / 64][NBP];
-  __shared__ uint32_t tot[NBP];
 
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
   const int t = threadIdx.x;
   const int wave = t >> 6;
-
-  for (int i = t; i < (kScanThreads / 64) * NBP; i += kScanThreads) (&hist[0][0])[i] = 0u;
-
-  uint32_t q[W];
-#pragma unroll
-  for (int w = 0; w < W; ++w) q[w] = qcodes[(int64_t)bh * W + w];
+  const int lane = t & 63;
 
   const int64_t p0 = (int64_t)c * CH;
   const V *base = reinterpret_cast<const V *>(codes + ((int64_t)bh * cap + lo) * W);
+  // Stream the chunk's codes first (non-temporal: they are read exactly once).
   V v[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int64_t p = p0 + i * kScanThreads + t;
-    v[i] = (p < C) ? base[p] : CV::zero();
+    v[i] = (p < C) ? __builtin_nontemporal_load(base + p) : CV::zero();
   }
+  for (int i = t; i < (kScanThreads / 64) * NBP; i += kScanThreads) (&hist[0][0])[i] = 0u;
+  uint32_t q[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) q[w] = qcodes[(int64_t)bh * W + w];
   __syncthreads();
 
-  uint8_t *st = stash + (int64_t)bh * S * CH + p0;
+  uint32_t *st = stash + ((int64_t)bh * S + c) * stash_words_per_chunk<LPT>();
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int64_t p = p0 + i * kScanThreads + t;
-    const uint32_t d = CV::dist(v[i], q);
-    if (p < C) {
-      atomicAdd(&hist[wave][d], 1u);
-      st[i * kScanThreads + t] = (uint8_t)d;
-    } else {
-      st[i * kScanThreads + t] = 0xFF;  // never selected: T <= 128
+  for (int i4 = 0; i4 < LPT / 4; ++i4) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * i4 + j;
+      const int64_t p = p0 + i * kScanThreads + t;
+      uint32_t d = 0xFFu;                      // past the last candidate: never selected
+      if (p < C) {
+        d = CV::dist(v[i], q);
+        atomicAdd(&hist[wave][d], 1u);
+      }
+      packed |= d << (8 * j);
     }
+    st[i4 * kScanThreads + t] = packed;
   }
   __syncthreads();
-  if (t < NB) {
-    uint32_t s = 0;
+  // Inclusive cumulative histogram by one wavefront: lane l owns bins 2l, 2l+1 (and the
+  // last lane also bin NB-1 when NB is odd).
+  if (wave == 0) {
+    auto bin = [&](int b) -> uint32_t {
+      uint32_t s = 0;
 #pragma unroll
-    for (int w = 0; w < kScanThreads / 64; ++w) s += hist[w][t];
-    tot[t] = s;
-  }
-  __syncthreads();
-  if (t < NB) {
-    uint32_t s = 0;
-    for (int j = 0; j <= t; ++j) s += tot[j];
-    cum[((int64_t)bh * S + c) * NB + t] = s;
+      for (int w = 0; w < kScanThreads / 64; ++w) s += hist[w][b];
+      return s;
+    };
+    constexpr int PAIRS = (NB - 1) / 2;                // 64 or 32
+    uint32_t a = 0, b = 0;
+    if (lane < PAIRS) {
+      a = bin(2 * lane);
+      b = bin(2 * lane + 1);
+    }
+    const uint32_t inc = wave_incl_scan_u32(a + b);
+    uint32_t *out = cum + ((int64_t)bh * S + c) * NB;
+    if (lane < PAIRS) {
+      out[2 * lane] = inc - b;
+      out[2 * lane + 1] = inc;
+    }
+    if (lane == PAIRS - 1) out[NB - 1] = inc + bin(NB - 1);
   }
 }
 
-// grid (BH); one workgroup per head.
+// grid (BH); one workgroup per head.  Every load phase keeps all its loads in flight.
 template <int NB>
 __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
     const uint32_t *__restrict__ cum, int S, int keff, int4 *__restrict__ meta,
     int2 *__restrict__ params, int32_t *__restrict__ count) {
-  constexpr int NG = kSelThreads / NB;
-  __shared__ uint32_t part[NG][NB];
+  constexpr int BINS = NB - 1;                 // 128 or 64 (the last bin is extra)
+  constexpr int NGR = kSelThreads / BINS;      // 8 or 16 groups of chunks
+  constexpr int UNR = 8;
+  __shared__ uint32_t part[NGR][NB];
   __shared__ uint32_t gcum[NB];
   __shared__ uint32_t scan_lds[2][kSelThreads / 64];
   __shared__ int sT, sQ;
@@ -122,17 +149,30 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
     sQ = 0;
   }
   if (keff > 0) {
-    for (int e = tid; e < NG * NB; e += kSelThreads) {
-      const int g = e / NB, tb = e - g * NB;
-      uint32_t s = 0;
-      for (int c = g; c < S; c += NG) s += cb[(int64_t)c * NB + tb];
-      part[g][tb] = s;
+    const int tb = tid % BINS, g = tid / BINS;
+    uint32_t s = 0, s_last = 0;
+    for (int c0 = g; c0 < S; c0 += NGR * UNR) {
+      uint32_t vals[UNR], lastv[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int c = c0 + u * NGR;
+        vals[u] = c < S ? cb[(int64_t)c * NB + tb] : 0u;
+        lastv[u] = (c < S && tb == 0) ? cb[(int64_t)c * NB + BINS] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        s += vals[u];
+        s_last += lastv[u];
+      }
     }
+    part[g][tb] = s;
+    if (tb == 0) part[g][BINS] = s_last;
     __syncthreads();
     if (tid < NB) {
-      uint32_t s = 0;
-      for (int g = 0; g < NG; ++g) s += part[g][tid];
-      gcum[tid] = s;
+      uint32_t a = 0;
+#pragma unroll
+      for (int gg = 0; gg < NGR; ++gg) a += part[gg][tid];
+      gcum[tid] = a;
     }
     __syncthreads();
     if (tid < NB) {
@@ -171,69 +211,70 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
   }
 }
 
-template <int LPT> struct ByteVec;
-template <> struct ByteVec<16> {
-  __device__ static void load(const uint8_t *p, uint32_t *w) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(p);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  }
-};
-template <> struct ByteVec<8> {
-  __device__ static void load(const uint8_t *p, uint32_t *w) {
-    const uint2 v = *reinterpret_cast<const uint2 *>(p);
-    w[0] = v.x; w[1] = v.y;
-  }
-};
-template <> struct ByteVec<4> {
-  __device__ static void load(const uint8_t *p, uint32_t *w) {
-    w[0] = *reinterpret_cast<const uint32_t *>(p);
-  }
-};
-
-// grid (S, BH); thread t owns the LPT consecutive candidates t*LPT .. t*LPT+LPT-1.
+// grid (S, BH).  Same thread <-> token mapping as the scan.  Selected tokens are
+// compacted in token order (item-major, then thread) with wavefront ballots: the rank
+// of token (i, t) among the chunk's selected tokens is the count over items i' < i,
+// plus earlier wavefronts of item i, plus earlier lanes of its own wavefront.
 template <int LPT>
 __global__ __launch_bounds__(kScanThreads) void topk_emit_kernel(
-    const uint8_t *__restrict__ stash, const int4 *__restrict__ meta,
+    const uint32_t *__restrict__ stash, const int4 *__restrict__ meta,
     const int2 *__restrict__ params, int S, int64_t lo, int k, int32_t *__restrict__ idx) {
   constexpr int CH = kScanThreads * LPT;
-  __shared__ uint32_t scan_lds[kScanThreads / 64];
+  constexpr int NW = kScanThreads / 64;
+  __shared__ uint32_t cnt[2][LPT * NW];     // per (item, wave): #below T, #at T
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
   const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  // Issue every load of the block before branching on any of them.
   const int2 pr = params[bh];
+  const int4 mt = meta[(int64_t)bh * S + c];
+  const uint32_t *sp = stash + ((int64_t)bh * S + c) * stash_words_per_chunk<LPT>();
+  uint32_t w[LPT / 4];
+#pragma unroll
+  for (int i4 = 0; i4 < LPT / 4; ++i4) w[i4] = sp[i4 * kScanThreads + t];
   const int T = pr.x;
   const int quota = pr.y;
   if (T < 0) return;
-  const int4 mt = meta[(int64_t)bh * S + c];
   const int lt_before = mt.x, eq_before = mt.y;
   if (mt.z == 0 && (mt.w == 0 || eq_before >= quota)) return;  // nothing selected here
 
-  uint32_t w[LPT / 4];
-  ByteVec<LPT>::load(stash + ((int64_t)bh * S + c) * CH + (int64_t)t * LPT, w);
-  uint32_t lt = 0, eq = 0;
+  const uint64_t below_me = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t blt[LPT], beq[LPT];
 #pragma unroll
-  for (int e = 0; e < LPT; ++e) {
-    const int d = (w[e >> 2] >> (8 * (e & 3))) & 0xFF;
-    lt += d < T;
-    eq += d == T;
-  }
-  uint32_t total;
-  const uint32_t ex = block_excl_scan_u32<kScanThreads>(lt | (eq << 16), scan_lds, total);
-  int lt_run = (int)(ex & 0xFFFFu);
-  int eq_run = (int)(ex >> 16);
-  int32_t *out = idx + (int64_t)bh * k;
-  const int64_t tok0 = lo + (int64_t)c * CH + (int64_t)t * LPT;
-#pragma unroll
-  for (int e = 0; e < LPT; ++e) {
-    const int d = (w[e >> 2] >> (8 * (e & 3))) & 0xFF;
-    if (d < T) {
-      out[lt_before + lt_run + min(eq_before + eq_run, quota)] = (int32_t)(tok0 + e);
-      ++lt_run;
-    } else if (d == T) {
-      if (eq_before + eq_run < quota)
-        out[lt_before + lt_run + eq_before + eq_run] = (int32_t)(tok0 + e);
-      ++eq_run;
+  for (int i = 0; i < LPT; ++i) {
+    const int d = (w[i >> 2] >> (8 * (i & 3))) & 0xFF;
+    blt[i] = __ballot(d < T);
+    beq[i] = __ballot(d == T);
+    if (lane == 0) {
+      cnt[0][i * NW + wave] = (uint32_t)__popcll(blt[i]);
+      cnt[1][i * NW + wave] = (uint32_t)__popcll(beq[i]);
     }
+  }
+  __syncthreads();
+  // Exclusive scan of the (item, wave) counts, LPT*NW <= 64 entries, by wavefront 0.
+  if (wave == 0) {
+    const bool in = lane < LPT * NW;
+    const uint32_t a = in ? cnt[0][lane] : 0u, b = in ? cnt[1][lane] : 0u;
+    const uint32_t ia = wave_incl_scan_u32(a), ib = wave_incl_scan_u32(b);
+    if (in) {
+      cnt[0][lane] = ia - a;
+      cnt[1][lane] = ib - b;
+    }
+  }
+  __syncthreads();
+  int32_t *out = idx + (int64_t)bh * k;
+  const int64_t tok0 = lo + (int64_t)c * CH + t;
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int d = (w[i >> 2] >> (8 * (i & 3))) & 0xFF;
+    if (d > T) continue;
+    const int lt_rank = lt_before + (int)cnt[0][i * NW + wave] + __popcll(blt[i] & below_me);
+    const int eq_rank = eq_before + (int)cnt[1][i * NW + wave] + __popcll(beq[i] & below_me);
+    const int32_t tok = (int32_t)(tok0 + i * kScanThreads);
+    if (d < T) out[lt_rank + min(eq_rank, quota)] = tok;
+    else if (eq_rank < quota) out[lt_rank + eq_rank] = tok;
   }
 }
 
@@ -245,7 +286,7 @@ __global__ void window_indices_kernel(int32_t n_sinks, int64_t local0, int32_t n
 
 template <int W, int LPT>
 void scan_launch(const RetrievePlan &p, const uint32_t *codes, const uint32_t *qcodes,
-                 int64_t cap, uint8_t *stash, uint32_t *cum, hipStream_t st) {
+                 int64_t cap, uint32_t *stash, uint32_t *cum, hipStream_t st) {
   hipLaunchKernelGGL((hamming_scan_kernel<W, LPT>), dim3(p.S, p.BH), dim3(kScanThreads), 0,
                      st, codes, qcodes, cap, p.lo, p.C, p.S, stash, cum);
 }
@@ -289,7 +330,7 @@ hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
                                hipStream_t st) {
   if (p.BH == 0 || p.S == 0) return hipSuccess;
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  uint8_t *stash = w8 + p.off_stash;
+  uint32_t *stash = reinterpret_cast<uint32_t *>(w8 + p.off_stash);
   uint32_t *cum = reinterpret_cast<uint32_t *>(w8 + p.off_cum);
   if (p.W == 4) {
     if (p.lpt == 16) scan_launch<4, 16>(p, codes, qcodes, cap, stash, cum, st);
@@ -307,7 +348,7 @@ hipError_t launch_topk_select(const RetrievePlan &p, int k, int32_t *idx, int32_
                               void *ws, hipStream_t st) {
   if (p.BH == 0) return hipSuccess;
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  const uint8_t *stash = w8 + p.off_stash;
+  const uint32_t *stash = reinterpret_cast<const uint32_t *>(w8 + p.off_stash);
   const uint32_t *cum = reinterpret_cast<const uint32_t *>(w8 + p.off_cum);
   int4 *meta = reinterpret_cast<int4 *>(w8 + p.off_meta);
   int2 *params = reinterpret_cast<int2 *>(w8 + p.off_params);

@@ -37,6 +37,9 @@ RETRIEVE_CASES = [
     (128, 1, 2, 1000, 4, 64, 0, 0),         # k = 0
     (64, 1, 1, 1, 0, 0, 5, 0),              # single token
     (128, 2, 2, 4100, 4, 0, 4096, 2),       # k = C, two distinct codes
+    (128, 1, 8, 300001, 4, 64, 6001, 0),    # >= 2M tokens: 8 codes per thread
+    (64, 2, 4, 600000, 4, 512, 3000, 0),    # >= 4M tokens: 16 codes per thread
+    (128, 1, 8, 540000, 0, 0, 1024, 9),     # 16 codes per thread, heavy ties
 ]
 
 
