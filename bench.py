@@ -119,14 +119,15 @@ def build_retrieval_case(args, torch, hk, synth):
                      "Q": synth.to_device(synth.make_q(wl, replica=r), wl.dtype),
                      "planted": (g["planted_pos"], g["planted_delta"]) if r == 0 else None})
     B, Hkv, N, k = wl.B, wl.Hkv, wl.N, wl.k
-    wsb = hk.retrieve_topk_workspace(128, B, Hkv, N, 0, 0, k)
-    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     idx = torch.empty((B, Hkv, k), dtype=torch.int32, device="cuda")
     count = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
-    wsd = torch.empty(max(1, hk.sparse_decode_workspace(B, wl.Hq, Hkv, k)), dtype=torch.uint8,
-                      device="cuda")
     o = torch.empty((B, wl.Hq, 128), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, wl.Hq), dtype=torch.float32, device="cuda")
+    if args.unfused:
+        ws = hk.workspace(hk.retrieve_topk_workspace(128, B, Hkv, N, 0, 0, k))
+        wsd = hk.workspace(hk.sparse_decode_workspace(B, wl.Hq, Hkv, k))
+    else:
+        ws = hk.workspace(hk.retrieve_attend_workspace(128, B, wl.Hq, Hkv, N, 0, 0, k))
 
     def step(i, timers=None):
         rp = reps[i % R]
@@ -136,13 +137,13 @@ def build_retrieval_case(args, torch, hk, synth):
         if timers:
             timers[0].stop()
             timers[1].start()
-        hk.topk_select(128, B, Hkv, N, 0, 0, k, idx, count, ws)
+        if args.unfused:
+            hk.topk_select(128, B, Hkv, N, 0, 0, k, idx, count, ws)
+            hk.sparse_decode(rp["Q"], K, V, idx, k, count=count, o=o, lse=lse, ws=wsd)
+        else:
+            hk.select_attend(128, rp["Q"], K, V, N, 0, 0, k, idx, count, o, lse, ws)
         if timers:
             timers[1].stop()
-            timers[2].start()
-        hk.sparse_decode(rp["Q"], K, V, idx, k, count=count, o=o, lse=lse, ws=wsd)
-        if timers:
-            timers[2].stop()
 
     def check():
         step(0)
@@ -156,11 +157,13 @@ def build_retrieval_case(args, torch, hk, synth):
 
     scan_bytes = B * Hkv * N * 16
     gather_bytes = B * Hkv * k * 2 * 128 * 2 + B * wl.Hq * 128 * 2
-    names = ["hamming_scan", "topk_select", "sparse_decode"]
+    names = ["hamming_scan", "select+attend"]
     info = {"workload": wl.name, "B": B, "Hq": wl.Hq, "Hkv": Hkv, "N": N, "k": k,
             "code_bits": 128, "kv_dtype": "bf16", "replicas": R,
             "rotating_code_bytes": R * scan_bytes}
-    return step, check, names, {"hamming_scan": scan_bytes, "sparse_decode": gather_bytes}, info, \
+    info["step"] = ("hk_hamming_scan + hk_topk_select + hk_sparse_decode" if args.unfused
+                    else "hk_hamming_scan + hk_select_attend (= hk_retrieve_attend)")
+    return step, check, names, {"hamming_scan": scan_bytes, "select+attend": gather_bytes}, info, \
         {"wl": wl, "reps": reps, "kv": kv}
 
 
@@ -182,10 +185,12 @@ def build_full_case(args, torch, hk, synth):
     step_obj = DecodeStep(K, V, codes, spec.bits, wl.N, wl.n_sink, wl.n_local, wl.k, wl.Hq, h)
     Qs = [synth.to_device(synth.make_q(wl, replica=r), wl.dtype) for r in range(R)]
 
+    run = step_obj.unfused if args.unfused else step_obj
+
     def step(i, timers=None):
         if timers:
             timers[0].start()
-        step_obj(Qs[i % R])
+        run(Qs[i % R])
         if timers:
             timers[0].stop()
 
@@ -266,6 +271,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prefill", action="store_true", help="also time the key encode of the whole cache")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the step through the separate calls instead of the fused one")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes 10 times (calibrates "
+                         "the HBM byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -282,6 +292,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dsts = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        for i in range(10):
+            dsts[i % 2].copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 10}))
+        return
     build = build_retrieval_case if args.workload == 2 else build_full_case
     step, check, names, alg_bytes, info, ctx = build(args, torch, hk, synth)
     check()

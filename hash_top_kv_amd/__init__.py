@@ -49,6 +49,11 @@ _SIGNATURES = {
     "hk_sparse_decode": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _I64, _P, _I, _F,
                               _P, _P, _P, _SZ, _P]),
     "hk_lse_merge": (_I, [_P, _P, _I, _I64, _I, _P, _P, _P]),
+    "hk_retrieve_attend_workspace": (_SZ, [_I, _I, _I, _I, _I64, _I, _I, _I]),
+    "hk_select_attend": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I64, _I, _I, _I, _F,
+                              _P, _P, _P, _P, _P, _SZ, _P]),
+    "hk_retrieve_attend": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I64, _I, _I,
+                                _I, _F, _P, _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -60,7 +65,7 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
-                              "`python -m hash_top_kv_amd.build` (no fallback exists)")
+                              "`python hash_top_kv_amd/build.py` (no fallback exists)")
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(L, name)
@@ -164,6 +169,12 @@ def encode_query(h: Hash, q: torch.Tensor, Hkv: int, qcodes: torch.Tensor | None
     return qcodes
 
 
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled device workspace (the calls need zeros on first use and leave their
+    counters zero)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
 def retrieve_topk_workspace(bits, B, Hkv, n_ctx, n_sink, n_local, k) -> int:
     return int(lib().hk_retrieve_topk_workspace(bits, B, Hkv, n_ctx, n_sink, n_local, k))
 
@@ -174,7 +185,7 @@ def _topk_buffers(B, Hkv, k, device, idx, count, ws, ws_bytes):
     if count is None:
         count = torch.empty((B, Hkv), dtype=torch.int32, device=device)
     if ws is None:
-        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
+        ws = workspace(ws_bytes, device)
     _need(idx, "idx", dtype=torch.int32)
     if idx.shape[:2] != (B, Hkv) or idx.shape[2] < k:
         raise ValueError("idx must be [B, Hkv, >= k]")
@@ -269,7 +280,7 @@ def sparse_decode(q, k, v, idx, max_count: int, count=None, idx_stride=None, sca
     _need(lse, "lse", dtype=torch.float32, shape=(B, Hq))
     wsb = sparse_decode_workspace(B, Hq, Hkv, max_count, d)
     if ws is None:
-        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+        ws = workspace(wsb, q.device)
     _need(ws, "ws", dtype=torch.uint8)
     _check(lib().hk_sparse_decode(_ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, d, cap, _ptr(idx),
                                   idx_stride, _ptr(count), max_count, float(scale), _ptr(o),
@@ -294,4 +305,57 @@ def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, o=None, lse=None):
     _need(lse, "lse", dtype=torch.float32, shape=lse_parts.shape[1:])
     _check(lib().hk_lse_merge(_ptr(o_parts), _ptr(lse_parts), P, rows, d, _ptr(o), _ptr(lse),
                               _stream()), "hk_lse_merge")
+    return o, lse
+
+
+def retrieve_attend_workspace(bits, B, Hq, Hkv, n_ctx, n_sink, n_local, k) -> int:
+    return int(lib().hk_retrieve_attend_workspace(bits, B, Hq, Hkv, n_ctx, n_sink, n_local, k))
+
+
+def retrieve_attend(codes, qcodes, bits, q, k, v, n_ctx, n_sink, n_local, topk, scale=None,
+                    idx=None, count=None, o=None, lse=None, ws=None):
+    """hk_retrieve_attend: Hamming top-k + attention over the selected tokens and the
+    sink/local window, merged.  Returns (o [B, Hq, 128], lse [B, Hq], idx, count)."""
+    _need(codes, "codes", dtype=torch.int32)
+    B, Hkv, cap, W = codes.shape
+    _need(qcodes, "qcodes", dtype=torch.int32, shape=(B, Hkv, W))
+    dt = _dtype_code(q)
+    _need(q, "q")
+    _need(k, "k", dtype=q.dtype)
+    _need(v, "v", dtype=q.dtype, shape=k.shape)
+    Hq, d = q.shape[1], q.shape[2]
+    if tuple(k.shape[:3]) != (B, Hkv, cap):
+        raise ValueError("k must be [B, Hkv, cap, d] like the codes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    wsb = retrieve_attend_workspace(bits, B, Hq, Hkv, n_ctx, n_sink, n_local, topk)
+    idx, count, ws = _topk_buffers(B, Hkv, topk, codes.device, idx, count, ws, wsb)
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(o, "o", dtype=torch.float32, shape=(B, Hq, d))
+    _need(lse, "lse", dtype=torch.float32, shape=(B, Hq))
+    _check(lib().hk_retrieve_attend(_ptr(codes), _ptr(qcodes), bits, _ptr(q), _ptr(k), _ptr(v), dt,
+                                    B, Hq, Hkv, d, cap, n_ctx, n_sink, n_local, topk, float(scale),
+                                    _ptr(idx), _ptr(count), _ptr(o), _ptr(lse), _ptr(ws),
+                                    ws.numel(), _stream()), "hk_retrieve_attend")
+    return o, lse, idx, count
+
+
+def select_attend(bits, q, k, v, n_ctx, n_sink, n_local, topk, idx, count, o, lse, ws,
+                  scale=None):
+    """hk_select_attend: the part of hk_retrieve_attend after hk_hamming_scan (same ws)."""
+    dt = _dtype_code(q)
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx"), (count, "count"), (o, "o"),
+                 (lse, "lse"), (ws, "ws")):
+        _need(t, n)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(lib().hk_select_attend(bits, _ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, d, cap, n_ctx,
+                                  n_sink, n_local, topk, float(scale), _ptr(idx), _ptr(count),
+                                  _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream()),
+           "hk_select_attend")
     return o, lse

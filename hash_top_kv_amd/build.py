@@ -1,6 +1,6 @@
 """Build libhk.so (HIP for gfx950) in-tree with hipcc.
 
-    python -m hash_top_kv_amd.build        # or __graft_entry__.build()
+    python hash_top_kv_amd/build.py        # or __graft_entry__.build()
 
 Each translation unit compiles to hash_top_kv_amd/_build/*.o in parallel, then one
 shared library is linked next to this file.  Packed-fp32 instructions are disabled for
@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhk.so")
-SOURCES = ["api.hip", "retrieve.hip", "attend.hip", "encode.hip"]
+SOURCES = ["api.hip", "retrieve.hip", "attend.hip", "fused.hip", "encode.hip"]
 ARCH = "gfx950"
 
 

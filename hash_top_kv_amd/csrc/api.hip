@@ -119,6 +119,63 @@ hk_status hk_retrieve_topk(const uint32_t *codes, const uint32_t *qcodes, int bi
   return from_hip(launch_topk_select(p, k, idx, count, ws, as_stream(stream)));
 }
 
+size_t hk_retrieve_attend_workspace(int bits, int B, int Hq, int Hkv, int64_t n_ctx,
+                                    int n_sink, int n_local, int topk) {
+  if (check_retrieve(bits, B, Hkv, n_ctx, n_ctx, n_sink, n_local, topk) != HK_OK) return 0;
+  if (Hkv <= 0 || Hq < Hkv || Hq % Hkv != 0 || Hq / Hkv > kMaxGroup) return 0;
+  return plan_fused(bits, B, Hq, Hkv, n_ctx, n_sink, n_local, topk).total;
+}
+
+hk_status hk_retrieve_attend(const uint32_t *codes, const uint32_t *qcodes, int bits,
+                             const void *q, const void *kc, const void *vc, int dtype, int B,
+                             int Hq, int Hkv, int d, int64_t cap, int64_t n_ctx, int n_sink,
+                             int n_local, int topk, float scale, int32_t *idx, int32_t *count,
+                             float *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
+  hk_status s = check_retrieve(bits, B, Hkv, cap, n_ctx, n_sink, n_local, topk);
+  if (s != HK_OK) return s;
+  if (dtype != HK_F32 && dtype != HK_BF16) return HK_ERR_UNSUPPORTED;
+  if (d != kHeadDim) return HK_ERR_UNSUPPORTED;
+  if (Hkv <= 0 || Hq < Hkv || Hq % Hkv != 0) return HK_ERR_INVALID_ARGUMENT;
+  if (Hq / Hkv > kMaxGroup) return HK_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq == 0) return HK_OK;
+  const FusedPlan p = plan_fused(bits, B, Hq, Hkv, n_ctx, n_sink, n_local, topk);
+  if (!q || !count || !o || !lse || !ws) return HK_ERR_INVALID_ARGUMENT;
+  if (p.parts > 0 && (!kc || !vc)) return HK_ERR_INVALID_ARGUMENT;
+  if (p.r.S > 0 && (!codes || !qcodes)) return HK_ERR_INVALID_ARGUMENT;
+  if (p.r.keff > 0 && !idx) return HK_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
+  const hipStream_t st = as_stream(stream);
+  hipError_t e = launch_hamming_scan(p.r, codes, qcodes, cap, ws, st);
+  if (e == hipSuccess) e = launch_topk_threshold(p.r, count, ws, st);
+  if (e == hipSuccess)
+    e = launch_fused_attend(p, q, kc, vc, dtype, B, Hq, Hkv, cap, scale, topk, idx, o, lse, ws, st);
+  return from_hip(e);
+}
+
+hk_status hk_select_attend(int bits, const void *q, const void *kc, const void *vc, int dtype,
+                           int B, int Hq, int Hkv, int d, int64_t cap, int64_t n_ctx,
+                           int n_sink, int n_local, int topk, float scale, int32_t *idx,
+                           int32_t *count, float *o, float *lse, void *ws, size_t ws_bytes,
+                           void *stream) {
+  hk_status s = check_retrieve(bits, B, Hkv, cap, n_ctx, n_sink, n_local, topk);
+  if (s != HK_OK) return s;
+  if (dtype != HK_F32 && dtype != HK_BF16) return HK_ERR_UNSUPPORTED;
+  if (d != kHeadDim) return HK_ERR_UNSUPPORTED;
+  if (Hkv <= 0 || Hq < Hkv || Hq % Hkv != 0) return HK_ERR_INVALID_ARGUMENT;
+  if (Hq / Hkv > kMaxGroup) return HK_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq == 0) return HK_OK;
+  const FusedPlan p = plan_fused(bits, B, Hq, Hkv, n_ctx, n_sink, n_local, topk);
+  if (!q || !count || !o || !lse || !ws) return HK_ERR_INVALID_ARGUMENT;
+  if (p.parts > 0 && (!kc || !vc)) return HK_ERR_INVALID_ARGUMENT;
+  if (p.r.keff > 0 && !idx) return HK_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
+  const hipStream_t st = as_stream(stream);
+  hipError_t e = launch_topk_threshold(p.r, count, ws, st);
+  if (e == hipSuccess)
+    e = launch_fused_attend(p, q, kc, vc, dtype, B, Hq, Hkv, cap, scale, topk, idx, o, lse, ws, st);
+  return from_hip(e);
+}
+
 hk_status hk_window_indices(int64_t n_ctx, int n_sink, int n_local, int32_t *idx,
                             int32_t *n_out, void *stream) {
   if (n_ctx < 0 || n_sink < 0 || n_local < 0 || !n_out) return HK_ERR_INVALID_ARGUMENT;
@@ -164,7 +221,7 @@ hk_status hk_lse_merge(const float *o_parts, const float *lse_parts, int P, int6
   if (P < 1 || d < 1 || rows < 0) return HK_ERR_INVALID_ARGUMENT;
   if (rows == 0) return HK_OK;
   if (!o_parts || !lse_parts || !o || !lse) return HK_ERR_INVALID_ARGUMENT;
-  if (rows > (int64_t)4 * INT32_MAX) return HK_ERR_UNSUPPORTED;
+  if (rows > INT32_MAX) return HK_ERR_UNSUPPORTED;
   return from_hip(launch_lse_merge(o_parts, lse_parts, P, rows, d, o, lse, as_stream(stream)));
 }
 

@@ -1,0 +1,158 @@
+// Fused top-k emit + exact attention over the selected tokens, for one decode step.
+//
+// After the Hamming scan and the threshold, each chunk's workgroup compacts its selected
+// tokens (writing them to the head's ascending index list, as hk_topk_select does, and
+// to LDS), gathers their K/V rows and computes the partial attention of the G query
+// heads of its KV head over them.  Extra workgroups do the same over slices of the static
+// sink + local window.  The partials of a head -- disjoint token sets -- are then merged
+// by log-sum-exp rescaling (RetrievalAttention, atlas summary: Approach), which gives
+// attention over the selected tokens and the window together.
+//
+// Compared with emit -> sparse decode -> merge, this saves one kernel and one dependent
+// memory round trip (re-reading the index list) on the decode step's critical path.
+#include "attend_core.h"
+#include "select_core.h"
+
+namespace hk {
+namespace {
+
+// grid (S + Sw, B*Hkv).  Blocks c < S: chunk c of the retrieval; blocks c >= S: window
+// slice c - S.  Writes the normalised partial of part c.
+template <int LPT, bool BF16, int G>
+__global__ __launch_bounds__(kScanThreads) void emit_attend_kernel(
+    const uint32_t *__restrict__ stash, const int4 *__restrict__ meta,
+    const int2 *__restrict__ params, int S, int64_t lo, int k, int32_t *__restrict__ idx,
+    const void *__restrict__ q, const void *__restrict__ kc, const void *__restrict__ vc,
+    int Hq, int Hkv, int64_t cap, float scale_log2, int win_sinks, int64_t win_local0,
+    int n_win, int win_rows, float *__restrict__ part_o, float *__restrict__ part_lse,
+    int64_t rows) {
+  constexpr int CH = kScanThreads * LPT;
+  __shared__ int32_t sel[CH];
+  const int c = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / Hkv;
+  const int hkv = bh - b * Hkv;
+  const int t = threadIdx.x;
+  const int qw = t >> 4;
+  const int64_t row0 = (int64_t)b * Hq + (int64_t)hkv * G;
+  const size_t head_row0 = (size_t)bh * (size_t)cap;
+
+  GroupAttention<BF16, G> ga;
+  ga.init(q, row0, scale_log2);
+  if (c < S) {
+    const int2 pr = params[bh];
+    const int4 mt = meta[(int64_t)bh * S + c];
+    const uint32_t *sp = stash + ((int64_t)bh * S + c) * stash_words_per_chunk<LPT>();
+    uint32_t w[LPT / 4];
+#pragma unroll
+    for (int i4 = 0; i4 < LPT / 4; ++i4) w[i4] = sp[i4 * kScanThreads + t];
+    const int T = pr.x;
+    const int quota = pr.y;
+    const int nsel = T >= 0 ? chunk_selected(mt, quota) : 0;
+    if (nsel > 0) {
+      int32_t *out = idx + (int64_t)bh * k;
+      emit_chunk<LPT>(w, T, quota, mt.x, mt.y, lo + (int64_t)c * CH,
+                      [&](int pos, int lpos, int32_t tok) {
+                        out[pos] = tok;
+                        sel[lpos] = tok;
+                      });
+      __syncthreads();
+    }
+    const int nrows = nsel > qw ? (nsel - qw + kQuarterWaves - 1) / kQuarterWaves : 0;
+    ga.run(kc, vc, head_row0, nrows, [&](int j) { return sel[qw + kQuarterWaves * j]; });
+  } else {
+    const int r0 = (c - S) * win_rows;
+    const int r1 = min(n_win, r0 + win_rows);
+    const int nrows = r1 > r0 + qw ? (r1 - r0 - qw + kQuarterWaves - 1) / kQuarterWaves : 0;
+    ga.run(kc, vc, head_row0, nrows, [&](int j) {
+      const int r = r0 + qw + kQuarterWaves * j;
+      return r < win_sinks ? r : (int)(win_local0 + (r - win_sinks));
+    });
+  }
+  ga.combine_store(part_o + ((int64_t)c * rows + row0) * kHeadDim, part_lse + (int64_t)c * rows + row0);
+}
+
+template <int LPT, bool BF16, int G>
+void fused_launch(const FusedPlan &p, const uint32_t *stash, const int4 *meta,
+                  const int2 *params, int k, int32_t *idx, const void *q, const void *kc,
+                  const void *vc, int Hq, int Hkv, int64_t cap, float scale_log2, float *po,
+                  float *pl, int64_t rows, hipStream_t st) {
+  hipLaunchKernelGGL((emit_attend_kernel<LPT, BF16, G>), dim3(p.parts, p.r.BH),
+                     dim3(kScanThreads), 0, st, stash, meta, params, p.r.S, p.r.lo, k, idx, q,
+                     kc, vc, Hq, Hkv, cap, scale_log2, p.win_sinks, p.win_local0, p.n_win,
+                     p.win_rows, po, pl, rows);
+}
+
+template <int LPT, bool BF16>
+void fused_dispatch_g(const FusedPlan &p, const uint32_t *stash, const int4 *meta,
+                      const int2 *params, int k, int32_t *idx, const void *q, const void *kc,
+                      const void *vc, int Hq, int Hkv, int64_t cap, float sl2, float *po,
+                      float *pl, int64_t rows, hipStream_t st) {
+#define HK_FUSED_CASE(GG)                                                                   \
+  case GG:                                                                                  \
+    fused_launch<LPT, BF16, GG>(p, stash, meta, params, k, idx, q, kc, vc, Hq, Hkv, cap,   \
+                                sl2, po, pl, rows, st);                                     \
+    break;
+  switch (p.G) {
+    HK_FUSED_CASE(1) HK_FUSED_CASE(2) HK_FUSED_CASE(3) HK_FUSED_CASE(4)
+    HK_FUSED_CASE(5) HK_FUSED_CASE(6) HK_FUSED_CASE(7) HK_FUSED_CASE(8)
+    default: break;
+  }
+#undef HK_FUSED_CASE
+}
+
+}  // namespace
+
+FusedPlan plan_fused(int bits, int B, int Hq, int Hkv, int64_t n_ctx, int n_sink, int n_local,
+                     int k) {
+  FusedPlan p;
+  p.r = plan_retrieve(bits, B, Hkv, n_ctx, n_sink, n_local, k);
+  p.G = Hkv > 0 ? Hq / Hkv : 1;
+  const int64_t sinks = n_sink < n_ctx ? n_sink : n_ctx;
+  const int64_t local0 = (n_ctx - n_local) > n_sink ? (n_ctx - n_local) : n_sink;
+  p.win_sinks = (int)sinks;
+  p.win_local0 = local0;
+  p.n_win = (int)(sinks + (n_ctx > local0 ? n_ctx - local0 : 0));
+  p.Sw = (p.n_win + p.win_rows - 1) / p.win_rows;
+  p.parts = p.r.S + p.Sw;
+  size_t off = p.r.total;
+  const size_t rows = (size_t)B * Hq;
+  p.off_o = off;
+  off = align_up(off + (size_t)p.parts * rows * kHeadDim * sizeof(float), 256);
+  p.off_lse = off;
+  off = align_up(off + (size_t)p.parts * rows * sizeof(float), 256);
+  p.total = off;
+  return p;
+}
+
+hipError_t launch_fused_attend(const FusedPlan &p, const void *q, const void *kc,
+                               const void *vc, int dtype, int B, int Hq, int Hkv, int64_t cap,
+                               float scale, int k, int32_t *idx, float *o, float *lse, void *ws,
+                               hipStream_t st) {
+  const int64_t rows = (int64_t)B * Hq;
+  if (rows == 0) return hipSuccess;
+  uint8_t *w8 = static_cast<uint8_t *>(ws);
+  float *po = reinterpret_cast<float *>(w8 + p.off_o);
+  float *pl = reinterpret_cast<float *>(w8 + p.off_lse);
+  if (p.parts > 0) {
+    const uint32_t *stash = reinterpret_cast<const uint32_t *>(w8 + p.r.off_stash);
+    const int4 *meta = reinterpret_cast<const int4 *>(w8 + p.r.off_meta);
+    const int2 *params = reinterpret_cast<const int2 *>(w8 + p.r.off_params);
+    const float sl2 = scale * kLog2e;
+    const bool bf = dtype == HK_BF16;
+#define HK_LPT(L)                                                                            \
+  if (bf) fused_dispatch_g<L, true>(p, stash, meta, params, k, idx, q, kc, vc, Hq, Hkv, cap, \
+                                    sl2, po, pl, rows, st);                                  \
+  else fused_dispatch_g<L, false>(p, stash, meta, params, k, idx, q, kc, vc, Hq, Hkv, cap,   \
+                                  sl2, po, pl, rows, st);
+    if (p.r.lpt == 16) { HK_LPT(16) }
+    else if (p.r.lpt == 8) { HK_LPT(8) }
+    else { HK_LPT(4) }
+#undef HK_LPT
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_lse_merge_parts(po, pl, p.parts, rows, kHeadDim, o, lse, st);
+}
+
+}  // namespace hk

@@ -34,6 +34,8 @@ hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
                                hipStream_t st);
 hipError_t launch_topk_select(const RetrievePlan &p, int k, int32_t *idx, int32_t *count,
                               void *ws, hipStream_t st);
+hipError_t launch_topk_threshold(const RetrievePlan &p, int32_t *count, void *ws,
+                                 hipStream_t st);
 hipError_t launch_window_indices(int64_t n_ctx, int n_sink, int n_local, int32_t *idx,
                                  hipStream_t st);
 
@@ -53,6 +55,26 @@ hipError_t launch_sparse_decode(const DecodePlan &p, const void *q, const void *
                                 float *lse, void *ws, hipStream_t st);
 hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int P,
                             int64_t rows, int d, float *o, float *lse, hipStream_t st);
+// Same kernel, also for P == 0 (every row empty: o = 0, lse = -inf).
+hipError_t launch_lse_merge_parts(const float *o_parts, const float *lse_parts, int P,
+                                  int64_t rows, int d, float *o, float *lse, hipStream_t st);
+
+// ---------------------------------------------------------------- fused step
+// hk_retrieve_attend: the retrieval workspace (RetrievePlan) followed by one normalised
+// partial per chunk of each head and per window slice: o [parts][B*Hq][d], lse
+// [parts][B*Hq], parts = S + window slices.
+struct FusedPlan {
+  RetrievePlan r;
+  int win_sinks = 0, n_win = 0, win_rows = 64, Sw = 0, parts = 0, G = 1;
+  int64_t win_local0 = 0;
+  size_t off_o = 0, off_lse = 0, total = 0;
+};
+FusedPlan plan_fused(int bits, int B, int Hq, int Hkv, int64_t n_ctx, int n_sink, int n_local,
+                     int k);
+hipError_t launch_fused_attend(const FusedPlan &p, const void *q, const void *kc,
+                               const void *vc, int dtype, int B, int Hq, int Hkv, int64_t cap,
+                               float scale, int k, int32_t *idx, float *o, float *lse, void *ws,
+                               hipStream_t st);
 
 // ---------------------------------------------------------------- encoders
 hipError_t launch_encode_keys(const hk_hash &h, const void *k, int B, int Hkv, int64_t cap,

@@ -17,12 +17,11 @@
 //   topk_emit      re-reads the one-byte distances of a chunk and writes the selected
 //                  tokens (all with D < T, and the first `quota` with D == T in index
 //                  order) at their final positions, so the output is ascending.
-#include "hk_internal.h"
+#include "select_core.h"
 
 namespace hk {
 namespace {
 
-constexpr int kScanThreads = 256;
 constexpr int kSelThreads = 1024;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -44,13 +43,6 @@ template <> struct CodeVec<2> {
     return __builtin_popcount(v.x ^ q[0]) + __builtin_popcount(v.y ^ q[1]);
   }
 };
-
-// Token p of a chunk is handled by thread p % 256 as its item p / 256, so every load
-// instruction of a wavefront reads one contiguous run of codes.  A thread's distances
-// are stored four to a 32-bit word: word (i/4)*256 + t of the chunk holds items
-// i..i+3 of thread t (one dword store per four tokens, coalesced).
-template <int LPT>
-__device__ __forceinline__ int64_t stash_words_per_chunk() { return (int64_t)LPT / 4 * kScanThreads; }
 
 // grid (S, BH); chunk c of head bh covers candidate offsets [c*CH, (c+1)*CH).
 template <int W, int LPT>
@@ -211,22 +203,15 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
   }
 }
 
-// grid (S, BH).  Same thread <-> token mapping as the scan.  Selected tokens are
-// compacted in token order (item-major, then thread) with wavefront ballots: the rank
-// of token (i, t) among the chunk's selected tokens is the count over items i' < i,
-// plus earlier wavefronts of item i, plus earlier lanes of its own wavefront.
+// grid (S, BH).  Same thread <-> token mapping as the scan.
 template <int LPT>
 __global__ __launch_bounds__(kScanThreads) void topk_emit_kernel(
     const uint32_t *__restrict__ stash, const int4 *__restrict__ meta,
     const int2 *__restrict__ params, int S, int64_t lo, int k, int32_t *__restrict__ idx) {
   constexpr int CH = kScanThreads * LPT;
-  constexpr int NW = kScanThreads / 64;
-  __shared__ uint32_t cnt[2][LPT * NW];     // per (item, wave): #below T, #at T
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
   const int t = threadIdx.x;
-  const int wave = t >> 6;
-  const int lane = t & 63;
   // Issue every load of the block before branching on any of them.
   const int2 pr = params[bh];
   const int4 mt = meta[(int64_t)bh * S + c];
@@ -236,46 +221,10 @@ __global__ __launch_bounds__(kScanThreads) void topk_emit_kernel(
   for (int i4 = 0; i4 < LPT / 4; ++i4) w[i4] = sp[i4 * kScanThreads + t];
   const int T = pr.x;
   const int quota = pr.y;
-  if (T < 0) return;
-  const int lt_before = mt.x, eq_before = mt.y;
-  if (mt.z == 0 && (mt.w == 0 || eq_before >= quota)) return;  // nothing selected here
-
-  const uint64_t below_me = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint64_t blt[LPT], beq[LPT];
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int d = (w[i >> 2] >> (8 * (i & 3))) & 0xFF;
-    blt[i] = __ballot(d < T);
-    beq[i] = __ballot(d == T);
-    if (lane == 0) {
-      cnt[0][i * NW + wave] = (uint32_t)__popcll(blt[i]);
-      cnt[1][i * NW + wave] = (uint32_t)__popcll(beq[i]);
-    }
-  }
-  __syncthreads();
-  // Exclusive scan of the (item, wave) counts, LPT*NW <= 64 entries, by wavefront 0.
-  if (wave == 0) {
-    const bool in = lane < LPT * NW;
-    const uint32_t a = in ? cnt[0][lane] : 0u, b = in ? cnt[1][lane] : 0u;
-    const uint32_t ia = wave_incl_scan_u32(a), ib = wave_incl_scan_u32(b);
-    if (in) {
-      cnt[0][lane] = ia - a;
-      cnt[1][lane] = ib - b;
-    }
-  }
-  __syncthreads();
+  if (T < 0 || chunk_selected(mt, quota) == 0) return;
   int32_t *out = idx + (int64_t)bh * k;
-  const int64_t tok0 = lo + (int64_t)c * CH + t;
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int d = (w[i >> 2] >> (8 * (i & 3))) & 0xFF;
-    if (d > T) continue;
-    const int lt_rank = lt_before + (int)cnt[0][i * NW + wave] + __popcll(blt[i] & below_me);
-    const int eq_rank = eq_before + (int)cnt[1][i * NW + wave] + __popcll(beq[i] & below_me);
-    const int32_t tok = (int32_t)(tok0 + i * kScanThreads);
-    if (d < T) out[lt_rank + min(eq_rank, quota)] = tok;
-    else if (eq_rank < quota) out[lt_rank + eq_rank] = tok;
-  }
+  emit_chunk<LPT>(w, T, quota, mt.x, mt.y, lo + (int64_t)c * CH,
+                  [&](int pos, int, int32_t tok) { out[pos] = tok; });
 }
 
 __global__ void window_indices_kernel(int32_t n_sinks, int64_t local0, int32_t n,
@@ -344,11 +293,10 @@ hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
   return hipGetLastError();
 }
 
-hipError_t launch_topk_select(const RetrievePlan &p, int k, int32_t *idx, int32_t *count,
-                              void *ws, hipStream_t st) {
+hipError_t launch_topk_threshold(const RetrievePlan &p, int32_t *count, void *ws,
+                                 hipStream_t st) {
   if (p.BH == 0) return hipSuccess;
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  const uint32_t *stash = reinterpret_cast<const uint32_t *>(w8 + p.off_stash);
   const uint32_t *cum = reinterpret_cast<const uint32_t *>(w8 + p.off_cum);
   int4 *meta = reinterpret_cast<int4 *>(w8 + p.off_meta);
   int2 *params = reinterpret_cast<int2 *>(w8 + p.off_params);
@@ -358,8 +306,18 @@ hipError_t launch_topk_select(const RetrievePlan &p, int k, int32_t *idx, int32_
   else
     hipLaunchKernelGGL((topk_threshold_kernel<65>), dim3(p.BH), dim3(kSelThreads), 0, st,
                        cum, p.S, p.keff, meta, params, count);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_select(const RetrievePlan &p, int k, int32_t *idx, int32_t *count,
+                              void *ws, hipStream_t st) {
+  if (p.BH == 0) return hipSuccess;
+  hipError_t e = launch_topk_threshold(p, count, ws, st);
   if (e != hipSuccess || p.S == 0 || p.keff == 0) return e;
+  uint8_t *w8 = static_cast<uint8_t *>(ws);
+  const uint32_t *stash = reinterpret_cast<const uint32_t *>(w8 + p.off_stash);
+  const int4 *meta = reinterpret_cast<const int4 *>(w8 + p.off_meta);
+  const int2 *params = reinterpret_cast<const int2 *>(w8 + p.off_params);
   if (p.lpt == 16)
     hipLaunchKernelGGL((topk_emit_kernel<16>), dim3(p.S, p.BH), dim3(kScanThreads), 0, st,
                        stash, meta, params, p.S, p.lo, k, idx);

@@ -17,8 +17,9 @@ import math
 
 import torch
 
-from . import (Hash, encode_query, lse_merge, retrieve_topk_workspace, sparse_decode,
-               sparse_decode_workspace, window_indices, _check, _ptr, _stream, lib)
+from . import (Hash, encode_query, lse_merge, retrieve_attend, retrieve_attend_workspace,
+               retrieve_topk_workspace, sparse_decode, sparse_decode_workspace, window_indices,
+               workspace, _check, _ptr, _stream, lib)
 
 
 class DecodeStep:
@@ -35,12 +36,12 @@ class DecodeStep:
         self.count = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
         self.win = window_indices(n_ctx, n_sink, n_local, dev)
         self.n_win = int(self.win.numel())
-        self.ws_r = torch.empty(max(1, retrieve_topk_workspace(bits, B, Hkv, n_ctx, n_sink,
-                                                               n_local, k)),
-                                dtype=torch.uint8, device=dev)
+        self.ws_r = workspace(retrieve_topk_workspace(bits, B, Hkv, n_ctx, n_sink, n_local, k), dev)
         wd = max(sparse_decode_workspace(B, Hq, Hkv, self.keff, d),
                  sparse_decode_workspace(B, Hq, Hkv, self.n_win, d))
-        self.ws_d = torch.empty(max(1, wd), dtype=torch.uint8, device=dev)
+        self.ws_d = workspace(wd, dev)
+        self.ws_f = workspace(retrieve_attend_workspace(bits, B, Hq, Hkv, n_ctx, n_sink, n_local,
+                                                        k), dev)
         self.o_parts = torch.empty((2, B, Hq, d), dtype=torch.float32, device=dev)
         self.lse_parts = torch.empty((2, B, Hq), dtype=torch.float32, device=dev)
         self.o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
@@ -56,7 +57,19 @@ class DecodeStep:
                                   self.ws_r.numel(), _stream()), "hk_retrieve_topk")
 
     def __call__(self, q: torch.Tensor, qcodes: torch.Tensor | None = None):
-        """Returns (o [B, Hq, d], lse [B, Hq]); with qcodes given the query is not hashed."""
+        """Returns (o [B, Hq, d], lse [B, Hq]); with qcodes given the query is not hashed.
+        hk_encode_query, then hk_retrieve_attend (retrieval, attention over the selected
+        tokens and the window, merge)."""
+        if qcodes is None:
+            qcodes = encode_query(self.hash, q, self.Hkv, self.qcodes)
+        retrieve_attend(self.codes, qcodes, self.bits, q, self.K, self.V, self.n_ctx,
+                        self.n_sink, self.n_local, self.k, scale=self.scale, idx=self.idx,
+                        count=self.count, o=self.o, lse=self.lse, ws=self.ws_f)
+        return self.o, self.lse
+
+    def unfused(self, q: torch.Tensor, qcodes: torch.Tensor | None = None):
+        """The same step through the separate calls: hk_encode_query, hk_retrieve_topk,
+        hk_sparse_decode over the top-k list and over the window, hk_lse_merge."""
         if qcodes is None:
             qcodes = encode_query(self.hash, q, self.Hkv, self.qcodes)
         self.retrieve(qcodes)

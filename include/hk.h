@@ -130,6 +130,44 @@ hk_status hk_topk_select(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, in
                          int k, int32_t *idx, int32_t *count, void *ws, size_t ws_bytes,
                          void *stream);
 
+/* Workspace bytes needed by hk_retrieve_attend. */
+size_t hk_retrieve_attend_workspace(int bits, int B, int Hq, int Hkv, int64_t n_ctx,
+                                    int n_sink, int n_local, int topk);
+
+/* One decode step after the query hash, fused: Hamming top-k retrieval as
+ * hk_retrieve_topk (same idx and count), then exact attention of every query head over
+ * its KV head's selected tokens together with the static sink + local window
+ * [0, min(n_sink, n_ctx)) U [max(n_sink, n_ctx - n_local), n_ctx), i.e. the log-sum-exp
+ * merge of the two partial attentions (RetrievalAttention, atlas summary: Approach;
+ * Spotlight Attention: summary).  Equal, up to floating-point rounding, to
+ * hk_retrieve_topk + hk_sparse_decode over idx + hk_sparse_decode over the window +
+ * hk_lse_merge, in fewer kernels: each chunk's workgroup attends directly over the
+ * tokens it selects.
+ *   codes, qcodes, bits, cap, n_ctx, n_sink, n_local, topk, idx, count: as in
+ *               hk_retrieve_topk (idx may be NULL when no token can be selected).
+ *   q, kc, vc, dtype, d, scale: as q, k, v, dtype, d, scale of hk_sparse_decode.
+ *   o, lse      device float [B][Hq][d] and [B][Hq] (written): the merged attention; an
+ *               empty selection and window give o = 0, lse = -inf.
+ *   ws          hk_retrieve_attend_workspace(...) bytes, 256-byte aligned, contents on
+ *               entry irrelevant.
+ * Errors: as hk_retrieve_topk and hk_sparse_decode. */
+hk_status hk_retrieve_attend(const uint32_t *codes, const uint32_t *qcodes, int bits,
+                             const void *q, const void *kc, const void *vc, int dtype, int B,
+                             int Hq, int Hkv, int d, int64_t cap, int64_t n_ctx, int n_sink,
+                             int n_local, int topk, float scale, int32_t *idx, int32_t *count,
+                             float *o, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* The part of hk_retrieve_attend that follows the Hamming scan: called after
+ * hk_hamming_scan(codes, qcodes, bits, B, Hkv, cap, n_ctx, n_sink, n_local, topk, ws, ...)
+ * on the same stream and workspace (of hk_retrieve_attend_workspace(...) bytes), it
+ * produces exactly what hk_retrieve_attend produces.  For callers that time or overlap
+ * the scan separately. */
+hk_status hk_select_attend(int bits, const void *q, const void *kc, const void *vc, int dtype,
+                           int B, int Hq, int Hkv, int d, int64_t cap, int64_t n_ctx,
+                           int n_sink, int n_local, int topk, float scale, int32_t *idx,
+                           int32_t *count, float *o, float *lse, void *ws, size_t ws_bytes,
+                           void *stream);
+
 /* Write the static window [0, min(s, n)) U [max(s, n - w), n) in ascending order
  * (tokens kept by fixed patterns: RetrievalAttention, elamur summary: Summary).
  *   idx    device int32 array of at least *n_out entries (written), or NULL to

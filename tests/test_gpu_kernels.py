@@ -67,21 +67,40 @@ def test_retrieve_topk_bit_exact(case):
             assert np.array_equal(idx[b, h, :want.size], want), (b, h)
 
 
-def test_retrieve_split_halves_equal_whole():
+def test_retrieve_split_halves_equal_whole_and_workspace_reuse():
+    """The two halves equal the whole call, and one workspace serves many calls: each
+    call leaves its counters at zero (inputs differ between the calls)."""
     rng = np.random.default_rng(2)
-    codes = rng.integers(0, 2 ** 32, size=(2, 2, 20000, 4), dtype=np.uint32)
-    qc = rng.integers(0, 2 ** 32, size=(2, 2, 4), dtype=np.uint32)
-    c, q = codes_tensor(codes), codes_tensor(qc)
-    idx1, cnt1 = hk.retrieve_topk(c, q, 128, 20000, 4, 64, 400)
     wsb = hk.retrieve_topk_workspace(128, 2, 2, 20000, 4, 64, 400)
-    ws = torch.full((wsb,), 0xAB, dtype=torch.uint8, device="cuda")   # poisoned workspace
-    idx2 = torch.full((2, 2, 400), -7, dtype=torch.int32, device="cuda")
-    cnt2 = torch.zeros((2, 2), dtype=torch.int32, device="cuda")
-    hk.hamming_scan(c, q, 128, 20000, 4, 64, 400, ws)
-    hk.topk_select(128, 2, 2, 20000, 4, 64, 400, idx2, cnt2, ws)
+    ws = hk.workspace(wsb)
+    for trial in range(3):
+        codes = rng.integers(0, 2 ** 32, size=(2, 2, 20000, 4), dtype=np.uint32)
+        qc = rng.integers(0, 2 ** 32, size=(2, 2, 4), dtype=np.uint32)
+        c, q = codes_tensor(codes), codes_tensor(qc)
+        idx1, cnt1 = hk.retrieve_topk(c, q, 128, 20000, 4, 64, 400, ws=ws)
+        idx2 = torch.full((2, 2, 400), -7, dtype=torch.int32, device="cuda")
+        cnt2 = torch.zeros((2, 2), dtype=torch.int32, device="cuda")
+        hk.hamming_scan(c, q, 128, 20000, 4, 64, 400, ws)
+        hk.topk_select(128, 2, 2, 20000, 4, 64, 400, idx2, cnt2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2)
+        assert (idx2 >= 0).all()                                 # every slot written
+        for b in range(2):
+            for h in range(2):
+                want = oracle.select_topk(codes[b, h], qc[b, h], 20000, 4, 64, 400)
+                assert np.array_equal(idx1[b, h].cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("shape", [(2, 8, 2, [700, 2000]), (3, 8, 8, [1024, 3, 0])],
+                         ids=["merge-kernel", "merge-in-gather"])
+def test_sparse_decode_workspace_reuse(shape):
+    B, Hq, Hkv, counts = shape
+    K, V, Q, idx, cnt, idx_np, cnt_np, maxc = _attention_case("bf16", B, Hq, Hkv, 3000, counts, 21)
+    ws = hk.workspace(hk.sparse_decode_workspace(B, Hq, Hkv, maxc))
+    outs = [hk.sparse_decode(Q, K, V, idx, maxc, count=cnt, ws=ws) for _ in range(3)]
     torch.cuda.synchronize()
-    assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2)
-    assert (idx2 >= 0).all()                                 # every slot written
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
 
 
 def test_retrieve_is_deterministic():
@@ -319,3 +338,66 @@ def test_invalid_arguments_enqueue_nothing():
     with pytest.raises(hk.HkError) as e:
         hk.retrieve_topk(c, q, 128, 10, 0, 0, 3, ws=ws)
     assert e.value.status == hk.HK_ERR_WORKSPACE_TOO_SMALL
+
+
+# ----------------------------------------------------------------- fused step
+FUSED_CASES = [
+    # bits, dtype, B, Hq, Hkv, N, s, w, k, pool
+    (128, "f32", 1, 1, 1, 4096, 4, 64, 82, 0),
+    (128, "bf16", 2, 8, 2, 20000, 4, 64, 400, 5),
+    (64, "bf16", 1, 7, 1, 9000, 4, 512, 181, 0),
+    (128, "bf16", 1, 4, 4, 60, 4, 64, 82, 0),       # no candidates: the window only
+    (128, "bf16", 2, 4, 2, 1000, 0, 0, 50, 0),      # no window
+    (128, "bf16", 1, 4, 2, 1000, 4, 64, 0, 0),      # k = 0: the window only
+    (128, "bf16", 1, 2, 2, 0, 4, 64, 10, 0),        # empty context
+    (128, "f32", 2, 16, 2, 70000, 4, 512, 1400, 0), # several window slices, G = 8
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_retrieve_attend_matches_oracle_and_unfused(case):
+    bits, dtype, B, Hq, Hkv, N, s, w, k, pool = case
+    say(f"retrieve_attend {case}")
+    W = bits // 32
+    rng = np.random.default_rng(N + k + 7)
+    cap = N + 5
+    if pool:
+        table = rng.integers(0, 2 ** 32, size=(pool, W), dtype=np.uint32)
+        codes = table[rng.integers(0, pool, size=(B, Hkv, cap))]
+    else:
+        codes = rng.integers(0, 2 ** 32, size=(B, Hkv, cap, W), dtype=np.uint32)
+    qc = rng.integers(0, 2 ** 32, size=(B, Hkv, W), dtype=np.uint32)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    K = torch.from_numpy(rng.standard_normal((B, Hkv, cap, 128)).astype(np.float32) * 1.5).to(tdt).cuda()
+    V = torch.from_numpy(rng.standard_normal((B, Hkv, cap, 128)).astype(np.float32)).to(tdt).cuda()
+    Q = torch.from_numpy(rng.standard_normal((B, Hq, 128)).astype(np.float32) * 1.5).to(tdt).cuda()
+    c, q = codes_tensor(codes), codes_tensor(qc)
+    o, lse, idx, cnt = hk.retrieve_attend(c, q, bits, Q, K, V, N, s, w, k)
+    torch.cuda.synchronize()
+    o, lse, idx, cnt = o.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    Kd, Vd, Qd = (x.cpu().to(torch.float64).numpy() for x in (K, V, Q))
+    G = Hq // Hkv
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    scale = 1 / math.sqrt(128)
+    win = oracle.window_indices(N, s, w)
+    for b in range(B):
+        for h in range(Hkv):
+            sel = oracle.select_topk(codes[b, h], qc[b, h], N, s, w, k)
+            assert cnt[b, h] == sel.size and np.array_equal(idx[b, h, :sel.size], sel)
+            for g in range(G):
+                hq = h * G + g
+                o1, l1 = oracle.attend(Qd[b, hq], Kd[b, h][sel], Vd[b, h][sel], scale)
+                o2, l2 = oracle.attend(Qd[b, hq], Kd[b, h][win], Vd[b, h][win], scale)
+                ro, rl = oracle.lse_merge(np.stack([o1, o2]), np.array([l1, l2]))
+                assert np.max(np.abs(o[b, hq] - ro)) <= tol
+                assert (rl == -np.inf and lse[b, hq] == -np.inf) or abs(lse[b, hq] - rl) <= tol
+    # the unfused calls give the same result
+    if N > 0:
+        from hash_top_kv_amd.step import DecodeStep
+        st = DecodeStep(K, V, c, bits, N, s, w, k, Hq)
+        o2, l2 = st.unfused(Q, q)
+        torch.cuda.synchronize()
+        assert np.allclose(o2.cpu().numpy(), o, atol=1e-5, rtol=0)
+        l2 = l2.cpu().numpy()
+        fin = np.isfinite(lse)
+        assert np.array_equal(fin, np.isfinite(l2)) and np.allclose(l2[fin], lse[fin], atol=1e-5, rtol=0)
