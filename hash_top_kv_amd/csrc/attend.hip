@@ -27,20 +27,75 @@ __global__ __launch_bounds__(kAttThreads) void sparse_decode_kernel(
   const int bh = blockIdx.y;
   const int b = bh / Hkv;
   const int hkv = bh - b * Hkv;
-  const int qw = threadIdx.x >> 4;
   const int64_t row0 = (int64_t)b * Hq + (int64_t)hkv * G;
 
-  GroupAttention<BF16, G> ga;
+  typename AttentionCore<BF16, G>::type ga;
   ga.init(q, row0, scale_log2);
   int n = count ? count[bh] : max_count;
   n = n < 0 ? 0 : (n > max_count ? max_count : n);
   const int r0 = p * rows_per_split;
   const int r1 = min(n, r0 + rows_per_split);
-  const int nrows = r1 > r0 + qw ? (r1 - r0 - qw + kQuarterWaves - 1) / kQuarterWaves : 0;
-  const int32_t *ilist = idx + (int64_t)bh * idx_stride + r0 + qw;
-  ga.run(kc, vc, (size_t)bh * (size_t)cap, nrows,
-         [&](int j) { return ilist[(int64_t)kQuarterWaves * j]; });
+  const int32_t *ilist = idx + (int64_t)bh * idx_stride + r0;
+  ga.run_block(kc, vc, (size_t)bh * (size_t)cap, r1 > r0 ? r1 - r0 : 0,
+               [&](int r) { return ilist[r]; });
   ga.combine_store(out_o + ((int64_t)p * rows + row0) * kHeadDim, out_lse + (int64_t)p * rows + row0);
+}
+
+// Up to 64 parts of d = 128: one wavefront per output row.  Lane p reads lse_p; the
+// partial outputs (two columns per lane) are requested together with the lse's, 16 parts
+// at a time; weights are broadcast from lane p with readlane.
+__global__ __launch_bounds__(256) void lse_merge_small_kernel(
+    const float *__restrict__ o_parts, const float *__restrict__ lse_parts, int P,
+    int64_t rows, float *__restrict__ o, float *__restrict__ lse) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  constexpr int D = kHeadDim;
+  constexpr int PB = 16;
+  const float x = lane < P ? lse_parts[(int64_t)lane * rows + row] : -INFINITY;
+  float va[PB], vb[PB];
+#pragma unroll
+  for (int j = 0; j < PB; ++j) {
+    const int pp = j < P ? j : 0;
+    const float *op = o_parts + ((int64_t)pp * rows + row) * D;
+    va[j] = op[lane];
+    vb[j] = op[lane + 64];
+  }
+  float M = x;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (M == -INFINITY) {
+    o[row * D + lane] = 0.f;
+    o[row * D + lane + 64] = 0.f;
+    if (lane == 0) lse[row] = -INFINITY;
+    return;
+  }
+  const float w = lane < P ? __expf(x - M) : 0.f;
+  float S = w;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
+  float acc_a = 0.f, acc_b = 0.f;
+  for (int p0 = 0; p0 < P; p0 += PB) {
+    if (p0 > 0) {
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        const int pp = p0 + j < P ? p0 + j : 0;
+        const float *op = o_parts + ((int64_t)pp * rows + row) * D;
+        va[j] = op[lane];
+        vb[j] = op[lane + 64];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const float wf = p0 + j < P ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), p0 + j)) : 0.f;
+      acc_a = fmaf(wf, va[j], acc_a);
+      acc_b = fmaf(wf, vb[j], acc_b);
+    }
+  }
+  const float inv = 1.f / S;
+  o[row * D + lane] = acc_a * inv;
+  o[row * D + lane + 64] = acc_b * inv;
+  if (lane == 0) lse[row] = M + __logf(S);
 }
 
 // One workgroup per output row.  The row's P log-sum-exps and P x d partial outputs are
@@ -219,6 +274,11 @@ hipError_t launch_lse_merge_parts(const float *o_parts, const float *lse_parts, 
 hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int P,
                             int64_t rows, int d, float *o, float *lse, hipStream_t st) {
   if (rows == 0) return hipSuccess;
+  if (P <= 64 && d == kHeadDim) {
+    hipLaunchKernelGGL(lse_merge_small_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                       o_parts, lse_parts, P, rows, o, lse);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)rows), dim3(kMergeThreads), 0, st,
                      o_parts, lse_parts, P, rows, d, o, lse);
   return hipGetLastError();

@@ -63,22 +63,65 @@ template <> struct Row8<false> {      // 8 fp32 = 32 bytes
   }
 };
 
+// Query fragments and partial dot products.  bf16: the query stays packed (its values
+// are exact in bf16) and each lane's 8-element partial dot product is four
+// v_dot2c_f32_bf16 (exact products, fp32 accumulation) on the raw K words; fp32: the
+// query and the row are fp32.  The softmax scale is applied to the reduced dot product.
+template <bool BF16, int G> struct QueryFrag;
+template <int G> struct QueryFrag<true, G> {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  uint32_t qp[G][4];
+  __device__ void load(const void *q, int64_t row0, int col) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint4 r = Row8<true>::load(q, (size_t)(row0 + g) * kHeadDim + col * 8);
+      qp[g][0] = r.x; qp[g][1] = r.y; qp[g][2] = r.z; qp[g][3] = r.w;
+    }
+  }
+  __device__ float dot(int g, const uint4 &k) const {
+    float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qp[g][0]),
+                                              __builtin_bit_cast(bf16x2, k.x), 0.f, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qp[g][1]),
+                                        __builtin_bit_cast(bf16x2, k.y), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qp[g][2]),
+                                        __builtin_bit_cast(bf16x2, k.z), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qp[g][3]),
+                                        __builtin_bit_cast(bf16x2, k.w), a, false);
+    return a;
+  }
+};
+template <int G> struct QueryFrag<false, G> {
+  float qf[G][8];
+  __device__ void load(const void *q, int64_t row0, int col) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) Row8<false>::widen(Row8<false>::load(q, (size_t)(row0 + g) * kHeadDim + col * 8), qf[g]);
+  }
+  __device__ float dot(int g, const Row8<false>::Raw &k) const {
+    float kf[8];
+    Row8<false>::widen(k, kf);
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaf(qf[g][e], kf[e], a);
+    return a;
+  }
+};
+
 // Per-lane state of the G query heads of one group.
 template <bool BF16, int G>
 struct GroupAttention {
   using RL = Row8<BF16>;
   static constexpr int D = kHeadDim;
-  float qf[G][8];
+  QueryFrag<BF16, G> qfrag;
+  float scale_log2;
   float m[G], l[G], acc[G][8];
 
   // q [B][Hq][D]; query heads row0 .. row0 + G - 1 (row0 = b*Hq + hkv*G).
-  __device__ void init(const void *q, int64_t row0, float scale_log2) {
+  __device__ void init(const void *q, int64_t row0, float sl2) {
     const int col = threadIdx.x & 15;
+    qfrag.load(q, row0, col);
+    scale_log2 = sl2;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      RL::widen(RL::load(q, (size_t)(row0 + g) * D + col * 8), qf[g]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[g][e] *= scale_log2;
       m[g] = -INFINITY;
       l[g] = 0.f;
 #pragma unroll
@@ -123,15 +166,10 @@ struct GroupAttention {
       float s[G][kAttUnroll];
 #pragma unroll
       for (int u = 0; u < kAttUnroll; ++u) {
-        float kf[8];
-        RL::widen(kr[u], kf);
         const bool ok = grp * kAttUnroll + u < nrows;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          float a = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) a = fmaf(qf[g][e], kf[e], a);
-          a = row16_sum(a);
+          const float a = row16_sum(qfrag.dot(g, kr[u])) * scale_log2;
           s[g][u] = ok ? a : -INFINITY;
         }
       }
@@ -170,6 +208,16 @@ struct GroupAttention {
       }
       toks = toks_n;
     }
+  }
+
+  // The workgroup's rows 0 .. len-1, fetch_row(r) giving the token of row r: quarter-wave
+  // qw takes rows qw, qw + 16, ...
+  template <class FetchRow>
+  __device__ void run_block(const void *kc, const void *vc, size_t head_row0, int len,
+                            FetchRow fetch_row) {
+    const int qw = threadIdx.x >> 4;
+    const int nrows = len > qw ? (len - qw + kQuarterWaves - 1) / kQuarterWaves : 0;
+    run(kc, vc, head_row0, nrows, [&](int j) { return fetch_row(qw + kQuarterWaves * j); });
   }
 
   // Combine the 16 quarter-waves and store the normalised o (G rows of D at out_o) and
@@ -227,5 +275,175 @@ struct GroupAttention {
     }
   }
 };
+
+// ------------------------------------------------------------------ matrix-core variant
+// bf16 rows, G <= 16 query heads: per wavefront, tiles of 16 rows.
+//   scores  S^T[16 rows][16 heads] = K_tile . Q^T with four v_mfma_f32_16x16x32_bf16; lane l
+//           loads 16 bytes of row (l % 16) per k-step (dims 32*(l/16) + 8*ks ..), and holds
+//           the scores of head l % 16 for rows 4*(l/16) .. +3 -- which is already the
+//           A-operand layout of P for the second product, so no transpose is needed.
+//   output  O[16 heads][dims] += P . V_tile with eight v_mfma_f32_16x16x16_bf16, one per
+//           output dim t of 8*(l % 16) + t: lane l loads bytes 16*(l % 16) .. +15 of rows
+//           4*(l/16) .. +3 (each row read whole and coalesced by 16 lanes), and v_perm
+//           pairs element t of two rows into the B operand.
+// Softmax is online in base 2 with a lazy maximum: the running max moves (and O is
+// rescaled) only when a tile's max exceeds it by more than 8, so weights stay <= 2^8.
+// P enters the product rounded to bf16 and the normaliser sums the same rounded values.
+template <int G>
+struct GroupAttentionMfma {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  static constexpr int D = kHeadDim;
+  static constexpr float kLazy = 8.f;
+  bf16x8 qb[4];
+  float scale_log2, m, l;
+  f32x4 o[8];
+
+  __device__ void init(const void *q, int64_t row0, float sl2) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const uint16_t *qp = static_cast<const uint16_t *>(q) + (size_t)(row0 + n) * D + 32 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 v = n < G ? *reinterpret_cast<const uint4 *>(qp + 8 * ks) : make_uint4(0, 0, 0, 0);
+      qb[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+    scale_log2 = sl2;
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  struct Tile {
+    uint4 k[4], v[4];
+  };
+
+  template <class FetchRow>
+  __device__ void run_block(const void *kc, const void *vc, size_t head_row0, int len,
+                            FetchRow fetch_row) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int ntiles = (len + 15) >> 4;
+    const uint16_t *kb = static_cast<const uint16_t *>(kc);
+    const uint16_t *vb = static_cast<const uint16_t *>(vc);
+    auto load_tile = [&](int tile, Tile &T) {
+      const int r0 = tile * 16;
+      const int tok = r0 + n < len ? fetch_row(r0 + n) : 0;
+      const bool okk = r0 + n < len;
+      const uint16_t *kp = kb + (head_row0 + (size_t)tok) * D + 32 * g;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        T.k[ks] = okk ? *reinterpret_cast<const uint4 *>(kp + 8 * ks) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tv = __shfl(tok, 4 * g + j);
+        const bool okv = r0 + 4 * g + j < len;
+        T.v[j] = okv ? *reinterpret_cast<const uint4 *>(vb + (head_row0 + (size_t)tv) * D + 8 * n)
+                     : make_uint4(0, 0, 0, 0);
+      }
+    };
+    Tile cur, nxt;
+    if (wave < ntiles) load_tile(wave, cur);
+    for (int tile = wave; tile < ntiles; tile += kAttThreads / 64) {
+      if (tile + kAttThreads / 64 < ntiles) load_tile(tile + kAttThreads / 64, nxt);
+      // scores of head n, rows 4g .. 4g+3 of the tile
+      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[ks]), qb[ks], sc, 0, 0, 0);
+      float s[4];
+      const int rb = tile * 16 + 4 * g;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[j] = rb + j < len ? sc[j] * scale_log2 : -INFINITY;
+      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool need = mx > m + kLazy;                 // also the first valid tile
+      if (__ballot(need)) {
+        const float mn = need ? mx : m;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
+        l *= alpha;
+        m = mn;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float aj = __shfl(alpha, 4 * g + j);     // alpha of head 4g + j
+#pragma unroll
+          for (int t = 0; t < 8; ++t) o[t][j] *= aj;
+        }
+      }
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = s[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[j] - m);
+      const bf16x2 p01 = {(__bf16)p[0], (__bf16)p[1]};
+      const bf16x2 p23 = {(__bf16)p[2], (__bf16)p[3]};
+      const uint32_t w01 = __builtin_bit_cast(uint32_t, p01), w23 = __builtin_bit_cast(uint32_t, p23);
+      l += __uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xFFFF0000u) +
+           __uint_as_float(w23 << 16) + __uint_as_float(w23 & 0xFFFF0000u);
+      const s16x4 pa = __builtin_bit_cast(s16x4, uint2{w01, w23});
+      const uint32_t *v0 = reinterpret_cast<const uint32_t *>(&cur.v[0]);
+      const uint32_t *v1 = reinterpret_cast<const uint32_t *>(&cur.v[1]);
+      const uint32_t *v2 = reinterpret_cast<const uint32_t *>(&cur.v[2]);
+      const uint32_t *v3 = reinterpret_cast<const uint32_t *>(&cur.v[3]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t a = __builtin_amdgcn_perm(v1[t >> 1], v0[t >> 1], sel);
+        const uint32_t b = __builtin_amdgcn_perm(v3[t >> 1], v2[t >> 1], sel);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, uint2{a, b}), o[t], 0, 0, 0);
+      }
+      cur = nxt;
+    }
+  }
+
+  __device__ void combine_store(float *out_o, float *out_lse) {
+    __shared__ float s_m[kAttThreads / 64][G];
+    __shared__ float s_l[kAttThreads / 64][G];
+    __shared__ float s_o[kAttThreads / 64][G][D];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    if (g == 0 && n < G) {
+      s_m[wave][n] = m;
+      s_l[wave][n] = lt;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = 4 * g + j;
+      if (h < G) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) s_o[wave][h][8 * n + t] = o[t][j];
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * D; i += kAttThreads) {
+      const int h = i / D, e = i - h * D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kAttThreads / 64; ++w) M = fmaxf(M, s_m[w][h]);
+      float L = 0.f, O = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kAttThreads / 64; ++w) {
+          const float f = __builtin_amdgcn_exp2f(s_m[w][h] - M);
+          L += s_l[w][h] * f;
+          O += s_o[w][h][e] * f;
+        }
+      }
+      const bool empty = !(L > 0.f);
+      out_o[(size_t)h * D + e] = empty ? 0.f : O / L;
+      if (e == 0) out_lse[h] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
+    }
+  }
+};
+
+// The attention core used for an element type: matrix cores for bf16, VALU for fp32.
+template <bool BF16, int G> struct AttentionCore { using type = GroupAttention<false, G>; };
+template <int G> struct AttentionCore<true, G> { using type = GroupAttentionMfma<G>; };
 
 }  // namespace hk

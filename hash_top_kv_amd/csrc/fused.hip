@@ -16,56 +16,92 @@
 namespace hk {
 namespace {
 
-// grid (S + Sw, B*Hkv).  Blocks c < S: chunk c of the retrieval; blocks c >= S: window
-// slice c - S.  Writes the normalised partial of part c.
+// grid (Sc + Sw, B*Hkv).  Blocks c < Sc cover chunks [c*CPB, (c+1)*CPB) of the
+// retrieval; blocks c >= Sc cover window slice c - Sc.  Block c writes the normalised
+// partial of part c.  A chunk block compacts its chunks' selected tokens into an LDS
+// list (and into the head's index list) and attends over the list; when a list would
+// overflow LDS it is attended and emptied first, so any selection size works.
+constexpr int kListMax = 4096;
+constexpr int kMaxCpb = 4;                 // chunks per workgroup, bounded by registers
+
 template <int LPT, bool BF16, int G>
 __global__ __launch_bounds__(kScanThreads) void emit_attend_kernel(
     const uint32_t *__restrict__ stash, const int4 *__restrict__ meta,
-    const int2 *__restrict__ params, int S, int64_t lo, int k, int32_t *__restrict__ idx,
-    const void *__restrict__ q, const void *__restrict__ kc, const void *__restrict__ vc,
-    int Hq, int Hkv, int64_t cap, float scale_log2, int win_sinks, int64_t win_local0,
-    int n_win, int win_rows, float *__restrict__ part_o, float *__restrict__ part_lse,
-    int64_t rows) {
+    const int2 *__restrict__ params, int S, int CPB, int Sc, int64_t lo, int k,
+    int32_t *__restrict__ idx, const void *__restrict__ q, const void *__restrict__ kc,
+    const void *__restrict__ vc, int Hq, int Hkv, int64_t cap, float scale_log2,
+    int win_sinks, int64_t win_local0, int n_win, int win_rows, float *__restrict__ part_o,
+    float *__restrict__ part_lse, int64_t rows) {
   constexpr int CH = kScanThreads * LPT;
-  __shared__ int32_t sel[CH];
+  static_assert(CH <= kListMax, "a chunk's selection must fit the list");
+  __shared__ int32_t sel[kListMax];
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / Hkv;
   const int hkv = bh - b * Hkv;
   const int t = threadIdx.x;
-  const int qw = t >> 4;
   const int64_t row0 = (int64_t)b * Hq + (int64_t)hkv * G;
   const size_t head_row0 = (size_t)bh * (size_t)cap;
 
-  GroupAttention<BF16, G> ga;
-  ga.init(q, row0, scale_log2);
-  if (c < S) {
+  // The query fragment is loaded after the chunks are compacted: its load then issues
+  // with the first K/V rows and does not hold registers through the compaction.
+  typename AttentionCore<BF16, G>::type ga;
+  bool ga_ready = false;
+  auto attend_list = [&](int len) {
+    if (!ga_ready) {
+      ga.init(q, row0, scale_log2);
+      ga_ready = true;
+    }
+    ga.run_block(kc, vc, head_row0, len, [&](int r) { return sel[r]; });
+  };
+  if (c < Sc) {
     const int2 pr = params[bh];
-    const int4 mt = meta[(int64_t)bh * S + c];
-    const uint32_t *sp = stash + ((int64_t)bh * S + c) * stash_words_per_chunk<LPT>();
-    uint32_t w[LPT / 4];
-#pragma unroll
-    for (int i4 = 0; i4 < LPT / 4; ++i4) w[i4] = sp[i4 * kScanThreads + t];
     const int T = pr.x;
     const int quota = pr.y;
-    const int nsel = T >= 0 ? chunk_selected(mt, quota) : 0;
-    if (nsel > 0) {
-      int32_t *out = idx + (int64_t)bh * k;
-      emit_chunk<LPT>(w, T, quota, mt.x, mt.y, lo + (int64_t)c * CH,
+    const int c0 = c * CPB;
+    const int c1 = min(S, c0 + CPB);
+    int len = 0;
+    int32_t *out = idx + (int64_t)bh * k;
+    // Every chunk's stash words and counts are requested before any is compacted.
+    uint32_t wall[kMaxCpb][LPT / 4];
+    int4 mall[kMaxCpb];
+#pragma unroll
+    for (int i = 0; i < kMaxCpb; ++i) {
+      const int ch = c0 + i < c1 ? c0 + i : c0;
+      mall[i] = meta[(int64_t)bh * S + ch];
+      const uint32_t *sp = stash + ((int64_t)bh * S + ch) * stash_words_per_chunk<LPT>();
+#pragma unroll
+      for (int i4 = 0; i4 < LPT / 4; ++i4) wall[i][i4] = sp[i4 * kScanThreads + t];
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxCpb; ++i) {
+      const int ch = c0 + i;
+      if (ch >= c1) break;
+      const int4 mt = mall[i];
+      const int nsel = T >= 0 ? chunk_selected(mt, quota) : 0;
+      if (nsel == 0) continue;
+      if (len + nsel > kListMax) {
+        attend_list(len);
+        __syncthreads();                     // the list is reused
+        len = 0;
+      }
+      const int base = len;
+      emit_chunk<LPT>(wall[i], T, quota, mt.x, mt.y, lo + (int64_t)ch * CH,
                       [&](int pos, int lpos, int32_t tok) {
                         out[pos] = tok;
-                        sel[lpos] = tok;
+                        sel[base + lpos] = tok;
                       });
       __syncthreads();
+      len += nsel;
     }
-    const int nrows = nsel > qw ? (nsel - qw + kQuarterWaves - 1) / kQuarterWaves : 0;
-    ga.run(kc, vc, head_row0, nrows, [&](int j) { return sel[qw + kQuarterWaves * j]; });
+    if (len > 0) attend_list(len);
+    if (!ga_ready) ga.init(q, row0, scale_log2);
   } else {
-    const int r0 = (c - S) * win_rows;
+    ga.init(q, row0, scale_log2);
+    const int r0 = (c - Sc) * win_rows;
     const int r1 = min(n_win, r0 + win_rows);
-    const int nrows = r1 > r0 + qw ? (r1 - r0 - qw + kQuarterWaves - 1) / kQuarterWaves : 0;
-    ga.run(kc, vc, head_row0, nrows, [&](int j) {
-      const int r = r0 + qw + kQuarterWaves * j;
+    ga.run_block(kc, vc, head_row0, r1 > r0 ? r1 - r0 : 0, [&](int rr) {
+      const int r = r0 + rr;
       return r < win_sinks ? r : (int)(win_local0 + (r - win_sinks));
     });
   }
@@ -78,9 +114,9 @@ void fused_launch(const FusedPlan &p, const uint32_t *stash, const int4 *meta,
                   const void *vc, int Hq, int Hkv, int64_t cap, float scale_log2, float *po,
                   float *pl, int64_t rows, hipStream_t st) {
   hipLaunchKernelGGL((emit_attend_kernel<LPT, BF16, G>), dim3(p.parts, p.r.BH),
-                     dim3(kScanThreads), 0, st, stash, meta, params, p.r.S, p.r.lo, k, idx, q,
-                     kc, vc, Hq, Hkv, cap, scale_log2, p.win_sinks, p.win_local0, p.n_win,
-                     p.win_rows, po, pl, rows);
+                     dim3(kScanThreads), 0, st, stash, meta, params, p.r.S, p.cpb, p.Sc, p.r.lo,
+                     k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2, p.win_sinks, p.win_local0,
+                     p.n_win, p.win_rows, po, pl, rows);
 }
 
 template <int LPT, bool BF16>
@@ -113,8 +149,17 @@ FusedPlan plan_fused(int bits, int B, int Hq, int Hkv, int64_t n_ctx, int n_sink
   p.win_sinks = (int)sinks;
   p.win_local0 = local0;
   p.n_win = (int)(sinks + (n_ctx > local0 ? n_ctx - local0 : 0));
+  // Chunks per workgroup: about 64 selected rows per workgroup (four 16-row tiles, one
+  // per wavefront), while keeping at least 128 workgroups.
+  const int64_t chunks = (int64_t)p.r.BH * p.r.S;
+  const int64_t per_chunk = p.r.S > 0 ? (p.r.keff + p.r.S - 1) / p.r.S : 1;
+  int cpb = 1;
+  while (cpb < kMaxCpb && per_chunk * cpb < 64 && chunks / (2 * cpb) >= 128) cpb *= 2;
+  p.cpb = cpb;
+  p.Sc = (p.r.S + cpb - 1) / cpb;
+  // Window slices: about 64 rows each, fewer when the chunk blocks alone are few.
   p.Sw = (p.n_win + p.win_rows - 1) / p.win_rows;
-  p.parts = p.r.S + p.Sw;
+  p.parts = p.Sc + p.Sw;
   size_t off = p.r.total;
   const size_t rows = (size_t)B * Hq;
   p.off_o = off;

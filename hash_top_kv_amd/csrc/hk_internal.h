@@ -61,11 +61,11 @@ hipError_t launch_lse_merge_parts(const float *o_parts, const float *lse_parts, 
 
 // ---------------------------------------------------------------- fused step
 // hk_retrieve_attend: the retrieval workspace (RetrievePlan) followed by one normalised
-// partial per chunk of each head and per window slice: o [parts][B*Hq][d], lse
-// [parts][B*Hq], parts = S + window slices.
+// partial per group of `cpb` chunks of each head and per window slice: o [parts][B*Hq][d],
+// lse [parts][B*Hq], parts = Sc + Sw.
 struct FusedPlan {
   RetrievePlan r;
-  int win_sinks = 0, n_win = 0, win_rows = 64, Sw = 0, parts = 0, G = 1;
+  int win_sinks = 0, n_win = 0, win_rows = 64, Sw = 0, parts = 0, G = 1, cpb = 1, Sc = 0;
   int64_t win_local0 = 0;
   size_t off_o = 0, off_lse = 0, total = 0;
 };

@@ -190,6 +190,7 @@ def test_sparse_decode_matches_oracle(case):
     for b in range(B):
         lists = [idx_np[b, h, :cnt_np[b, h]] for h in range(Hkv)]
         ro, rl = oracle.sparse_attention(Qd[b], Kd[b], Vd[b], lists, scale)
+        say(f"  batch {b}: max |o - oracle| = {np.max(np.abs(o[b] - ro)):.2e}")
         assert np.max(np.abs(o[b] - ro)) <= tol
         fin = np.isfinite(rl)
         assert np.array_equal(fin, np.isfinite(lse[b]))
@@ -380,6 +381,7 @@ def test_retrieve_attend_matches_oracle_and_unfused(case):
     tol = 1e-5 if dtype == "f32" else 2e-2
     scale = 1 / math.sqrt(128)
     win = oracle.window_indices(N, s, w)
+    worst = 0.0
     for b in range(B):
         for h in range(Hkv):
             sel = oracle.select_topk(codes[b, h], qc[b, h], N, s, w, k)
@@ -391,13 +393,17 @@ def test_retrieve_attend_matches_oracle_and_unfused(case):
                 ro, rl = oracle.lse_merge(np.stack([o1, o2]), np.array([l1, l2]))
                 assert np.max(np.abs(o[b, hq] - ro)) <= tol
                 assert (rl == -np.inf and lse[b, hq] == -np.inf) or abs(lse[b, hq] - rl) <= tol
+                worst = max(worst, float(np.max(np.abs(o[b, hq] - ro))))
+    say(f"  max |o - oracle| = {worst:.2e}")
     # the unfused calls give the same result
     if N > 0:
         from hash_top_kv_amd.step import DecodeStep
         st = DecodeStep(K, V, c, bits, N, s, w, k, Hq)
         o2, l2 = st.unfused(Q, q)
         torch.cuda.synchronize()
-        assert np.allclose(o2.cpu().numpy(), o, atol=1e-5, rtol=0)
+        # bf16 paths round the softmax weights to bf16 before the P.V product, against
+        # running maxima that differ between the two schedules
+        assert np.allclose(o2.cpu().numpy(), o, atol=tol, rtol=0)
         l2 = l2.cpu().numpy()
         fin = np.isfinite(lse)
-        assert np.array_equal(fin, np.isfinite(l2)) and np.allclose(l2[fin], lse[fin], atol=1e-5, rtol=0)
+        assert np.array_equal(fin, np.isfinite(l2)) and np.allclose(l2[fin], lse[fin], atol=tol, rtol=0)
