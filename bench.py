@@ -1,23 +1,25 @@
 """Benchmark of the binary-hash KV retrieval decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--hash i]
-                    [--replicas R] [--no-cpu] [--graph] [--prefill]
+                    [--replicas R] [--no-cpu] [--prefill] [--unfused]
 
 Default workload: retrieval at 512K tokens -- 8 KV heads x 524,288 cached 128-bit codes
 (uniform random bits plus 1% planted near neighbours of the query code), top-1024 per
 head, then exact attention over the 1024 selected bf16 K/V rows of each head.  One step
-is hk_hamming_scan + hk_topk_select (= hk_retrieve_topk) + hk_sparse_decode.  Other
-workloads (--workload 0/1/3/4) run the whole step: hk_encode_query, hk_retrieve_topk,
-hk_sparse_decode over the top-k list and over the sink + local window, hk_lse_merge.
+is hk_hamming_scan + hk_select_attend (together hk_retrieve_attend).  Other workloads
+(--workload 0/1/3/4) run the whole step after the keys were encoded: hk_encode_query,
+hk_hamming_scan, hk_select_attend (top-k list and sink + local window, merged).  With
+--unfused the separate calls run instead (hk_retrieve_topk, hk_sparse_decode, ...).
 
 Inputs are resident in HBM before timing.  R replicas of the per-step inputs (codes,
 query codes, queries) rotate so that the bytes a step reads are not left in the 256 MB
-Infinity Cache or the L2 by the previous steps (R * code bytes >> 256 MB).
+Infinity Cache or the L2 by the previous steps.
 
 Prints ONE JSON line.  `value` is microseconds per decode step (lower is better).
 `roofline` describes the dominant kernel (the Hamming scan): algorithmic bytes per
-launch over its average duration, timed with HIP events on the launch stream.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+launch over its average duration, timed with HIP events on the launch stream around
+back-to-back launches.  `cpu_baseline` times the CPU oracle on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -38,8 +40,10 @@ METRIC = "retrieve+sparse-attn µs/decode step @512K tok; achieved HBM GB/s vs p
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 KERNEL_SOURCES = ["include/hk.h", "hash_top_kv_amd/csrc/hk_internal.h",
+                  "hash_top_kv_amd/csrc/select_core.h", "hash_top_kv_amd/csrc/attend_core.h",
                   "hash_top_kv_amd/csrc/retrieve.hip", "hash_top_kv_amd/csrc/attend.hip",
-                  "hash_top_kv_amd/csrc/encode.hip", "hash_top_kv_amd/csrc/api.hip"]
+                  "hash_top_kv_amd/csrc/fused.hip", "hash_top_kv_amd/csrc/encode.hip",
+                  "hash_top_kv_amd/csrc/api.hip"]
 
 
 def source_digest(files=KERNEL_SOURCES) -> str:
@@ -105,7 +109,9 @@ class Timer:
 
 
 def build_retrieval_case(args, torch, hk, synth):
-    """Workload 2: given codes, per-step hk_hamming_scan + hk_topk_select + hk_sparse_decode."""
+    """Workload 2: given codes; a step is hk_hamming_scan + hk_select_attend (the fused
+    hk_retrieve_attend), or with --unfused hk_hamming_scan + hk_topk_select +
+    hk_sparse_decode."""
     wl = synth.WORKLOADS[2]
     R = args.replicas
     kv = synth.make_kv(wl)
@@ -129,24 +135,21 @@ def build_retrieval_case(args, torch, hk, synth):
     else:
         ws = hk.workspace(hk.retrieve_attend_workspace(128, B, wl.Hq, Hkv, N, 0, 0, k))
 
-    def step(i, timers=None):
+    def scan(i):
         rp = reps[i % R]
-        if timers:
-            timers[0].start()
         hk.hamming_scan(rp["codes"], rp["qcodes"], 128, N, 0, 0, k, ws)
-        if timers:
-            timers[0].stop()
-            timers[1].start()
+
+    def rest(i):
+        rp = reps[i % R]
         if args.unfused:
             hk.topk_select(128, B, Hkv, N, 0, 0, k, idx, count, ws)
             hk.sparse_decode(rp["Q"], K, V, idx, k, count=count, o=o, lse=lse, ws=wsd)
         else:
             hk.select_attend(128, rp["Q"], K, V, N, 0, 0, k, idx, count, o, lse, ws)
-        if timers:
-            timers[1].stop()
 
     def check():
-        step(0)
+        scan(0)
+        rest(0)
         torch.cuda.synchronize()
         pos, dl = reps[0]["planted"]
         got = idx.cpu().numpy()
@@ -157,18 +160,18 @@ def build_retrieval_case(args, torch, hk, synth):
 
     scan_bytes = B * Hkv * N * 16
     gather_bytes = B * Hkv * k * 2 * 128 * 2 + B * wl.Hq * 128 * 2
-    names = ["hamming_scan", "select+attend"]
     info = {"workload": wl.name, "B": B, "Hq": wl.Hq, "Hkv": Hkv, "N": N, "k": k,
             "code_bits": 128, "kv_dtype": "bf16", "replicas": R,
-            "rotating_code_bytes": R * scan_bytes}
-    info["step"] = ("hk_hamming_scan + hk_topk_select + hk_sparse_decode" if args.unfused
-                    else "hk_hamming_scan + hk_select_attend (= hk_retrieve_attend)")
-    return step, check, names, {"hamming_scan": scan_bytes, "select+attend": gather_bytes}, info, \
-        {"wl": wl, "reps": reps, "kv": kv}
+            "rotating_code_bytes": R * scan_bytes,
+            "step": ("hk_hamming_scan + hk_topk_select + hk_sparse_decode" if args.unfused
+                     else "hk_hamming_scan + hk_select_attend (= hk_retrieve_attend)")}
+    parts = [("hamming_scan", scan, scan_bytes), ("select+attend", rest, gather_bytes)]
+    return parts, check, info, {"wl": wl, "reps": reps, "kv": kv}
 
 
 def build_full_case(args, torch, hk, synth):
-    """Workloads 0, 1, 3, 4: the whole step through DecodeStep, keys encoded beforehand."""
+    """Workloads 0, 1, 3, 4: hk_encode_query + hk_hamming_scan + hk_select_attend (the
+    whole step after the keys were encoded), or with --unfused the separate calls."""
     from hash_top_kv_amd.step import DecodeStep
     wl = synth.WORKLOADS[args.workload]
     spec = wl.hashes[args.hash]
@@ -182,32 +185,50 @@ def build_full_case(args, torch, hk, synth):
     codes = torch.empty((wl.B, wl.Hkv, wl.N, spec.words), dtype=torch.int32, device="cuda")
     hk.encode_keys(h, K, codes)
     torch.cuda.synchronize()
-    step_obj = DecodeStep(K, V, codes, spec.bits, wl.N, wl.n_sink, wl.n_local, wl.k, wl.Hq, h)
+    # Copies of the code cache so that consecutive steps read codes from HBM, not from
+    # the 256 MB Infinity Cache (only needed while the codes are small).
+    C = wl.N - wl.n_sink - wl.n_local
+    scan_bytes = wl.B * wl.Hkv * C * spec.bits // 8
+    ncopies = 1 if scan_bytes * 1 >= (512 << 20) else max(1, min(R, -(-(512 << 20) // scan_bytes)))
+    code_sets = [codes] + [codes.clone() for _ in range(ncopies - 1)]
+    steps = [DecodeStep(K, V, cs, spec.bits, wl.N, wl.n_sink, wl.n_local, wl.k, wl.Hq, h)
+             for cs in code_sets]
     Qs = [synth.to_device(synth.make_q(wl, replica=r), wl.dtype) for r in range(R)]
 
-    run = step_obj.unfused if args.unfused else step_obj
+    def st(i):
+        return steps[i % len(steps)]
 
-    def step(i, timers=None):
-        if timers:
-            timers[0].start()
-        run(Qs[i % R])
-        if timers:
-            timers[0].stop()
+    def enc(i):
+        st(i).encode(Qs[i % R])
+
+    def scan(i):
+        st(i).scan(st(i).qcodes)
+
+    def rest(i):
+        st(i).select_attend(Qs[i % R])
+
+    def unfused(i):
+        st(i).unfused(Qs[i % R])
 
     def check():
-        step(0)
+        st(0)(Qs[0])
         torch.cuda.synchronize()
-        assert bool((step_obj.count == step_obj.keff).all())
+        assert bool((st(0).count == st(0).keff).all())
 
-    C = wl.N - wl.n_sink - wl.n_local
     esz = 4 if wl.dtype == "f32" else 2
-    scan_bytes = wl.B * wl.Hkv * C * spec.bits // 8
-    gather_bytes = wl.B * wl.Hkv * (step_obj.keff + step_obj.n_win) * 2 * 128 * esz
+    s0 = steps[0]
+    gather_bytes = wl.B * wl.Hkv * (s0.keff + s0.n_win) * 2 * 128 * esz
     info = {"workload": wl.name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "N": wl.N, "k": wl.k,
             "n_sink": wl.n_sink, "n_local": wl.n_local, "hash": f"{spec.kind}-{spec.bits}",
-            "kv_dtype": wl.dtype, "replicas": R}
-    return step, check, ["decode_step"], {"hamming_scan": scan_bytes, "sparse_decode": gather_bytes}, \
-        info, {"wl": wl, "K": K, "h": h, "codes": codes, "spec": spec}
+            "kv_dtype": wl.dtype, "replicas": R, "code_copies": ncopies,
+            "step": ("hk_encode_query + hk_retrieve_topk + 2 x hk_sparse_decode + hk_lse_merge"
+                     if args.unfused else "hk_encode_query + hk_hamming_scan + hk_select_attend")}
+    if args.unfused:
+        parts = [("decode_step", unfused, None)]
+    else:
+        parts = [("encode_query", enc, None), ("hamming_scan", scan, scan_bytes),
+                 ("select+attend", rest, gather_bytes)]
+    return parts, check, info, {"wl": wl, "K": K, "h": h, "codes": codes, "spec": spec}
 
 
 def time_prefill(torch, hk, ctx, steps):
@@ -302,8 +323,12 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "launches": 10}))
         return
     build = build_retrieval_case if args.workload == 2 else build_full_case
-    step, check, names, alg_bytes, info, ctx = build(args, torch, hk, synth)
+    parts, check, info, ctx = build(args, torch, hk, synth)
     check()
+
+    def step(i):
+        for _, fn, _ in parts:
+            fn(i)
 
     for i in range(args.warmup):
         step(i)
@@ -320,34 +345,56 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # Per-call durations, live, with events on the launch stream around each call.
     kern = {}
     if not args.no_kernel_timing:
-        timers = [Timer(torch, args.steps) for _ in names]
+        # Each part of the step with an event pair around it inside the step loop (the
+        # pair adds its own overhead, so these figures are upper bounds).
+        timers = [Timer(torch, args.steps) for _ in parts]
         for i in range(args.steps):
-            step(i, timers)
+            for (name, fn, _), t in zip(parts, timers):
+                t.start()
+                fn(i)
+                t.stop()
         torch.cuda.synchronize()
-        for n, t in zip(names, timers):
+        for (name, fn, nbytes), t in zip(parts, timers):
             ms = t.mean_ms()
-            ent = {"us": round(ms * 1e3, 3)}
-            if n in alg_bytes:
-                ent["alg_bytes"] = alg_bytes[n]
-                ent["gbs"] = round(alg_bytes[n] / ms / 1e6, 1)
-                ent["frac_of_peak"] = round(alg_bytes[n] / ms / 1e6 / HBM_PEAK_GBS, 4)
-            kern[n] = ent
+            ent = {"us_in_step": round(ms * 1e3, 3)}
+            if nbytes:
+                ent["alg_bytes"] = nbytes
+                ent["gbs_in_step"] = round(nbytes / ms / 1e6, 1)
+            kern[name] = ent
+        # The Hamming scan alone, launched back to back over rotating code replicas
+        # between one event pair: its average launch duration.
+        scan = [p for p in parts if p[0] == "hamming_scan"]
+        if scan:
+            _, fn, nbytes = scan[0]
+            n = max(args.steps, 50)
+            for i in range(8):
+                fn(i)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(n):
+                fn(i)
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / n
+            kern["hamming_scan"].update({"us_per_launch": round(ms * 1e3, 3),
+                                         "gbs": round(nbytes / ms / 1e6, 1),
+                                         "frac_of_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)})
 
     roofline = None
-    if "hamming_scan" in kern:
-        a = kern["hamming_scan"]["gbs"]
+    sc = kern.get("hamming_scan", {})
+    if "gbs" in sc:
+        a = sc["gbs"]
         roofline = {"kernel": "hamming_scan", "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4),
                     "traffic": read_traffic(f"hamming_scan_w{args.workload}"),
-                    "alg_bytes_per_launch": alg_bytes["hamming_scan"],
-                    "us_per_launch": kern["hamming_scan"]["us"]}
+                    "alg_bytes_per_launch": sc["alg_bytes"], "us_per_launch": sc["us_per_launch"]}
     out = {"metric": METRIC, "value": round(ms_step * 1e3, 3), "unit": "us/step", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
            "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
-           "dtype": "u32+f32", "data": "synthetic",
+           "dtype": "u32+" + ("f32" if info.get("kv_dtype") == "f32" else "bf16"),
+           "data": "synthetic",
            "config": info, "roofline": roofline, "kernels": kern,
            "wall_ms_timed_region": round(wall_ms, 3)}
     if args.prefill and args.workload != 2:

@@ -3,6 +3,8 @@
 Sequences the C entry points with preallocated buffers (no allocation per step, so a
 step can be captured in a HIP graph):
 
+    hk_encode_query -> hk_hamming_scan -> hk_select_attend   (fused; = hk_retrieve_attend)
+or, through the separate calls (DecodeStep.unfused):
     hk_encode_query -> hk_retrieve_topk -> hk_sparse_decode (top-k list)
                     -> hk_sparse_decode (sink + local window) -> hk_lse_merge
 
@@ -17,9 +19,9 @@ import math
 
 import torch
 
-from . import (Hash, encode_query, lse_merge, retrieve_attend, retrieve_attend_workspace,
-               retrieve_topk_workspace, sparse_decode, sparse_decode_workspace, window_indices,
-               workspace, _check, _ptr, _stream, lib)
+from . import (Hash, encode_query, hamming_scan, lse_merge, retrieve_attend_workspace,
+               retrieve_topk_workspace, select_attend, sparse_decode, sparse_decode_workspace,
+               window_indices, workspace, _check, _ptr, _stream, lib)
 
 
 class DecodeStep:
@@ -61,10 +63,21 @@ class DecodeStep:
         hk_encode_query, then hk_retrieve_attend (retrieval, attention over the selected
         tokens and the window, merge)."""
         if qcodes is None:
-            qcodes = encode_query(self.hash, q, self.Hkv, self.qcodes)
-        retrieve_attend(self.codes, qcodes, self.bits, q, self.K, self.V, self.n_ctx,
-                        self.n_sink, self.n_local, self.k, scale=self.scale, idx=self.idx,
-                        count=self.count, o=self.o, lse=self.lse, ws=self.ws_f)
+            qcodes = self.encode(q)
+        self.scan(qcodes)
+        return self.select_attend(q)
+
+    # The parts of a fused step, in order (hk_retrieve_attend = scan + select_attend).
+    def encode(self, q):
+        return encode_query(self.hash, q, self.Hkv, self.qcodes)
+
+    def scan(self, qcodes):
+        hamming_scan(self.codes, qcodes, self.bits, self.n_ctx, self.n_sink, self.n_local,
+                     self.k, self.ws_f)
+
+    def select_attend(self, q):
+        select_attend(self.bits, q, self.K, self.V, self.n_ctx, self.n_sink, self.n_local,
+                      self.k, self.idx, self.count, self.o, self.lse, self.ws_f, scale=self.scale)
         return self.o, self.lse
 
     def unfused(self, q: torch.Tensor, qcodes: torch.Tensor | None = None):
