@@ -20,6 +20,11 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhk.so")
 SOURCES = ["api.hip", "retrieve.hip", "attend.hip", "fused.hip", "encode.hip"]
 ARCH = "gfx950"
+# The attention kernels keep their matrix-core accumulators in ordinary VGPRs: the
+# online-softmax rescale multiplies them in place, which with accumulation registers
+# costs a copy out and back per tile and a larger register footprint.
+EXTRA_FLAGS = {"attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -37,7 +42,8 @@ def common_flags() -> list[str]:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

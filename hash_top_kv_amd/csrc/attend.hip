@@ -15,6 +15,8 @@
 namespace hk {
 namespace {
 
+constexpr int kMaxSliceRows = 256;         // rows_per_split never exceeds this
+
 // grid (P, B*Hkv).  Writes either the final (o, lse) of its query heads (P == 1) or the
 // normalised partial of slice p into out_o + p*rows*d, out_lse + p*rows.
 template <bool BF16, int G>
@@ -29,15 +31,20 @@ __global__ __launch_bounds__(kAttThreads) void sparse_decode_kernel(
   const int hkv = bh - b * Hkv;
   const int64_t row0 = (int64_t)b * Hq + (int64_t)hkv * G;
 
-  typename AttentionCore<BF16, G>::type ga;
-  ga.init(q, row0, scale_log2);
+  // The slice's token indices are staged in LDS first (one coalesced read), so the
+  // row gathers never wait on an index load.
+  __shared__ int32_t s_idx[kMaxSliceRows];
   int n = count ? count[bh] : max_count;
   n = n < 0 ? 0 : (n > max_count ? max_count : n);
   const int r0 = p * rows_per_split;
   const int r1 = min(n, r0 + rows_per_split);
+  const int len = r1 > r0 ? r1 - r0 : 0;
   const int32_t *ilist = idx + (int64_t)bh * idx_stride + r0;
-  ga.run_block(kc, vc, (size_t)bh * (size_t)cap, r1 > r0 ? r1 - r0 : 0,
-               [&](int r) { return ilist[r]; });
+  for (int r = threadIdx.x; r < len; r += kAttThreads) s_idx[r] = ilist[r];
+  typename AttentionCore<BF16, G>::type ga;
+  ga.init(q, row0, scale_log2);
+  __syncthreads();
+  ga.run_block(kc, vc, (size_t)bh * (size_t)cap, len, [&](int r) { return s_idx[r]; });
   ga.combine_store(out_o + ((int64_t)p * rows + row0) * kHeadDim, out_lse + (int64_t)p * rows + row0);
 }
 

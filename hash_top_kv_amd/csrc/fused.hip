@@ -157,8 +157,9 @@ FusedPlan plan_fused(int bits, int B, int Hq, int Hkv, int64_t n_ctx, int n_sink
   while (cpb < kMaxCpb && per_chunk * cpb < 64 && chunks / (2 * cpb) >= 128) cpb *= 2;
   p.cpb = cpb;
   p.Sc = (p.r.S + cpb - 1) / cpb;
-  // Window slices: about 64 rows each, fewer when the chunk blocks alone are few.
-  p.Sw = (p.n_win + p.win_rows - 1) / p.win_rows;
+  // Window slices: at most 64 rows each, of equal size.
+  p.Sw = (p.n_win + 63) / 64;
+  p.win_rows = p.Sw > 0 ? (p.n_win + p.Sw - 1) / p.Sw : 64;
   p.parts = p.Sc + p.Sw;
   size_t off = p.r.total;
   const size_t rows = (size_t)B * Hq;

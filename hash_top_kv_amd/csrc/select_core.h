@@ -37,15 +37,13 @@ __device__ __forceinline__ void emit_chunk(const uint32_t *w, int T, int quota, 
   const int wave = t >> 6;
   const int lane = t & 63;
   const uint64_t below_me = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint64_t blt[LPT], beq[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int d = (w[i >> 2] >> (8 * (i & 3))) & 0xFF;
-    blt[i] = __ballot(d < T);
-    beq[i] = __ballot(d == T);
+    const uint64_t blt = __ballot(d < T), beq = __ballot(d == T);
     if (lane == 0) {
-      cnt[0][i * NW + wave] = (uint32_t)__popcll(blt[i]);
-      cnt[1][i * NW + wave] = (uint32_t)__popcll(beq[i]);
+      cnt[0][i * NW + wave] = (uint32_t)__popcll(blt);
+      cnt[1][i * NW + wave] = (uint32_t)__popcll(beq);
     }
   }
   __syncthreads();
@@ -61,12 +59,15 @@ __device__ __forceinline__ void emit_chunk(const uint32_t *w, int T, int quota, 
   }
   __syncthreads();
   const int first = lt_before + (eq_before < quota ? eq_before : quota);
+  // The ballots are taken again rather than kept from the counting pass: 2*LPT wave masks
+  // held across the barriers would cost as many scalar or vector register pairs.
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int d = (w[i >> 2] >> (8 * (i & 3))) & 0xFF;
+    const uint64_t blt = __ballot(d < T), beq = __ballot(d == T);
     if (d > T) continue;
-    const int lt_rank = lt_before + (int)cnt[0][i * NW + wave] + __popcll(blt[i] & below_me);
-    const int eq_rank = eq_before + (int)cnt[1][i * NW + wave] + __popcll(beq[i] & below_me);
+    const int lt_rank = lt_before + (int)cnt[0][i * NW + wave] + __popcll(blt & below_me);
+    const int eq_rank = eq_before + (int)cnt[1][i * NW + wave] + __popcll(beq & below_me);
     const int32_t tok = (int32_t)(tok0 + i * kScanThreads + t);
     int pos = -1;
     if (d < T) pos = lt_rank + min(eq_rank, quota);
