@@ -191,8 +191,7 @@ hipError_t launch_fused_attend(const FusedPlan &p, const void *q, const void *kc
                                     sl2, po, pl, rows, st);                                  \
   else fused_dispatch_g<L, false>(p, stash, meta, params, k, idx, q, kc, vc, Hq, Hkv, cap,   \
                                   sl2, po, pl, rows, st);
-    if (p.r.lpt == 16) { HK_LPT(16) }
-    else if (p.r.lpt == 8) { HK_LPT(8) }
+    if (p.r.lpt == 8) { HK_LPT(8) }
     else { HK_LPT(4) }
 #undef HK_LPT
     hipError_t e = hipGetLastError();

@@ -18,14 +18,15 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ---------------------------------------------------------------- retrieval plan
 // Candidate tokens of each (b, KV head) are cut into S chunks of `ch` tokens; one
 // workgroup scans one chunk.  The workspace holds
-//   stash  [BH][S*ch] uint8   per-token Hamming distance (255 past the last candidate)
-//   cum    [BH][S][NB] uint32 per-chunk inclusive cumulative distance histogram
-//   meta   [BH][S] int4      (#dist<T before chunk, #dist==T before chunk, #<T, #==T)
-//   params [BH] int2         (threshold T or -1, tie quota)
+//   stash  [BH][S*ch] uint8     per-token Hamming distance (255 past the last candidate)
+//   hist   [BH][S][BINS + BINS/8] uint32 per-chunk histogram of distances 0 .. BINS-1
+//                               (BINS = bits), then counts of 8 consecutive distances
+//   meta   [BH][S] int4        (#dist<T before chunk, #dist==T before chunk, #<T, #==T)
+//   params [BH] int2           (threshold T or -1, tie quota)
 struct RetrievePlan {
-  int W = 0, NB = 0, lpt = 0, ch = 0, S = 0, BH = 0, keff = 0;
+  int W = 0, BINS = 0, lpt = 0, ch = 0, S = 0, BH = 0, keff = 0;
   int64_t lo = 0, C = 0;
-  size_t off_stash = 0, off_cum = 0, off_meta = 0, off_params = 0, total = 0;
+  size_t off_stash = 0, off_hist = 0, off_meta = 0, off_params = 0, total = 0;
 };
 RetrievePlan plan_retrieve(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, int n_local,
                            int k);
@@ -91,6 +92,51 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
     if (lane >= o) v += n;
   }
   return v;
+}
+
+// Sums each of K per-lane values (K = 8 or 16) over the 64 lanes of a wavefront, by a
+// butterfly that halves the values held per lane at every exchange, then adds across the
+// remaining lane bits.  Returns, in lane l, the total of value bitrev(l mod K), where
+// bitrev reverses log2(K) bits.
+template <int M>
+__device__ __forceinline__ uint32_t swizzle_xor(uint32_t v) {     // lane ^ M, M < 32
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (M << 10));
+}
+template <int K, int M>
+__device__ __forceinline__ void transpose_sum_step(uint32_t (&x)[K], int lane) {
+  constexpr int H = K / (2 * M);
+  // Lanes with bit M set keep the upper half and send the lower; the choice is made with
+  // masks, not with a select between elements (which the compiler turns into a dynamic
+  // index into the array and so into scratch memory).
+  const uint32_t up = (lane & M) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const uint32_t d = (x[i] ^ x[i + H]) & up;
+    const uint32_t send = x[i + H] ^ d;
+    const uint32_t keep = x[i] ^ d;
+    x[i] = keep + swizzle_xor<M>(send);
+  }
+}
+template <int K>
+__device__ __forceinline__ int bitrev_k(int l) {
+  int r = 0;
+#pragma unroll
+  for (int b = 1; b < K; b <<= 1) r = (r << 1) | ((l & b) ? 1 : 0);
+  return r;
+}
+template <int K>
+__device__ __forceinline__ uint32_t wave_transpose_sum(uint32_t (&x)[K]) {
+  static_assert(K == 8 || K == 16, "8 or 16 values");
+  const int lane = threadIdx.x & 63;
+  transpose_sum_step<K, 1>(x, lane);
+  transpose_sum_step<K, 2>(x, lane);
+  transpose_sum_step<K, 4>(x, lane);
+  if constexpr (K == 16) transpose_sum_step<K, 8>(x, lane);
+  uint32_t r = x[0];
+  if constexpr (K == 8) r += swizzle_xor<8>(r);
+  r += swizzle_xor<16>(r);
+  r += (uint32_t)__shfl_xor((int)r, 32, 64);
+  return r;
 }
 
 // Exclusive scan over a workgroup of NT threads (NT multiple of 64).  `lds` holds

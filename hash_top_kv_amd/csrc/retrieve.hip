@@ -8,8 +8,8 @@
 //   hamming_scan   reads each candidate code once with 16-byte (or 8-byte) loads,
 //                  XOR + popcount against the query code, stores the distance as one
 //                  byte, and builds the chunk's distance histogram in LDS (one private
-//                  histogram per wavefront).  The chunk's cumulative histogram goes to
-//                  the workspace.  This kernel is bound by HBM bandwidth.
+//                  histogram per wavefront), written out per chunk.  This kernel is
+//                  bound by HBM bandwidth.
 //   topk_threshold one workgroup per head: sums the chunk histograms, finds the
 //                  threshold T = min{t : #(D <= t) >= k_eff} and the tie quota
 //                  k_eff - #(D < T), and an exclusive prefix over chunks of the counts
@@ -22,7 +22,6 @@
 namespace hk {
 namespace {
 
-constexpr int kSelThreads = 1024;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -44,14 +43,18 @@ template <> struct CodeVec<2> {
   }
 };
 
-// grid (S, BH); chunk c of head bh covers candidate offsets [c*CH, (c+1)*CH).
+// grid (S, BH); chunk c of head bh covers candidate offsets [c*CH, (c+1)*CH).  The
+// histogram of the chunk goes to hist[bh][c]: bins 0 .. 32W-1, then 4W "superbins", each
+// the count of 8 consecutive distances (the count at distance 32W follows from the
+// chunk size).
 template <int W, int LPT>
 __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
     const uint32_t *__restrict__ codes, const uint32_t *__restrict__ qcodes, int64_t cap,
-    int64_t lo, int64_t C, int S, uint32_t *__restrict__ stash, uint32_t *__restrict__ cum) {
-  constexpr int NB = 32 * W + 1;
-  constexpr int NBP = (NB + 3) & ~3;
+    int64_t lo, int64_t C, int S, uint32_t *__restrict__ stash, uint32_t *__restrict__ hist_out) {
+  constexpr int BINS = 32 * W;
+  constexpr int NBP = BINS + 4;
   constexpr int CH = kScanThreads * LPT;
+  static_assert(BINS + BINS / 8 <= kScanThreads, "one thread per histogram entry");
   using CV = CodeVec<W>;
   using V = typename CV::T;
   __shared__ uint32_t hist[kScanThreads / 64][NBP];
@@ -60,22 +63,32 @@ __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
   const int bh = blockIdx.y;
   const int t = threadIdx.x;
   const int wave = t >> 6;
-  const int lane = t & 63;
 
-  const int64_t p0 = (int64_t)c * CH;
-  const V *base = reinterpret_cast<const V *>(codes + ((int64_t)bh * cap + lo) * W);
-  // Stream the chunk's codes first (non-temporal: they are read exactly once).
-  V v[LPT];
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int64_t p = p0 + i * kScanThreads + t;
-    v[i] = (p < C) ? __builtin_nontemporal_load(base + p) : CV::zero();
-  }
+  // The histograms are cleared and the query code read before the codes are requested:
+  // a barrier after the code loads would make every thread wait for all of them, while
+  // here each token is processed as soon as its own load has landed.
   for (int i = t; i < (kScanThreads / 64) * NBP; i += kScanThreads) (&hist[0][0])[i] = 0u;
   uint32_t q[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) q[w] = qcodes[(int64_t)bh * W + w];
   __syncthreads();
+
+  const int64_t p0 = (int64_t)c * CH;
+  const V *base = reinterpret_cast<const V *>(codes + ((int64_t)bh * cap + lo) * W);
+  // Non-temporal loads: the codes are read exactly once.  Whole chunks load without
+  // predication; only the last chunk of a head can be partial.
+  V v[LPT];
+  if (p0 + CH <= C) {
+    const V *bp = base + p0 + t;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) v[i] = __builtin_nontemporal_load(bp + i * kScanThreads);
+  } else {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int64_t p = p0 + i * kScanThreads + t;
+      v[i] = (p < C) ? __builtin_nontemporal_load(base + p) : CV::zero();
+    }
+  }
 
   uint32_t *st = stash + ((int64_t)bh * S + c) * stash_words_per_chunk<LPT>();
 #pragma unroll
@@ -95,102 +108,179 @@ __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
     st[i4 * kScanThreads + t] = packed;
   }
   __syncthreads();
-  // Inclusive cumulative histogram by one wavefront: lane l owns bins 2l, 2l+1 (and the
-  // last lane also bin NB-1 when NB is odd).
-  if (wave == 0) {
-    auto bin = [&](int b) -> uint32_t {
-      uint32_t s = 0;
+  constexpr int NSB = BINS / 8;
+  uint32_t *out = hist_out + ((int64_t)bh * S + c) * (BINS + NSB);
+  if (t < BINS) {
+    uint32_t sum = 0;
 #pragma unroll
-      for (int w = 0; w < kScanThreads / 64; ++w) s += hist[w][b];
-      return s;
-    };
-    constexpr int PAIRS = (NB - 1) / 2;                // 64 or 32
-    uint32_t a = 0, b = 0;
-    if (lane < PAIRS) {
-      a = bin(2 * lane);
-      b = bin(2 * lane + 1);
-    }
-    const uint32_t inc = wave_incl_scan_u32(a + b);
-    uint32_t *out = cum + ((int64_t)bh * S + c) * NB;
-    if (lane < PAIRS) {
-      out[2 * lane] = inc - b;
-      out[2 * lane + 1] = inc;
-    }
-    if (lane == PAIRS - 1) out[NB - 1] = inc + bin(NB - 1);
+    for (int w = 0; w < kScanThreads / 64; ++w) sum += hist[w][t];
+    out[t] = sum;
+  } else if (t < BINS + NSB) {
+    const int b0 = 8 * (t - BINS);
+    uint32_t sum = 0;
+#pragma unroll
+    for (int w = 0; w < kScanThreads / 64; ++w)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += hist[w][b0 + e];
+    out[t] = sum;
   }
 }
 
-// grid (BH); one workgroup per head.  Every load phase keeps all its loads in flight.
-template <int NB>
-__global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
-    const uint32_t *__restrict__ cum, int S, int keff, int4 *__restrict__ meta,
-    int2 *__restrict__ params, int32_t *__restrict__ count) {
-  constexpr int BINS = NB - 1;                 // 128 or 64 (the last bin is extra)
-  constexpr int NGR = kSelThreads / BINS;      // 8 or 16 groups of chunks
-  constexpr int UNR = 8;
-  __shared__ uint32_t part[NGR][NB];
-  __shared__ uint32_t gcum[NB];
-  __shared__ uint32_t scan_lds[2][kSelThreads / 64];
-  __shared__ int sT, sQ;
-  const int bh = blockIdx.x;
-  const int tid = threadIdx.x;
-  const uint32_t *cb = cum + (int64_t)bh * S * NB;
+// grid (BH); one workgroup per head, one thread per chunk (tiles of kThrThreads chunks).
+// A two-level radix select over the chunk histograms:
+//   1. superbin totals over all chunks -> the superbin holding T (or T = BINS when the
+//      histogrammed distances hold fewer than k_eff candidates);
+//   2. that superbin's 8 bins, totalled over the chunks -> T and the tie quota;
+//   3. per chunk, #(D < T) (its superbins below T's plus its bins of T's superbin below
+//      T) and #(D == T), then an exclusive prefix of both over chunks into meta.
+// For up to kThrThreads chunks per head every value is read once and kept in registers.
+constexpr int kThrThreads = 256;
 
-  if (tid == 0) {
-    sT = -1;
-    sQ = 0;
+template <int K>
+__device__ __forceinline__ void load_u32x(const uint32_t *p, uint32_t (&x)[K]) {
+#pragma unroll
+  for (int i = 0; i < K / 4; ++i) {
+    const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+    x[4 * i] = v.x;
+    x[4 * i + 1] = v.y;
+    x[4 * i + 2] = v.z;
+    x[4 * i + 3] = v.w;
   }
-  if (keff > 0) {
-    const int tb = tid % BINS, g = tid / BINS;
-    uint32_t s = 0, s_last = 0;
-    for (int c0 = g; c0 < S; c0 += NGR * UNR) {
-      uint32_t vals[UNR], lastv[UNR];
+}
+
+// Sum of K values over the workgroup: per-wavefront transposed sums, then LDS.
+// Returns the total of value i in thread i < K (others: undefined).  red holds
+// kThrThreads / 64 * 16 entries.
+template <int K>
+__device__ __forceinline__ uint32_t block_sum_k(uint32_t (&x)[K], uint32_t *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t r = wave_transpose_sum<K>(x);
+  if (lane < K) red[wave * 16 + bitrev_k<K>(lane)] = r;
+  __syncthreads();
+  uint32_t t = 0;
+  if ((int)threadIdx.x < K) {
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int c = c0 + u * NGR;
-        vals[u] = c < S ? cb[(int64_t)c * NB + tb] : 0u;
-        lastv[u] = (c < S && tb == 0) ? cb[(int64_t)c * NB + BINS] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        s += vals[u];
-        s_last += lastv[u];
-      }
-    }
-    part[g][tb] = s;
-    if (tb == 0) part[g][BINS] = s_last;
-    __syncthreads();
-    if (tid < NB) {
-      uint32_t a = 0;
-#pragma unroll
-      for (int gg = 0; gg < NGR; ++gg) a += part[gg][tid];
-      gcum[tid] = a;
-    }
-    __syncthreads();
-    if (tid < NB) {
-      const uint32_t below = tid ? gcum[tid - 1] : 0u;
-      if (gcum[tid] >= (uint32_t)keff && below < (uint32_t)keff) {
-        sT = tid;
-        sQ = keff - (int)below;
-      }
-    }
+    for (int w = 0; w < kThrThreads / 64; ++w) t += red[w * 16 + threadIdx.x];
   }
   __syncthreads();
-  const int T = sT;
-  const int quota = sQ;
+  return t;
+}
+
+template <int BINS>
+__global__ __launch_bounds__(kThrThreads) void topk_threshold_kernel(
+    const uint32_t *__restrict__ hist, int S, int64_t C, int CH, int keff,
+    int4 *__restrict__ meta, int2 *__restrict__ params, int32_t *__restrict__ count) {
+  constexpr int NSB = BINS / 8;                // 16 or 8 superbins
+  constexpr int ROW = BINS + NSB;
+  constexpr int NT = kThrThreads;
+  __shared__ uint32_t red[NT / 64 * 16];
+  __shared__ uint32_t tot[16];
+  __shared__ uint32_t scan_lds[2][NT / 64];
+  __shared__ int sh[4];                        // T, quota, superbin of T, count below it
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint32_t *hb = hist + (int64_t)bh * S * ROW;
+  auto row = [&](int c) { return hb + (int64_t)(c < S ? c : S - 1) * ROW; };
+
+  uint32_t sb0[NSB], bb0[8];                   // the first tile's values, kept
+  if (keff > 0) {
+    // 1. superbin totals
+    uint32_t acc[NSB];
+#pragma unroll
+    for (int i = 0; i < NSB; ++i) acc[i] = 0u;
+    for (int c0 = 0; c0 < S; c0 += NT) {
+      uint32_t x[NSB];
+      load_u32x<NSB>(row(c0 + tid) + BINS, x);
+      const bool ok = c0 + tid < S;
+#pragma unroll
+      for (int i = 0; i < NSB; ++i) {
+        x[i] = ok ? x[i] : 0u;
+        acc[i] += x[i];
+        if (c0 == 0) sb0[i] = x[i];
+      }
+    }
+    const uint32_t st = block_sum_k<NSB>(acc, red);
+    if (tid < NSB) tot[tid] = st;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t below = 0;
+      int s = 0;
+      while (s < NSB && below + tot[s] < (uint32_t)keff) below += tot[s++];
+      sh[2] = s;                               // NSB: T = BINS
+      sh[3] = (int)below;
+    }
+    __syncthreads();
+    const int Ts = sh[2];
+    if (Ts < NSB) {
+      // 2. the 8 bins of superbin Ts
+      uint32_t bacc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bacc[i] = 0u;
+      for (int c0 = 0; c0 < S; c0 += NT) {
+        uint32_t x[8];
+        load_u32x<8>(row(c0 + tid) + 8 * Ts, x);
+        const bool ok = c0 + tid < S;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          x[i] = ok ? x[i] : 0u;
+          bacc[i] += x[i];
+          if (c0 == 0) bb0[i] = x[i];
+        }
+      }
+      const uint32_t bt = block_sum_k<8>(bacc, red);
+      if (tid < 8) tot[tid] = bt;
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t below = (uint32_t)sh[3];
+        int b = 0;
+        while (below + tot[b] < (uint32_t)keff) below += tot[b++];   // stops at b < 8
+        sh[0] = 8 * Ts + b;
+        sh[1] = keff - (int)below;
+      }
+    } else if (tid == 0) {
+      sh[0] = BINS;
+      sh[1] = keff - sh[3];
+    }
+  } else if (tid == 0) {
+    sh[0] = -1;
+    sh[1] = 0;
+  }
+  __syncthreads();
+  const int T = sh[0];
+  const int quota = sh[1];
+  // 3. per-chunk counts and their prefix over chunks
   uint32_t carry_lt = 0, carry_eq = 0;
-  for (int base = 0; base < S; base += kSelThreads) {
-    const int c = base + tid;
+  for (int c0 = 0; c0 < S && T >= 0; c0 += NT) {
+    const int c = c0 + tid;
+    const int Ts = T >> 3;
+    uint32_t sbv[NSB], bbv[8];
+    if (c0 == 0) {
+#pragma unroll
+      for (int i = 0; i < NSB; ++i) sbv[i] = sb0[i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bbv[i] = bb0[i];
+    } else {
+      load_u32x<NSB>(row(c) + BINS, sbv);
+      if (T < BINS) load_u32x<8>(row(c) + 8 * Ts, bbv);
+    }
     uint32_t lt = 0, eq = 0;
-    if (c < S && T >= 0) {
-      const uint32_t a = T > 0 ? cb[(int64_t)c * NB + T - 1] : 0u;
-      const uint32_t b = cb[(int64_t)c * NB + T];
-      lt = a;
-      eq = b - a;
+    if (c < S) {
+#pragma unroll
+      for (int i = 0; i < NSB; ++i) lt += (i < Ts) ? sbv[i] : 0u;
+      if (T < BINS) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          lt += (8 * Ts + i < T) ? bbv[i] : 0u;
+          eq += (8 * Ts + i == T) ? bbv[i] : 0u;
+        }
+      } else {                                 // distance BINS is not in the histogram
+        const int64_t n = C - (int64_t)c * CH;
+        eq = (uint32_t)(n < CH ? n : CH) - lt;
+      }
     }
     uint32_t tl, te;
-    const uint32_t lt_ex = block_excl_scan_u32<kSelThreads>(lt, scan_lds[0], tl);
-    const uint32_t eq_ex = block_excl_scan_u32<kSelThreads>(eq, scan_lds[1], te);
+    const uint32_t lt_ex = block_excl_scan_u32<NT>(lt, scan_lds[0], tl);
+    const uint32_t eq_ex = block_excl_scan_u32<NT>(eq, scan_lds[1], te);
     if (c < S)
       meta[(int64_t)bh * S + c] =
           make_int4((int)(carry_lt + lt_ex), (int)(carry_eq + eq_ex), (int)lt, (int)eq);
@@ -235,9 +325,9 @@ __global__ void window_indices_kernel(int32_t n_sinks, int64_t local0, int32_t n
 
 template <int W, int LPT>
 void scan_launch(const RetrievePlan &p, const uint32_t *codes, const uint32_t *qcodes,
-                 int64_t cap, uint32_t *stash, uint32_t *cum, hipStream_t st) {
+                 int64_t cap, uint32_t *stash, uint32_t *hist, hipStream_t st) {
   hipLaunchKernelGGL((hamming_scan_kernel<W, LPT>), dim3(p.S, p.BH), dim3(kScanThreads), 0,
-                     st, codes, qcodes, cap, p.lo, p.C, p.S, stash, cum);
+                     st, codes, qcodes, cap, p.lo, p.C, p.S, stash, hist);
 }
 
 }  // namespace
@@ -246,26 +336,25 @@ RetrievePlan plan_retrieve(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, 
                            int k) {
   RetrievePlan p;
   p.W = bits / 32;
-  p.NB = bits + 1;
+  p.BINS = bits;
   p.BH = B * Hkv;
   p.lo = n_sink;
   const int64_t hi = n_ctx - n_local;
   p.C = hi > p.lo ? hi - p.lo : 0;
   p.keff = (int)(k < p.C ? k : p.C);
   if (p.keff < 0) p.keff = 0;
-  // Chunk size: the largest of 16/8/4 codes per thread that still gives >= 1024
-  // workgroups, so that 256 CUs each see several.
+  // Chunk size: 2048 codes (8 per thread) when that still gives >= 1024 workgroups, so
+  // that 256 CUs each see several, else 1024.  Larger chunks lengthen each workgroup's
+  // tail (the histogram and distance stores follow its last load) and measured slower.
   const int64_t tok = (int64_t)p.BH * p.C;
-  p.lpt = 16;
-  if ((tok + 4095) / 4096 < 1024) p.lpt = 8;
-  if (p.lpt == 8 && (tok + 2047) / 2048 < 1024) p.lpt = 4;
+  p.lpt = (tok + 2047) / 2048 >= 1024 ? 8 : 4;
   p.ch = kScanThreads * p.lpt;
   p.S = (int)((p.C + p.ch - 1) / p.ch);
   size_t off = 0;
   p.off_stash = off;
   off = align_up(off + (size_t)p.BH * p.S * p.ch, 256);
-  p.off_cum = off;
-  off = align_up(off + (size_t)p.BH * p.S * p.NB * sizeof(uint32_t), 256);
+  p.off_hist = off;
+  off = align_up(off + (size_t)p.BH * p.S * (p.BINS + p.BINS / 8) * sizeof(uint32_t), 256);
   p.off_meta = off;
   off = align_up(off + (size_t)p.BH * p.S * sizeof(int4), 256);
   p.off_params = off;
@@ -280,15 +369,13 @@ hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
   if (p.BH == 0 || p.S == 0) return hipSuccess;
   uint8_t *w8 = static_cast<uint8_t *>(ws);
   uint32_t *stash = reinterpret_cast<uint32_t *>(w8 + p.off_stash);
-  uint32_t *cum = reinterpret_cast<uint32_t *>(w8 + p.off_cum);
+  uint32_t *hist = reinterpret_cast<uint32_t *>(w8 + p.off_hist);
   if (p.W == 4) {
-    if (p.lpt == 16) scan_launch<4, 16>(p, codes, qcodes, cap, stash, cum, st);
-    else if (p.lpt == 8) scan_launch<4, 8>(p, codes, qcodes, cap, stash, cum, st);
-    else scan_launch<4, 4>(p, codes, qcodes, cap, stash, cum, st);
+    if (p.lpt == 8) scan_launch<4, 8>(p, codes, qcodes, cap, stash, hist, st);
+    else scan_launch<4, 4>(p, codes, qcodes, cap, stash, hist, st);
   } else {
-    if (p.lpt == 16) scan_launch<2, 16>(p, codes, qcodes, cap, stash, cum, st);
-    else if (p.lpt == 8) scan_launch<2, 8>(p, codes, qcodes, cap, stash, cum, st);
-    else scan_launch<2, 4>(p, codes, qcodes, cap, stash, cum, st);
+    if (p.lpt == 8) scan_launch<2, 8>(p, codes, qcodes, cap, stash, hist, st);
+    else scan_launch<2, 4>(p, codes, qcodes, cap, stash, hist, st);
   }
   return hipGetLastError();
 }
@@ -297,15 +384,15 @@ hipError_t launch_topk_threshold(const RetrievePlan &p, int32_t *count, void *ws
                                  hipStream_t st) {
   if (p.BH == 0) return hipSuccess;
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  const uint32_t *cum = reinterpret_cast<const uint32_t *>(w8 + p.off_cum);
+  const uint32_t *hist = reinterpret_cast<const uint32_t *>(w8 + p.off_hist);
   int4 *meta = reinterpret_cast<int4 *>(w8 + p.off_meta);
   int2 *params = reinterpret_cast<int2 *>(w8 + p.off_params);
-  if (p.NB == 129)
-    hipLaunchKernelGGL((topk_threshold_kernel<129>), dim3(p.BH), dim3(kSelThreads), 0, st,
-                       cum, p.S, p.keff, meta, params, count);
+  if (p.BINS == 128)
+    hipLaunchKernelGGL((topk_threshold_kernel<128>), dim3(p.BH), dim3(kThrThreads), 0, st,
+                       hist, p.S, p.C, p.ch, p.keff, meta, params, count);
   else
-    hipLaunchKernelGGL((topk_threshold_kernel<65>), dim3(p.BH), dim3(kSelThreads), 0, st,
-                       cum, p.S, p.keff, meta, params, count);
+    hipLaunchKernelGGL((topk_threshold_kernel<64>), dim3(p.BH), dim3(kThrThreads), 0, st,
+                       hist, p.S, p.C, p.ch, p.keff, meta, params, count);
   return hipGetLastError();
 }
 
@@ -318,10 +405,7 @@ hipError_t launch_topk_select(const RetrievePlan &p, int k, int32_t *idx, int32_
   const uint32_t *stash = reinterpret_cast<const uint32_t *>(w8 + p.off_stash);
   const int4 *meta = reinterpret_cast<const int4 *>(w8 + p.off_meta);
   const int2 *params = reinterpret_cast<const int2 *>(w8 + p.off_params);
-  if (p.lpt == 16)
-    hipLaunchKernelGGL((topk_emit_kernel<16>), dim3(p.S, p.BH), dim3(kScanThreads), 0, st,
-                       stash, meta, params, p.S, p.lo, k, idx);
-  else if (p.lpt == 8)
+  if (p.lpt == 8)
     hipLaunchKernelGGL((topk_emit_kernel<8>), dim3(p.S, p.BH), dim3(kScanThreads), 0, st,
                        stash, meta, params, p.S, p.lo, k, idx);
   else

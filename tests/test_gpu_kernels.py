@@ -38,8 +38,10 @@ RETRIEVE_CASES = [
     (64, 1, 1, 1, 0, 0, 5, 0),              # single token
     (128, 2, 2, 4100, 4, 0, 4096, 2),       # k = C, two distinct codes
     (128, 1, 8, 300001, 4, 64, 6001, 0),    # >= 2M tokens: 8 codes per thread
-    (64, 2, 4, 600000, 4, 512, 3000, 0),    # >= 4M tokens: 16 codes per thread
-    (128, 1, 8, 540000, 0, 0, 1024, 9),     # 16 codes per thread, heavy ties
+    (64, 2, 4, 600000, 4, 512, 3000, 0),    # 8 codes per thread, 64-bit
+    (128, 1, 8, 540000, 0, 0, 1024, 9),     # > 256 chunks per head (second threshold
+                                            # window for 128-bit codes), heavy ties
+    (64, 1, 2, 1100000, 0, 0, 500, 0),      # > 512 chunks per head (64-bit codes)
 ]
 
 
@@ -65,6 +67,26 @@ def test_retrieve_topk_bit_exact(case):
             want = oracle.select_topk(codes[b, h], qc[b, h], N, s, w, k)
             assert count[b, h] == want.size
             assert np.array_equal(idx[b, h, :want.size], want), (b, h)
+
+
+@pytest.mark.parametrize("bits", [64, 128])
+def test_retrieve_ties_at_the_largest_distance(bits):
+    """Most codes are the complement of the query code (distance = bits, a bin the
+    per-chunk histograms leave out): the threshold lands on it and the tie quota is
+    taken in index order."""
+    rng = np.random.default_rng(bits)
+    W = bits // 32
+    B, Hkv, N, k = 1, 3, 20000, 700
+    qc = rng.integers(0, 2 ** 32, size=(B, Hkv, W), dtype=np.uint32)
+    codes = np.broadcast_to(~qc[:, :, None, :], (B, Hkv, N, W)).copy()
+    few = rng.choice(N, size=150, replace=False)
+    codes[:, :, few] = rng.integers(0, 2 ** 32, size=(B, Hkv, few.size, W), dtype=np.uint32)
+    idx, count = hk.retrieve_topk(codes_tensor(codes), codes_tensor(qc), bits, N, 0, 0, k)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    for h in range(Hkv):
+        want = oracle.select_topk(codes[0, h], qc[0, h], N, 0, 0, k)
+        assert np.array_equal(idx[0, h], want), h
 
 
 def test_retrieve_split_halves_equal_whole_and_workspace_reuse():
