@@ -48,61 +48,68 @@ __global__ __launch_bounds__(kAttThreads) void sparse_decode_kernel(
   ga.combine_store(out_o + ((int64_t)p * rows + row0) * kHeadDim, out_lse + (int64_t)p * rows + row0);
 }
 
-// Up to 64 parts of d = 128: one wavefront per output row.  Lane p reads lse_p; the
-// partial outputs (two columns per lane) are requested together with the lse's, 16 parts
-// at a time; weights are broadcast from lane p with readlane.
+// Up to 64 parts of d = 128: one workgroup per output row.  Wavefront w merges parts
+// w, w+4, ... (up to 16, every load in flight at once: the lse of each part and two
+// columns per lane); the four wavefront results combine through LDS.
+constexpr int kMergeSmallParts = 64;
+
 __global__ __launch_bounds__(256) void lse_merge_small_kernel(
     const float *__restrict__ o_parts, const float *__restrict__ lse_parts, int P,
     int64_t rows, float *__restrict__ o, float *__restrict__ lse) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
   constexpr int D = kHeadDim;
-  constexpr int PB = 16;
-  const float x = lane < P ? lse_parts[(int64_t)lane * rows + row] : -INFINITY;
-  float va[PB], vb[PB];
+  constexpr int PW = kMergeSmallParts / 4;     // parts per wavefront
+  __shared__ float s_m[4], s_s[4];
+  __shared__ float s_acc[4][D];
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  float x[PW], va[PW], vb[PW];
 #pragma unroll
-  for (int j = 0; j < PB; ++j) {
-    const int pp = j < P ? j : 0;
+  for (int j = 0; j < PW; ++j) {
+    const int p = wave + 4 * j;
+    const int pp = p < P ? p : 0;
+    x[j] = p < P ? lse_parts[(int64_t)pp * rows + row] : -INFINITY;
     const float *op = o_parts + ((int64_t)pp * rows + row) * D;
     va[j] = op[lane];
     vb[j] = op[lane + 64];
   }
-  float M = x;
+  float M = -INFINITY;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (M == -INFINITY) {
-    o[row * D + lane] = 0.f;
-    o[row * D + lane + 64] = 0.f;
-    if (lane == 0) lse[row] = -INFINITY;
-    return;
+  for (int j = 0; j < PW; ++j) M = fmaxf(M, x[j]);
+  float S = 0.f, acc_a = 0.f, acc_b = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+      const float wgt = __expf(x[j] - M);      // 0 for parts past P and empty parts
+      S += wgt;
+      acc_a = fmaf(wgt, va[j], acc_a);
+      acc_b = fmaf(wgt, vb[j], acc_b);
+    }
   }
-  const float w = lane < P ? __expf(x - M) : 0.f;
-  float S = w;
+  if (lane == 0) {
+    s_m[wave] = M;
+    s_s[wave] = S;
+  }
+  s_acc[wave][lane] = acc_a;
+  s_acc[wave][lane + 64] = acc_b;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int e = threadIdx.x;
+    float Mt = -INFINITY;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
-  float acc_a = 0.f, acc_b = 0.f;
-  for (int p0 = 0; p0 < P; p0 += PB) {
-    if (p0 > 0) {
+    for (int w = 0; w < 4; ++w) Mt = fmaxf(Mt, s_m[w]);
+    float St = 0.f, at = 0.f;
+    if (Mt != -INFINITY) {
 #pragma unroll
-      for (int j = 0; j < PB; ++j) {
-        const int pp = p0 + j < P ? p0 + j : 0;
-        const float *op = o_parts + ((int64_t)pp * rows + row) * D;
-        va[j] = op[lane];
-        vb[j] = op[lane + 64];
+      for (int w = 0; w < 4; ++w) {
+        const float f = s_m[w] == -INFINITY ? 0.f : __expf(s_m[w] - Mt);
+        St += s_s[w] * f;
+        at += s_acc[w][e] * f;
       }
     }
-#pragma unroll
-    for (int j = 0; j < PB; ++j) {
-      const float wf = p0 + j < P ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), p0 + j)) : 0.f;
-      acc_a = fmaf(wf, va[j], acc_a);
-      acc_b = fmaf(wf, vb[j], acc_b);
-    }
+    o[row * D + e] = Mt == -INFINITY ? 0.f : at / St;
+    if (e == 0) lse[row] = Mt == -INFINITY ? -INFINITY : Mt + __logf(St);
   }
-  const float inv = 1.f / S;
-  o[row * D + lane] = acc_a * inv;
-  o[row * D + lane + 64] = acc_b * inv;
-  if (lane == 0) lse[row] = M + __logf(S);
 }
 
 // One workgroup per output row.  The row's P log-sum-exps and P x d partial outputs are
@@ -281,8 +288,8 @@ hipError_t launch_lse_merge_parts(const float *o_parts, const float *lse_parts, 
 hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int P,
                             int64_t rows, int d, float *o, float *lse, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  if (P <= 64 && d == kHeadDim) {
-    hipLaunchKernelGGL(lse_merge_small_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+  if (P <= kMergeSmallParts && d == kHeadDim) {
+    hipLaunchKernelGGL(lse_merge_small_kernel, dim3((unsigned)rows), dim3(256), 0, st,
                        o_parts, lse_parts, P, rows, o, lse);
     return hipGetLastError();
   }

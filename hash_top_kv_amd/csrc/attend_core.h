@@ -279,7 +279,8 @@ struct GroupAttention {
 // ------------------------------------------------------------------ matrix-core variant
 // bf16 rows, G <= 16 query heads: per wavefront, tiles of 16 rows.
 //   scores  S^T[16 rows][16 heads] = K_tile . Q^T with four v_mfma_f32_16x16x32_bf16; lane l
-//           loads 16 bytes of row (l % 16) per k-step (dims 32*(l/16) + 8*ks ..), and holds
+//           loads 16 bytes of row (l % 16) per k-step (dims 32*ks + 8*(l/16) .., so the four
+//           lanes of a row read 64 contiguous bytes per load instruction), and holds
 //           the scores of head l % 16 for rows 4*(l/16) .. +3 -- which is already the
 //           A-operand layout of P for the second product, so no transpose is needed.
 //   output  O[16 heads][dims] += P . V_tile with eight v_mfma_f32_16x16x16_bf16, one per
@@ -304,10 +305,10 @@ struct GroupAttentionMfma {
   __device__ void init(const void *q, int64_t row0, float sl2) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g = lane >> 4;
-    const uint16_t *qp = static_cast<const uint16_t *>(q) + (size_t)(row0 + n) * D + 32 * g;
+    const uint16_t *qp = static_cast<const uint16_t *>(q) + (size_t)(row0 + n) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint4 v = n < G ? *reinterpret_cast<const uint4 *>(qp + 8 * ks) : make_uint4(0, 0, 0, 0);
+      const uint4 v = n < G ? *reinterpret_cast<const uint4 *>(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
       qb[ks] = __builtin_bit_cast(bf16x8, v);
     }
     scale_log2 = sl2;
@@ -334,10 +335,10 @@ struct GroupAttentionMfma {
       const int r0 = tile * 16;
       const int tok = r0 + n < len ? fetch_row(r0 + n) : 0;
       const bool okk = r0 + n < len;
-      const uint16_t *kp = kb + (head_row0 + (size_t)tok) * D + 32 * g;
+      const uint16_t *kp = kb + (head_row0 + (size_t)tok) * D + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        T.k[ks] = okk ? *reinterpret_cast<const uint4 *>(kp + 8 * ks) : make_uint4(0, 0, 0, 0);
+        T.k[ks] = okk ? *reinterpret_cast<const uint4 *>(kp + 32 * ks) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tv = __shfl(tok, 4 * g + j);

@@ -22,10 +22,14 @@ namespace {
 // list (and into the head's index list) and attends over the list; when a list would
 // overflow LDS it is attended and emptied first, so any selection size works.
 constexpr int kListMax = 4096;
-constexpr int kMaxCpb = 4;                 // chunks per workgroup, bounded by registers
+constexpr int kMaxCpb = 8;                 // chunks per workgroup, bounded by registers
+// Workgroups resident at once at this kernel's register use (3 per CU).  Beyond that,
+// fewer and longer workgroups amortise each one's serial phases (stash read,
+// compaction, first gather, combine) over more rows.
+constexpr int64_t kResidentBlocks = 768;
 
 template <int LPT, bool BF16, int G>
-__global__ __launch_bounds__(kScanThreads) void emit_attend_kernel(
+__device__ __forceinline__ void emit_attend_body(
     const uint32_t *__restrict__ stash, const int4 *__restrict__ meta,
     const int2 *__restrict__ params, int S, int CPB, int Sc, int64_t lo, int k,
     int32_t *__restrict__ idx, const void *__restrict__ q, const void *__restrict__ kc,
@@ -62,39 +66,67 @@ __global__ __launch_bounds__(kScanThreads) void emit_attend_kernel(
     const int c1 = min(S, c0 + CPB);
     int len = 0;
     int32_t *out = idx + (int64_t)bh * k;
-    // Every chunk's stash words and counts are requested before any is compacted.
-    uint32_t wall[kMaxCpb][LPT / 4];
-    int4 mall[kMaxCpb];
+    const int nch = c1 - c0;
+    // Every chunk's stash words and counts are requested before any is compacted, and
+    // staged in LDS (indexed by chunk at run time without scratch memory).
+    __shared__ uint32_t sw[kMaxCpb][LPT / 4][kScanThreads];
+    __shared__ int4 smt[kMaxCpb];
+    {
+      uint32_t wl[kMaxCpb][LPT / 4];
 #pragma unroll
-    for (int i = 0; i < kMaxCpb; ++i) {
-      const int ch = c0 + i < c1 ? c0 + i : c0;
-      mall[i] = meta[(int64_t)bh * S + ch];
-      const uint32_t *sp = stash + ((int64_t)bh * S + ch) * stash_words_per_chunk<LPT>();
+      for (int i = 0; i < kMaxCpb; ++i) {
+        const int ch = c0 + i < c1 ? c0 + i : c0;
+        const uint32_t *sp = stash + ((int64_t)bh * S + ch) * stash_words_per_chunk<LPT>();
 #pragma unroll
-      for (int i4 = 0; i4 < LPT / 4; ++i4) wall[i][i4] = sp[i4 * kScanThreads + t];
-    }
-#pragma unroll
-    for (int i = 0; i < kMaxCpb; ++i) {
-      const int ch = c0 + i;
-      if (ch >= c1) break;
-      const int4 mt = mall[i];
-      const int nsel = T >= 0 ? chunk_selected(mt, quota) : 0;
-      if (nsel == 0) continue;
-      if (len + nsel > kListMax) {
-        attend_list(len);
-        __syncthreads();                     // the list is reused
-        len = 0;
+        for (int i4 = 0; i4 < LPT / 4; ++i4) wl[i][i4] = sp[i4 * kScanThreads + t];
       }
-      const int base = len;
-      emit_chunk<LPT>(wall[i], T, quota, mt.x, mt.y, lo + (int64_t)ch * CH,
-                      [&](int pos, int lpos, int32_t tok) {
-                        out[pos] = tok;
-                        sel[base + lpos] = tok;
-                      });
-      __syncthreads();
-      len += nsel;
+      if (t < kMaxCpb) smt[t] = meta[(int64_t)bh * S + (c0 + t < c1 ? c0 + t : c0)];
+#pragma unroll
+      for (int i = 0; i < kMaxCpb; ++i)
+#pragma unroll
+        for (int i4 = 0; i4 < LPT / 4; ++i4) sw[i][i4][t] = wl[i][i4];
     }
-    if (len > 0) attend_list(len);
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxCpb; ++i)
+      total += (i < nch && T >= 0) ? chunk_selected(smt[i], quota) : 0;
+    if (total > 0 && total <= kListMax) {
+      // All chunks compacted together: the block's selected tokens occupy positions
+      // [first, first + total) of the head's list.  The list goes to LDS first and to the
+      // index list afterwards, in coalesced stores.
+      const int4 m0 = smt[0];
+      const int first = m0.x + min(m0.y, quota);
+      emit_chunks<LPT, kMaxCpb>([&](int i, int kk) { return sw[i][kk][t]; },
+                                [&](int i) { return smt[i]; }, nch, T, quota,
+                                lo + (int64_t)c0 * CH,
+                                [&](int pos, int32_t tok) { sel[pos - first] = tok; });
+      __syncthreads();
+      for (int r = t; r < total; r += kScanThreads) out[first + r] = sel[r];
+      attend_list(total);
+    } else if (total > kListMax) {
+      // Too many for the list: chunk by chunk, attending whenever the list would overflow.
+      for (int i = 0; i < nch; ++i) {
+        const int4 mt = smt[i];
+        const int nsel = chunk_selected(mt, quota);
+        if (nsel == 0) continue;
+        if (len + nsel > kListMax) {
+          attend_list(len);
+          __syncthreads();                   // the list is reused
+          len = 0;
+        }
+        const int base = len - (mt.x + min(mt.y, quota));   // list slot = base + position
+        emit_chunks<LPT, 1>([&](int, int kk) { return sw[i][kk][t]; }, [&](int) { return mt; },
+                            1, T, quota, lo + (int64_t)(c0 + i) * CH,
+                            [&](int pos, int32_t tok) {
+                              out[pos] = tok;
+                              sel[base + pos] = tok;
+                            });
+        __syncthreads();
+        len += nsel;
+      }
+      if (len > 0) attend_list(len);
+    }
     if (!ga_ready) ga.init(q, row0, scale_log2);
   } else {
     ga.init(q, row0, scale_log2);
@@ -108,15 +140,46 @@ __global__ __launch_bounds__(kScanThreads) void emit_attend_kernel(
   ga.combine_store(part_o + ((int64_t)c * rows + row0) * kHeadDim, part_lse + (int64_t)c * rows + row0);
 }
 
+#define HK_EMIT_ATTEND_PARAMS                                                                 \
+  const uint32_t *__restrict__ stash, const int4 *__restrict__ meta,                         \
+      const int2 *__restrict__ params, int S, int CPB, int Sc, int64_t lo, int k,            \
+      int32_t *__restrict__ idx, const void *__restrict__ q, const void *__restrict__ kc,    \
+      const void *__restrict__ vc, int Hq, int Hkv, int64_t cap, float scale_log2,           \
+      int win_sinks, int64_t win_local0, int n_win, int win_rows, float *__restrict__ part_o, \
+      float *__restrict__ part_lse, int64_t rows
+#define HK_EMIT_ATTEND_ARGS                                                                   \
+  stash, meta, params, S, CPB, Sc, lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,          \
+      win_sinks, win_local0, n_win, win_rows, part_o, part_lse, rows
+
+// bf16 (matrix cores): held to 168 VGPRs, three workgroups per CU.  fp32 (VALU) keeps
+// the compiler's choice: its accumulators would spill under that limit.
+template <int LPT, int G>
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(3))) void
+emit_attend_bf16_kernel(HK_EMIT_ATTEND_PARAMS) {
+  emit_attend_body<LPT, true, G>(HK_EMIT_ATTEND_ARGS);
+}
+template <int LPT, int G>
+__global__ __launch_bounds__(kScanThreads) void emit_attend_f32_kernel(HK_EMIT_ATTEND_PARAMS) {
+  emit_attend_body<LPT, false, G>(HK_EMIT_ATTEND_ARGS);
+}
+#undef HK_EMIT_ATTEND_PARAMS
+#undef HK_EMIT_ATTEND_ARGS
+
 template <int LPT, bool BF16, int G>
 void fused_launch(const FusedPlan &p, const uint32_t *stash, const int4 *meta,
                   const int2 *params, int k, int32_t *idx, const void *q, const void *kc,
                   const void *vc, int Hq, int Hkv, int64_t cap, float scale_log2, float *po,
                   float *pl, int64_t rows, hipStream_t st) {
-  hipLaunchKernelGGL((emit_attend_kernel<LPT, BF16, G>), dim3(p.parts, p.r.BH),
-                     dim3(kScanThreads), 0, st, stash, meta, params, p.r.S, p.cpb, p.Sc, p.r.lo,
-                     k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2, p.win_sinks, p.win_local0,
-                     p.n_win, p.win_rows, po, pl, rows);
+  if constexpr (BF16)
+    hipLaunchKernelGGL((emit_attend_bf16_kernel<LPT, G>), dim3(p.parts, p.r.BH),
+                       dim3(kScanThreads), 0, st, stash, meta, params, p.r.S, p.cpb, p.Sc,
+                       p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2, p.win_sinks,
+                       p.win_local0, p.n_win, p.win_rows, po, pl, rows);
+  else
+    hipLaunchKernelGGL((emit_attend_f32_kernel<LPT, G>), dim3(p.parts, p.r.BH),
+                       dim3(kScanThreads), 0, st, stash, meta, params, p.r.S, p.cpb, p.Sc,
+                       p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2, p.win_sinks,
+                       p.win_local0, p.n_win, p.win_rows, po, pl, rows);
 }
 
 template <int LPT, bool BF16>
@@ -149,17 +212,23 @@ FusedPlan plan_fused(int bits, int B, int Hq, int Hkv, int64_t n_ctx, int n_sink
   p.win_sinks = (int)sinks;
   p.win_local0 = local0;
   p.n_win = (int)(sinks + (n_ctx > local0 ? n_ctx - local0 : 0));
-  // Chunks per workgroup: about 64 selected rows per workgroup (four 16-row tiles, one
-  // per wavefront), while keeping at least 128 workgroups.
+  // Chunks per workgroup: at least one 16-row tile of selected rows per workgroup and no
+  // more workgroups than are resident at once, while keeping at least 128 workgroups.
+  // (Each chunk adds compaction work for all of its tokens, so chunks are not merged
+  // just to give every wavefront a tile: that lengthens the serial phase.)
   const int64_t chunks = (int64_t)p.r.BH * p.r.S;
   const int64_t per_chunk = p.r.S > 0 ? (p.r.keff + p.r.S - 1) / p.r.S : 1;
   int cpb = 1;
-  while (cpb < kMaxCpb && per_chunk * cpb < 64 && chunks / (2 * cpb) >= 128) cpb *= 2;
+  while (cpb < kMaxCpb && chunks / (2 * cpb) >= 128 &&
+         (per_chunk * cpb < 16 || chunks / cpb > kResidentBlocks))
+    cpb *= 2;
   p.cpb = cpb;
   p.Sc = (p.r.S + cpb - 1) / cpb;
-  // Window slices: at most 64 rows each, of equal size.
-  p.Sw = (p.n_win + 63) / 64;
-  p.win_rows = p.Sw > 0 ? (p.n_win + p.Sw - 1) / p.Sw : 64;
+  // Window slices of about as many rows as a chunk workgroup attends (at least 64), of
+  // equal size.
+  const int64_t target = per_chunk * cpb > 64 ? per_chunk * cpb : 64;
+  p.Sw = (int)((p.n_win + target - 1) / target);
+  p.win_rows = p.Sw > 0 ? (int)((p.n_win + p.Sw - 1) / p.Sw) : 64;
   p.parts = p.Sc + p.Sw;
   size_t off = p.r.total;
   const size_t rows = (size_t)B * Hq;

@@ -74,18 +74,19 @@ __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
   __syncthreads();
 
   const int64_t p0 = (int64_t)c * CH;
+  const int64_t pw = p0 + (int64_t)wave * (64 * LPT) + (t & 63);   // item i: pw + 64*i
   const V *base = reinterpret_cast<const V *>(codes + ((int64_t)bh * cap + lo) * W);
   // Non-temporal loads: the codes are read exactly once.  Whole chunks load without
   // predication; only the last chunk of a head can be partial.
   V v[LPT];
   if (p0 + CH <= C) {
-    const V *bp = base + p0 + t;
+    const V *bp = base + pw;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) v[i] = __builtin_nontemporal_load(bp + i * kScanThreads);
+    for (int i = 0; i < LPT; ++i) v[i] = __builtin_nontemporal_load(bp + 64 * i);
   } else {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int64_t p = p0 + i * kScanThreads + t;
+      const int64_t p = pw + 64 * i;
       v[i] = (p < C) ? __builtin_nontemporal_load(base + p) : CV::zero();
     }
   }
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = 4 * i4 + j;
-      const int64_t p = p0 + i * kScanThreads + t;
+      const int64_t p = pw + 64 * i;
       uint32_t d = 0xFFu;                      // past the last candidate: never selected
       if (p < C) {
         d = CV::dist(v[i], q);
@@ -313,8 +314,8 @@ __global__ __launch_bounds__(kScanThreads) void topk_emit_kernel(
   const int quota = pr.y;
   if (T < 0 || chunk_selected(mt, quota) == 0) return;
   int32_t *out = idx + (int64_t)bh * k;
-  emit_chunk<LPT>(w, T, quota, mt.x, mt.y, lo + (int64_t)c * CH,
-                  [&](int pos, int, int32_t tok) { out[pos] = tok; });
+  emit_chunks<LPT, 1>([&](int, int kk) { return w[kk]; }, [&](int) { return mt; }, 1, T, quota,
+                      lo + (int64_t)c * CH, [&](int pos, int32_t tok) { out[pos] = tok; });
 }
 
 __global__ void window_indices_kernel(int32_t n_sinks, int64_t local0, int32_t n,

@@ -233,9 +233,13 @@ def test_sparse_decode_shared_list_stride0():
         assert np.max(np.abs(lse[b].cpu().numpy() - rl)) <= 2e-2
 
 
-def test_lse_merge_matches_oracle():
-    rng = np.random.default_rng(11)
-    P, rows, d = 5, 300, 128
+@pytest.mark.parametrize("P,d", [(1, 128), (5, 128), (37, 128), (64, 128), (65, 128), (200, 128),
+                                 (5, 96)], ids=lambda v: str(v))
+def test_lse_merge_matches_oracle(P, d):
+    """Both merge kernels: up to 64 parts of d = 128 (one workgroup per row, wavefronts
+    over parts), and the general one."""
+    rng = np.random.default_rng(11 + P + d)
+    rows = 300
     o_parts = rng.standard_normal((P, rows, d)).astype(np.float32)
     lse_parts = (rng.standard_normal((P, rows)) * 4).astype(np.float32)
     lse_parts[rng.random((P, rows)) < 0.3] = -np.inf
