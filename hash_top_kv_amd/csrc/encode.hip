@@ -83,33 +83,19 @@ struct HashPtrs {
 };
 
 // ------------------------------------------------------------------ VALU kernel
-// mode 0: row r = (bh, t0 + j) of the key cache; mode 1: row r = (b, KV head), the
-// input is the fp32 mean of the group's G query vectors.
+// fp32 keys: row r = (bh, t0 + j) of the key cache, one workgroup per key.
 template <bool BF16, bool MLP, int BITS>
 __global__ __launch_bounds__(256) void encode_valu_kernel(HashPtrs hp, const void *__restrict__ x,
-                                                          int mode, int64_t nt, int64_t cap,
-                                                          int64_t t0, int Hq, int Hkv,
+                                                          int64_t nt, int64_t cap, int64_t t0,
                                                           uint32_t *__restrict__ out) {
   constexpr int W = BITS / 32;
   __shared__ float xs[kHeadDim];
   __shared__ float hid[kHidden];
   const int64_t r = blockIdx.x;
   const int t = threadIdx.x;
-  uint32_t *dst;
-  if (mode == 0) {
-    const int64_t bh = r / nt, tok = t0 + (r - bh * nt);
-    if (t < kHeadDim) xs[t] = elem<BF16>(x, (size_t)(bh * cap + tok) * kHeadDim + t);
-    dst = out + (bh * cap + tok) * W;
-  } else {
-    const int64_t b = r / Hkv, g = r - b * Hkv;
-    const int G = Hq / Hkv;
-    if (t < kHeadDim) {
-      float s = 0.f;
-      for (int j = 0; j < G; ++j) s += elem<BF16>(x, (size_t)((b * Hq + g * G + j) * kHeadDim + t));
-      xs[t] = s / (float)G;
-    }
-    dst = out + r * W;
-  }
+  const int64_t bh = r / nt, tok = t0 + (r - bh * nt);
+  if (t < kHeadDim) xs[t] = elem<BF16>(x, (size_t)(bh * cap + tok) * kHeadDim + t);
+  uint32_t *dst = out + (bh * cap + tok) * W;
   __syncthreads();
   float y = 0.f;
   if constexpr (MLP) {
@@ -133,6 +119,320 @@ __global__ __launch_bounds__(256) void encode_valu_kernel(HashPtrs hp, const voi
   if ((t & 63) == 0 && wave * 64 < BITS) {
     dst[2 * wave] = (uint32_t)mask;
     if (2 * wave + 1 < W) dst[2 * wave + 1] = (uint32_t)(mask >> 32);
+  }
+}
+
+// ------------------------------------------------------------------ query kernel (fp32)
+// The query code of each (b, KV head) for fp32 hashes: the fp32 mean of the group's G
+// query vectors, hashed in fp32 arithmetic.  kQRows rows per workgroup.  Every thread requests its
+// whole weight rows at the start (row t of W1 or R; for the MLP also one half of row t/2
+// of W2), so the kernel makes one memory round trip before the arithmetic; the two
+// halves of a W2 row are summed by neighbouring lanes.
+constexpr int kQRows = 2;
+
+template <bool BF16, bool MLP, int BITS>
+__global__ __launch_bounds__(256) void encode_query_kernel(HashPtrs hp, const void *__restrict__ q,
+                                                           int64_t rows, int Hq, int Hkv,
+                                                           uint32_t *__restrict__ out) {
+  constexpr int D = kHeadDim, NH = kHidden, W = BITS / 32;
+  constexpr int EPV = BF16 ? 8 : 4;            // elements per 16-byte vector
+  constexpr int V1 = D / EPV;                  // vectors per GEMM1 row
+  constexpr int V2 = (NH / 2) / EPV;           // vectors per half GEMM2 row
+  __shared__ float xs[kQRows][D];
+  __shared__ float hid[kQRows][NH];
+  const int64_t r0 = (int64_t)blockIdx.x * kQRows;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+
+  auto unpack = [&](const uint4 &v, float *f) {
+    if constexpr (BF16) {
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(u[i] << 16);
+        f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+      }
+    } else {
+      f[0] = __uint_as_float(v.x);
+      f[1] = __uint_as_float(v.y);
+      f[2] = __uint_as_float(v.z);
+      f[3] = __uint_as_float(v.w);
+    }
+  };
+  constexpr size_t ES = BF16 ? 2 : 4;
+  const bool has1 = MLP || t < BITS;
+  uint4 w1[V1];
+  if (has1) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(
+        static_cast<const char *>(MLP ? hp.W1 : hp.R) + (size_t)t * D * ES);
+#pragma unroll
+    for (int i = 0; i < V1; ++i) w1[i] = p[i];
+  }
+  uint4 w2[MLP ? V2 : 1];
+  auto load_w2 = [&]() {
+    if (t < 2 * BITS) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(
+          static_cast<const char *>(hp.W2) + ((size_t)(t >> 1) * NH + (NH / 2) * (t & 1)) * ES);
+#pragma unroll
+      for (int i = 0; i < V2; ++i) w2[i] = p[i];
+    }
+  };
+  // bf16 weights: both rows in flight at once.  fp32 rows are twice as large; their W2
+  // half is requested after the first product so that the registers suffice.
+  if constexpr (MLP && BF16) load_w2();
+  const int G = Hq / Hkv;
+  for (int i = t; i < kQRows * D; i += 256) {
+    const int rr = i / D, e = i - rr * D;
+    const int64_t r = r0 + rr;
+    float sum = 0.f;
+    if (r < rows) {
+      const int64_t b = r / Hkv, g = r - b * Hkv;
+      float v[kMaxGroup];                      // all loads issued before any is summed
+#pragma unroll
+      for (int j = 0; j < kMaxGroup; ++j)
+        v[j] = j < G ? elem<BF16>(q, (size_t)((b * Hq + g * G + j) * D + e)) : 0.f;
+#pragma unroll
+      for (int j = 0; j < kMaxGroup; ++j) sum += v[j];
+    }
+    xs[rr][e] = sum / (float)G;
+  }
+  __syncthreads();
+  float a[kQRows];
+#pragma unroll
+  for (int rr = 0; rr < kQRows; ++rr) a[rr] = 0.f;
+  if (has1) {
+#pragma unroll
+    for (int i = 0; i < V1; ++i) {
+      float f[EPV];
+      unpack(w1[i], f);
+#pragma unroll
+      for (int rr = 0; rr < kQRows; ++rr)
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) a[rr] = fmaf(f[k], xs[rr][i * EPV + k], a[rr]);
+    }
+  }
+  float y[kQRows];
+  if constexpr (MLP) {
+    if constexpr (!BF16) load_w2();
+    const float bias1 = hp.b1 ? elem<BF16>(hp.b1, t) : 0.f;
+#pragma unroll
+    for (int rr = 0; rr < kQRows; ++rr) {
+      float h = gelu(a[rr] + bias1);
+      if constexpr (BF16) h = round_bf16(h);
+      hid[rr][t] = h;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < kQRows; ++rr) y[rr] = 0.f;
+    if (t < 2 * BITS) {
+      const int e0 = (NH / 2) * (t & 1);
+#pragma unroll
+      for (int i = 0; i < V2; ++i) {
+        float f[EPV];
+        unpack(w2[i], f);
+#pragma unroll
+        for (int rr = 0; rr < kQRows; ++rr)
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) y[rr] = fmaf(f[k], hid[rr][e0 + i * EPV + k], y[rr]);
+      }
+    }
+    const float bias2 = (hp.b2 && t < 2 * BITS) ? elem<BF16>(hp.b2, t >> 1) : 0.f;
+#pragma unroll
+    for (int rr = 0; rr < kQRows; ++rr) y[rr] += __shfl_xor(y[rr], 1) + bias2;
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < kQRows; ++rr) y[rr] = a[rr];
+  }
+  // Sign bits.  MLP: lanes 2j and 2j+1 both hold bit 32*wave + j; LSH: lane l holds bit
+  // 64*wave + l.
+#pragma unroll
+  for (int rr = 0; rr < kQRows; ++rr) {
+    const int64_t r = r0 + rr;
+    const bool valid = MLP ? (t < 2 * BITS) : (t < BITS);
+    const uint64_t m = __ballot(valid && y[rr] > 0.f);
+    if (r >= rows || lane != 0) continue;
+    if constexpr (MLP) {
+      if (wave < W) {
+        uint64_t x = m & 0x5555555555555555ull;            // even lanes -> 32 bits
+        x = (x | (x >> 1)) & 0x3333333333333333ull;
+        x = (x | (x >> 2)) & 0x0F0F0F0F0F0F0F0Full;
+        x = (x | (x >> 4)) & 0x00FF00FF00FF00FFull;
+        x = (x | (x >> 8)) & 0x0000FFFF0000FFFFull;
+        x = (x | (x >> 16)) & 0x00000000FFFFFFFFull;
+        out[r * W + wave] = (uint32_t)x;
+      }
+    } else {
+      if (2 * wave < W) {
+        out[r * W + 2 * wave] = (uint32_t)m;
+        out[r * W + 2 * wave + 1] = (uint32_t)(m >> 32);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ query kernel (bf16)
+// bf16 hashes on the matrix cores: 16 query rows per workgroup (one 16-row tile), one
+// 16-column tile of each product per wavefront (16 wavefronts, so the weight fragments,
+// the products and the GELUs are spread over as many SIMD slots as there are tiles).  The fp32 group mean x is split exactly into
+// three bf16 parts (x = hi + mid + lo to 24 bits), so x . w accumulates in fp32 from
+// exact products, as an fp32 dot product would.  The MLP's hidden activation is bf16 by
+// definition (rounded after GELU), so the second product needs no split.
+//   A operand (16 x 32): lane l holds row l%16, k = 8*(l/16) .. +7 of a 32-wide k-step;
+//   B operand (32 x 16): lane l holds column l%16, the same 8 k's;
+//   result: lane l holds column l%16 of rows 4*(l/16) .. +3.
+constexpr int kQTile = 16;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 split_bf16(const float (&x)[8], float (&rest)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t b = bf16_bits(x[i]);
+    r[i] = __builtin_bit_cast(__bf16, (uint16_t)b);
+    rest[i] = x[i] - __uint_as_float(b << 16);           // exact
+  }
+  return r;
+}
+
+template <bool MLP, int BITS>
+__global__ __launch_bounds__(1024) void encode_query_mfma_kernel(HashPtrs hp,
+                                                                 const uint16_t *__restrict__ q,
+                                                                 int64_t rows, int Hq, int Hkv,
+                                                                 uint32_t *__restrict__ out) {
+  constexpr int D = kHeadDim, NH = kHidden, W = BITS / 32;
+  constexpr int N1 = MLP ? NH : BITS;          // first product's columns
+  constexpr int NT1 = N1 / 16, NT2 = MLP ? BITS / 16 : 0;   // 16-column tiles
+  static_assert(NT1 <= 16 && NT2 <= 16, "one tile per wavefront");
+  // The weights are copied to LDS with contiguous loads (16 lanes per 256-byte row
+  // segment): reading the matrix-core fragments straight from memory (16 rows x 64 bytes
+  // per load instruction) takes several times longer through one CU.  Rows are padded by
+  // 16 bytes so that the fragment reads from LDS spread over the banks.
+  constexpr int P1 = D + 8, P2 = NH + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t w1s[N1 * P1];
+  __shared__ __attribute__((aligned(16))) uint16_t w2s[MLP ? BITS * P2 : 8];
+  __shared__ float xs[kQTile][D];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[MLP ? kQTile : 1][MLP ? P2 : 8];
+  __shared__ uint32_t words[kQTile][W];
+  const int64_t r0 = (int64_t)blockIdx.x * kQTile;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const bool has1 = wave < NT1, has2 = MLP && wave < NT2;
+  {
+    constexpr int C1 = N1 * D / 8, C2 = MLP ? BITS * NH / 8 : 0;   // 16-byte vectors
+    constexpr int L1 = (C1 + 1023) / 1024, L2 = (C2 + 1023) / 1024;
+    const uint4 *g1 = static_cast<const uint4 *>(MLP ? hp.W1 : hp.R);
+    uint4 v1[L1];
+#pragma unroll
+    for (int i = 0; i < L1; ++i) {
+      const int c = t + 1024 * i;
+      v1[i] = c < C1 ? g1[c] : make_uint4(0, 0, 0, 0);
+    }
+    uint4 v2[L2 > 0 ? L2 : 1];
+    if constexpr (MLP) {
+      const uint4 *g2 = static_cast<const uint4 *>(hp.W2);
+#pragma unroll
+      for (int i = 0; i < L2; ++i) {
+        const int c = t + 1024 * i;
+        v2[i] = c < C2 ? g2[c] : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < L1; ++i) {
+      const int c = t + 1024 * i;
+      if (c < C1) *reinterpret_cast<uint4 *>(&w1s[(c / (D / 8)) * P1 + 8 * (c % (D / 8))]) = v1[i];
+    }
+    if constexpr (MLP) {
+#pragma unroll
+      for (int i = 0; i < L2; ++i) {
+        const int c = t + 1024 * i;
+        if (c < C2) *reinterpret_cast<uint4 *>(&w2s[(c / (NH / 8)) * P2 + 8 * (c % (NH / 8))]) = v2[i];
+      }
+    }
+  }
+  if (t < kQTile * W) words[t / W][t % W] = 0u;
+  // Group means: thread t -> row t/64, dims 2*(t%64), +1.  All G <= 8 loads are issued
+  // before any is summed.
+  {
+    const int rr = t >> 6, e0 = 2 * (t & 63);
+    const int64_t r = r0 + rr;
+    float acc0 = 0.f, acc1 = 0.f;
+    if (r < rows) {
+      const int64_t b = r / Hkv, hg = r - b * Hkv;
+      const int G = Hq / Hkv;
+      uint32_t v[kMaxGroup];
+#pragma unroll
+      for (int j = 0; j < kMaxGroup; ++j)
+        v[j] = j < G ? *reinterpret_cast<const uint32_t *>(q + (size_t)((b * Hq + hg * G + j) * D + e0)) : 0u;
+#pragma unroll
+      for (int j = 0; j < kMaxGroup; ++j) {
+        acc0 += __uint_as_float(v[j] << 16);
+        acc1 += __uint_as_float(v[j] & 0xFFFF0000u);
+      }
+      acc0 = acc0 / (float)G;
+      acc1 = acc1 / (float)G;
+    }
+    xs[rr][e0] = acc0;
+    xs[rr][e0 + 1] = acc1;
+  }
+  __syncthreads();
+  f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (has1) {
+    // A fragments of x: three bf16 parts per k-step.
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int col = 16 * wave + n;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      float x[8], r1[8], r2[8], r3[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = xs[n][32 * ks + 8 * g + i];
+      const bf16x8 p0 = split_bf16(x, r1), p1 = split_bf16(r1, r2), p2 = split_bf16(r2, r3);
+      const bf16x8 bw = *reinterpret_cast<const bf16x8 *>(&w1s[col * P1 + 32 * ks + 8 * g]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p0, bw, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p1, bw, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p2, bw, acc, 0, 0, 0);
+    }
+    if constexpr (MLP) {
+      const float bias = hp.b1 ? elem<true>(hp.b1, col) : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hs[4 * g + j][col] = (uint16_t)bf16_bits(gelu(acc[j] + bias));
+    } else {
+      y = acc;
+    }
+  }
+  if constexpr (MLP) {
+    __syncthreads();
+    if (has2) {
+      const int col = 16 * wave + n;
+#pragma unroll
+      for (int ks = 0; ks < NH / 32; ++ks) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(&hs[n][32 * ks + 8 * g]);
+        const bf16x8 bw = *reinterpret_cast<const bf16x8 *>(&w2s[col * P2 + 32 * ks + 8 * g]);
+        y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw, y, 0, 0, 0);
+      }
+    }
+  }
+  // Sign bits: wavefront w covers bits 16w .. 16w+15; the ballot of register j holds, in
+  // lanes 16g .. 16g+15, those bits of row 4g + j.
+  constexpr int NT = MLP ? NT2 : NT1;
+  if (wave < NT) {
+    const int col = 16 * wave + n;
+    const float bias = (MLP && hp.b2) ? elem<true>(hp.b2, col) : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t m = __ballot(y[j] + bias > 0.f);
+      if (lane < 4) {
+        const int row = 4 * lane + j;
+        const uint32_t bits16 = (uint32_t)(m >> (16 * lane)) & 0xFFFFu;
+        atomicOr(&words[row][wave >> 1], bits16 << (16 * (wave & 1)));
+      }
+    }
+  }
+  __syncthreads();
+  if (t < kQTile * W) {
+    const int rr = t / W, wd = t - rr * W;
+    if (r0 + rr < rows) out[(r0 + rr) * W + wd] = words[rr][wd];
   }
 }
 
@@ -316,22 +616,22 @@ hipError_t mfma_launch(const HashPtrs &hp, const void *k, int64_t nt, int64_t ca
 }
 
 template <bool BF16, bool MLP, int BITS>
-hipError_t valu_launch(const HashPtrs &hp, const void *x, int mode, int64_t rows, int64_t nt,
-                       int64_t cap, int64_t t0, int Hq, int Hkv, uint32_t *out, hipStream_t st) {
+hipError_t valu_launch(const HashPtrs &hp, const void *x, int64_t rows, int64_t nt, int64_t cap,
+                       int64_t t0, uint32_t *out, hipStream_t st) {
   hipLaunchKernelGGL((encode_valu_kernel<BF16, MLP, BITS>), dim3((unsigned)rows), dim3(256), 0,
-                     st, hp, x, mode, nt, cap, t0, Hq, Hkv, out);
+                     st, hp, x, nt, cap, t0, out);
   return hipGetLastError();
 }
 
 template <bool BF16>
-hipError_t valu_dispatch(const hk_hash &h, const void *x, int mode, int64_t rows, int64_t nt,
-                         int64_t cap, int64_t t0, int Hq, int Hkv, uint32_t *out, hipStream_t st) {
+hipError_t valu_dispatch(const hk_hash &h, const void *x, int64_t rows, int64_t nt, int64_t cap,
+                         int64_t t0, uint32_t *out, hipStream_t st) {
   const HashPtrs hp{h.R, h.W1, h.b1, h.W2, h.b2};
   const bool mlp = h.kind == HK_HASH_MLP;
-  if (mlp && h.bits == 128) return valu_launch<BF16, true, 128>(hp, x, mode, rows, nt, cap, t0, Hq, Hkv, out, st);
-  if (mlp) return valu_launch<BF16, true, 64>(hp, x, mode, rows, nt, cap, t0, Hq, Hkv, out, st);
-  if (h.bits == 128) return valu_launch<BF16, false, 128>(hp, x, mode, rows, nt, cap, t0, Hq, Hkv, out, st);
-  return valu_launch<BF16, false, 64>(hp, x, mode, rows, nt, cap, t0, Hq, Hkv, out, st);
+  if (mlp && h.bits == 128) return valu_launch<BF16, true, 128>(hp, x, rows, nt, cap, t0, out, st);
+  if (mlp) return valu_launch<BF16, true, 64>(hp, x, rows, nt, cap, t0, out, st);
+  if (h.bits == 128) return valu_launch<BF16, false, 128>(hp, x, rows, nt, cap, t0, out, st);
+  return valu_launch<BF16, false, 64>(hp, x, rows, nt, cap, t0, out, st);
 }
 
 }  // namespace
@@ -341,7 +641,7 @@ hipError_t launch_encode_keys(const hk_hash &h, const void *k, int B, int Hkv, i
   const int64_t nt = t1 - t0;
   const int64_t total = (int64_t)B * Hkv * nt;
   if (total == 0) return hipSuccess;
-  if (h.dtype == HK_F32) return valu_dispatch<false>(h, k, 0, total, nt, cap, t0, 0, 1, codes, st);
+  if (h.dtype == HK_F32) return valu_dispatch<false>(h, k, total, nt, cap, t0, codes, st);
   const HashPtrs hp{h.R, h.W1, h.b1, h.W2, h.b2};
   const bool mlp = h.kind == HK_HASH_MLP;
   if (mlp && h.bits == 128) return mfma_launch<true, 128>(hp, k, nt, cap, t0, total, codes, st);
@@ -354,8 +654,29 @@ hipError_t launch_encode_query(const hk_hash &h, const void *q, int B, int Hq, i
                                uint32_t *qcodes, hipStream_t st) {
   const int64_t rows = (int64_t)B * Hkv;
   if (rows == 0) return hipSuccess;
-  if (h.dtype == HK_F32) return valu_dispatch<false>(h, q, 1, rows, 1, 0, 0, Hq, Hkv, qcodes, st);
-  return valu_dispatch<true>(h, q, 1, rows, 1, 0, 0, Hq, Hkv, qcodes, st);
+  const HashPtrs hp{h.R, h.W1, h.b1, h.W2, h.b2};
+  const bool mlp = h.kind == HK_HASH_MLP, bf = h.dtype == HK_BF16;
+  if (bf) {
+    const dim3 g16((unsigned)((rows + kQTile - 1) / kQTile));
+    const uint16_t *qb = static_cast<const uint16_t *>(q);
+    if (mlp && h.bits == 128)
+      hipLaunchKernelGGL((encode_query_mfma_kernel<true, 128>), g16, dim3(1024), 0, st, hp, qb, rows, Hq, Hkv, qcodes);
+    else if (mlp)
+      hipLaunchKernelGGL((encode_query_mfma_kernel<true, 64>), g16, dim3(1024), 0, st, hp, qb, rows, Hq, Hkv, qcodes);
+    else if (h.bits == 128)
+      hipLaunchKernelGGL((encode_query_mfma_kernel<false, 128>), g16, dim3(1024), 0, st, hp, qb, rows, Hq, Hkv, qcodes);
+    else
+      hipLaunchKernelGGL((encode_query_mfma_kernel<false, 64>), g16, dim3(1024), 0, st, hp, qb, rows, Hq, Hkv, qcodes);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((rows + kQRows - 1) / kQRows));
+#define HK_Q(BFV, MLPV, BITSV)                                                                \
+  hipLaunchKernelGGL((encode_query_kernel<BFV, MLPV, BITSV>), grid, dim3(256), 0, st, hp, q, \
+                     rows, Hq, Hkv, qcodes)
+  if (mlp) { if (h.bits == 128) HK_Q(false, true, 128); else HK_Q(false, true, 64); }
+  else { if (h.bits == 128) HK_Q(false, false, 128); else HK_Q(false, false, 64); }
+#undef HK_Q
+  return hipGetLastError();
 }
 
 }  // namespace hk
