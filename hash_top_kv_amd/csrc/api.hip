@@ -11,6 +11,10 @@ inline hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
 inline hk_status from_hip(hipError_t e) { return e == hipSuccess ? HK_OK : HK_ERR_HIP; }
 
+// The kernels read and write these tensors as 16-byte (8-byte for 64-bit codes) vectors.
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+inline uintptr_t code_align(int bits) { return bits == 64 ? 8 : 16; }
+
 hk_status check_hash(const hk_hash *h) {
   if (!h) return HK_ERR_INVALID_ARGUMENT;
   if (h->dtype != HK_F32 && h->dtype != HK_BF16) return HK_ERR_UNSUPPORTED;
@@ -18,9 +22,11 @@ hk_status check_hash(const hk_hash *h) {
   if (h->bits != 64 && h->bits != 128) return HK_ERR_UNSUPPORTED;
   if (h->kind == HK_HASH_LSH) {
     if (!h->R) return HK_ERR_INVALID_ARGUMENT;
+    if (!aligned(h->R, 16)) return HK_ERR_UNSUPPORTED;
   } else if (h->kind == HK_HASH_MLP) {
     if (h->hidden != kHidden) return HK_ERR_UNSUPPORTED;
     if (!h->W1 || !h->W2) return HK_ERR_INVALID_ARGUMENT;
+    if (!aligned(h->W1, 16) || !aligned(h->W2, 16)) return HK_ERR_UNSUPPORTED;
   } else {
     return HK_ERR_UNSUPPORTED;
   }
@@ -60,6 +66,7 @@ hk_status hk_encode_keys(const hk_hash *h, const void *k, int B, int Hkv, int64_
   if (B < 0 || Hkv < 0 || cap < 0 || t0 < 0 || t1 < t0 || t1 > cap) return HK_ERR_INVALID_ARGUMENT;
   if ((int64_t)B * Hkv * (t1 - t0) == 0) return HK_OK;
   if (!k || !codes) return HK_ERR_INVALID_ARGUMENT;
+  if (!aligned(k, 16) || !aligned(codes, code_align(h->bits))) return HK_ERR_UNSUPPORTED;
   return from_hip(launch_encode_keys(*h, k, B, Hkv, cap, t0, t1, codes, as_stream(stream)));
 }
 
@@ -70,6 +77,7 @@ hk_status hk_encode_query(const hk_hash *h, const void *q, int B, int Hq, int Hk
   if (B < 0 || Hq < 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq < Hkv) return HK_ERR_INVALID_ARGUMENT;
   if ((int64_t)B * Hkv == 0) return HK_OK;
   if (!q || !qcodes) return HK_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16)) return HK_ERR_UNSUPPORTED;
   return from_hip(launch_encode_query(*h, q, B, Hq, Hkv, qcodes, as_stream(stream)));
 }
 
@@ -87,6 +95,7 @@ hk_status hk_hamming_scan(const uint32_t *codes, const uint32_t *qcodes, int bit
   const RetrievePlan p = plan_retrieve(bits, B, Hkv, n_ctx, n_sink, n_local, k);
   if (p.BH == 0 || p.S == 0) return HK_OK;
   if (!codes || !qcodes || !ws) return HK_ERR_INVALID_ARGUMENT;
+  if (!aligned(codes, code_align(bits))) return HK_ERR_UNSUPPORTED;
   if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
   return from_hip(launch_hamming_scan(p, codes, qcodes, cap, ws, as_stream(stream)));
 }
@@ -113,6 +122,7 @@ hk_status hk_retrieve_topk(const uint32_t *codes, const uint32_t *qcodes, int bi
   if (p.BH == 0) return HK_OK;
   if (!count || !ws || (p.keff > 0 && !idx)) return HK_ERR_INVALID_ARGUMENT;
   if (p.S > 0 && (!codes || !qcodes)) return HK_ERR_INVALID_ARGUMENT;
+  if (p.S > 0 && !aligned(codes, code_align(bits))) return HK_ERR_UNSUPPORTED;
   if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
   hipError_t e = launch_hamming_scan(p, codes, qcodes, cap, ws, as_stream(stream));
   if (e != hipSuccess) return HK_ERR_HIP;
@@ -143,6 +153,8 @@ hk_status hk_retrieve_attend(const uint32_t *codes, const uint32_t *qcodes, int 
   if (p.parts > 0 && (!kc || !vc)) return HK_ERR_INVALID_ARGUMENT;
   if (p.r.S > 0 && (!codes || !qcodes)) return HK_ERR_INVALID_ARGUMENT;
   if (p.r.keff > 0 && !idx) return HK_ERR_INVALID_ARGUMENT;
+  if (p.r.S > 0 && !aligned(codes, code_align(bits))) return HK_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16)) return HK_ERR_UNSUPPORTED;
   if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
   const hipStream_t st = as_stream(stream);
   hipError_t e = launch_hamming_scan(p.r, codes, qcodes, cap, ws, st);
@@ -168,6 +180,7 @@ hk_status hk_select_attend(int bits, const void *q, const void *kc, const void *
   if (!q || !count || !o || !lse || !ws) return HK_ERR_INVALID_ARGUMENT;
   if (p.parts > 0 && (!kc || !vc)) return HK_ERR_INVALID_ARGUMENT;
   if (p.r.keff > 0 && !idx) return HK_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16)) return HK_ERR_UNSUPPORTED;
   if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
   const hipStream_t st = as_stream(stream);
   hipError_t e = launch_topk_threshold(p.r, count, ws, st);
@@ -208,6 +221,7 @@ hk_status hk_sparse_decode(const void *q, const void *k, const void *v, int dtyp
   if ((int64_t)B * Hq == 0) return HK_OK;
   if (!q || !o || !lse) return HK_ERR_INVALID_ARGUMENT;
   if (max_count > 0 && (!k || !v || !idx)) return HK_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return HK_ERR_UNSUPPORTED;
   const DecodePlan p = plan_decode(B, Hq, Hkv, max_count);
   if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
   if (p.total > 0 && !ws) return HK_ERR_INVALID_ARGUMENT;

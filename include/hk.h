@@ -28,6 +28,10 @@
  *    first), words in increasing order.  A bit is 1 iff its pre-sign value is > 0.
  *  - GQA: query head h belongs to KV head h / G with G = Hq / Hkv (contiguous groups).
  *  - Token indices are int32; contexts are limited to 2^31 - 1 tokens.
+ *  - Alignment: hash weights (R, W1, W2), keys, queries, K/V caches and key codes are
+ *    read or written as 16-byte vectors (8-byte for 64-bit codes); a pointer that is not
+ *    aligned to that returns HK_ERR_UNSUPPORTED.  (Allocations from hipMalloc and
+ *    PyTorch are 256-byte aligned; row strides are multiples of 16 bytes by the shapes.)
  */
 #ifndef HK_H
 #define HK_H

@@ -89,6 +89,19 @@ def test_host_validation_without_gpu(hk):
     assert L.hk_lse_merge(dummy, dummy, 0, 4, 128, dummy, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
     assert L.hk_lse_merge(dummy, dummy, 2, -1, 128, dummy, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
     assert L.hk_lse_merge(P, P, 2, 0, 128, P, P, P) == hk.HK_OK
+    # misaligned vector operands
+    odd = ctypes.c_void_p(0x1004)
+    h = hk._Hash(hk.HK_HASH_LSH, hk.HK_BF16, 128, 128, 0, odd, P, P, P, P)
+    assert L.hk_encode_keys(ctypes.byref(h), dummy, 1, 1, 10, 0, 10, dummy, P) == hk.HK_ERR_UNSUPPORTED
+    h = hk._Hash(hk.HK_HASH_LSH, hk.HK_BF16, 128, 128, 0, dummy, P, P, P, P)
+    assert L.hk_encode_keys(ctypes.byref(h), odd, 1, 1, 10, 0, 10, dummy, P) == hk.HK_ERR_UNSUPPORTED
+    assert L.hk_encode_keys(ctypes.byref(h), dummy, 1, 1, 10, 0, 10, odd, P) == hk.HK_ERR_UNSUPPORTED
+    assert L.hk_encode_query(ctypes.byref(h), odd, 1, 8, 4, dummy, P) == hk.HK_ERR_UNSUPPORTED
+    wsz = L.hk_retrieve_topk_workspace(128, 1, 1, 10, 0, 0, 3)
+    assert L.hk_retrieve_topk(odd, dummy, 128, 1, 1, 10, 10, 0, 0, 3, dummy, dummy, dummy, wsz, P) \
+        == hk.HK_ERR_UNSUPPORTED
+    assert L.hk_sparse_decode(dummy, odd, dummy, hk.HK_BF16, 1, 8, 4, 128, 10, dummy, 4, P, 4, f,
+                              dummy, dummy, dummy, 1 << 30, P) == hk.HK_ERR_UNSUPPORTED
     n = ctypes.c_int32(-1)
     assert L.hk_window_indices(100, 4, 64, P, ctypes.byref(n), P) == hk.HK_OK and n.value == 68
     assert L.hk_window_indices(-1, 4, 64, P, ctypes.byref(n), P) == hk.HK_ERR_INVALID_ARGUMENT
