@@ -24,7 +24,8 @@ ARCH = "gfx950"
 # online-softmax rescale multiplies them in place, which with accumulation registers
 # costs a copy out and back per tile and a larger register footprint.
 EXTRA_FLAGS = {"attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-               "fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+               "fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "encode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

@@ -6,58 +6,55 @@
 // Bit j of a code is [y_j > 0], stored at bit j%32 of word j/32.
 //
 // bf16 keys (prefill of a whole cache, or one appended token) run on the matrix cores:
-// each wavefront encodes 64 tokens per tile with v_mfma_f32_32x32x16_bf16.
+// each wavefront encodes 32 tokens per tile with v_mfma_f32_32x32x16_bf16.
 //   GEMM1   H^T = W1 . X^T   A = W1 fragments from LDS, B = the tokens' rows loaded
 //                            straight from HBM (each lane reads 128 contiguous bytes)
 //   GELU    on the fp32 accumulators, bias, rounding to bf16 -- the accumulator layout
 //           of H^T (one token column per lane) is already the B-operand layout of the
 //           second GEMM once W2's hidden index is permuted the same way in LDS, so the
-//           hidden activations never leave registers
+//           hidden activations never leave registers.
 //   GEMM2   Y^T = W2 . H^T
-//   pack    lane m (+32) holds 16 of the 32 bits of token m for each 32-bit output
-//           tile; the two halves are OR-ed across lanes m and m+32 and stored as one
-//           16-byte code per token.
+//   pack    lane i (+32) holds 16 of the 32 bits of token i for each 32-bit output
+//           tile; the two halves are OR-ed across lanes i and i+32, and each lane of
+//           the pair stores half of the token's code.
+// The MLP is bound by the vector ALU (the GELU: 11 vector instructions and two
+// transcendentals per hidden unit), not by the matrix cores.
 // Weights are staged in LDS once per workgroup in fragment order (64 lanes x 16 bytes
 // per fragment), so every fragment read is one conflict-free ds_read_b128.
 // Query codes (B*Hkv rows) and fp32 keys use a plain VALU kernel, one row per
 // workgroup.
 //
-// The erf of GELU uses the Chebyshev fit of erfc from Numerical Recipes (Press et al.,
-// section 6.2, "erfcc"), fractional error below 1.2e-7 everywhere: branch-free, one
-// reciprocal and one exponential.
+// The erf of GELU is the rational approximation of Abramowitz & Stegun 7.1.26
+// (absolute error below 1.5e-7): branch-free, one reciprocal and one exponential.
 #include "hk_internal.h"
 
 namespace hk {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr float kRsqrt2 = 0.70710678118654752f;
-
-// erfc(z) for z >= 0 (Numerical Recipes "erfcc").
-__device__ __forceinline__ float erfc_nonneg(float z) {
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
-  float p = 0.17087277f;
-  p = fmaf(p, t, -0.82215223f);
-  p = fmaf(p, t, 1.48851587f);
-  p = fmaf(p, t, -1.13520398f);
-  p = fmaf(p, t, 0.27886807f);
-  p = fmaf(p, t, -0.18628806f);
-  p = fmaf(p, t, 0.09678418f);
-  p = fmaf(p, t, 0.37409196f);
-  p = fmaf(p, t, 1.00002368f);
-  p = fmaf(p, t, -1.26551223f);
-  const float arg = fmaf(-z, z, p);
-  return t * __expf(arg);
-}
-
-// GELU(a) = a * Phi(a), Phi(a) = erfc(-a / sqrt 2) / 2.
+// GELU(a) = a Phi(a) = max(a, 0) - |a| Phi(-|a|), with Phi(-|a|) = erfc(|a| / sqrt 2) / 2
+// from the rational approximation of erf in Abramowitz & Stegun 7.1.26 (Hastings):
+// erfc(z) ~= t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z), for
+// z >= 0, absolute error at most 1.5e-7.  One reciprocal and one base-2 exponential;
+// exp(-a^2 / 2) / 2 = 2^(-a^2 log2(e) / 2 - 1).  For |a| > 13 the exponential underflows
+// to zero and GELU(a) is max(a, 0) to fp32 precision.
 __device__ __forceinline__ float gelu(float a) {
-  const float e = 0.5f * erfc_nonneg(fabsf(a) * kRsqrt2);  // Phi(-|a|)
-  return a >= 0.f ? fmaf(-a, e, a) : a * e;
+  constexpr float kP = 0.3275911f * 0.70710678118654752f;   // p / sqrt 2
+  constexpr float kHalfLog2e = -0.72134752044448170f;       // -log2(e) / 2
+  const float x = fabsf(a);
+  const float t = __builtin_amdgcn_rcpf(fmaf(kP, x, 1.0f));
+  float p = 1.061405429f;
+  p = fmaf(p, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  const float g = __builtin_amdgcn_exp2f(fmaf(x * kHalfLog2e, x, -1.0f));
+  return fmaf(-x, (p * t) * g, fmaxf(a, 0.f));
 }
 
 // Round to the nearest bf16 (ties to even); finite inputs.
@@ -437,15 +434,18 @@ __global__ __launch_bounds__(1024) void encode_query_mfma_kernel(HashPtrs hp,
 }
 
 // ------------------------------------------------------------------ MFMA kernel
-constexpr int kEncWaves = 4;
-
 template <bool MLP, int BITS> struct EncLayout {
   static constexpr int JT = BITS / 32;                // 32-bit output tiles
   static constexpr int F1 = MLP ? 8 * 8 : JT * 8;     // first-GEMM fragments
   static constexpr int F2 = MLP ? JT * 16 : 0;        // second-GEMM fragments
   static constexpr int NB1 = MLP ? kHidden : 0;       // b1 floats
   static constexpr int NB2 = MLP ? BITS : 0;          // b2 floats
-  static constexpr size_t bytes = (size_t)(F1 + F2) * 64 * 16 + (NB1 + NB2) * 4;
+  // Wavefronts per workgroup.  The MLP weights fill most of LDS, so one workgroup holds
+  // a CU: 8 wavefronts (2 per SIMD) let one wavefront's GELU run beside another's
+  // matrix-core work (12 measured no faster).  The LSH projection is small; several
+  // workgroups share a CU.
+  static constexpr int WAVES = MLP ? 8 : 4;
+  static constexpr int PER_CU = MLP ? 1 : 4;
 };
 
 // Bit position, inside its 32-bit tile, of accumulator register r of lane group g.
@@ -453,15 +453,20 @@ __device__ __forceinline__ constexpr int acc_row(int r, int g) {
   return 8 * (r >> 2) + 4 * g + (r & 3);
 }
 
-template <bool MLP, int BITS>
-__global__ __launch_bounds__(kEncWaves * 64) void encode_keys_mfma_kernel(
+// One tile = 32 tokens per wavefront.  Lane (i, g) (i = lane % 32, g = lane / 32) holds
+// token i of the tile: the B operand reads its elements 64 g + 8 ks .. + 7 for k-step
+// ks, and accumulator register r holds output row acc_row(r, g) of token i.
+// BIAS: the MLP has b1 or b2 (a null bias reads as zero).
+template <bool MLP, int BITS, bool BIAS>
+__global__ __launch_bounds__((EncLayout<MLP, BITS>::WAVES * 64)) void encode_keys_mfma_kernel(
     HashPtrs hp, const uint16_t *__restrict__ K, int64_t nt, int64_t cap, int64_t t0,
     int64_t total_rows, int64_t n_tiles, uint32_t *__restrict__ codes) {
   using L = EncLayout<MLP, BITS>;
   constexpr int JT = L::JT;
   constexpr int W = BITS / 32;
+  constexpr int NWG = L::WAVES * 64;
   __shared__ u32x4 frag[L::F1 + L::F2][64];
-  __shared__ float bias[L::NB1 + L::NB2 + 1];
+  __shared__ float bias[BIAS ? L::NB1 + L::NB2 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -471,15 +476,16 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_keys_mfma_kernel(
 
   // Stage the weights in fragment order.
   const uint16_t *A1 = static_cast<const uint16_t *>(MLP ? hp.W1 : hp.R);
-  for (int f = tid; f < L::F1 * 64; f += kEncWaves * 64) {
+  for (int f = tid; f < L::F1 * 64; f += NWG) {
     const int fi = f >> 6, fl = f & 63, i = fl & 31, g = fl >> 5;
     const int tile = fi >> 3, ks = fi & 7;      // (hidden or bit tile, k-step)
     const uint16_t *src = A1 + (size_t)(32 * tile + i) * kHeadDim + 64 * g + 8 * ks;
     frag[fi][fl] = *reinterpret_cast<const u32x4 *>(src);
   }
+  static_assert(MLP || !BIAS, "LSH has no bias");
   if constexpr (MLP) {
     const uint16_t *A2 = static_cast<const uint16_t *>(hp.W2);
-    for (int f = tid; f < L::F2 * 64; f += kEncWaves * 64) {
+    for (int f = tid; f < L::F2 * 64; f += NWG) {
       const int fi = f >> 6, fl = f & 63, i = fl & 31, g = fl >> 5;
       const int jt = fi >> 4, ks2 = fi & 15, ht = ks2 >> 1, half = ks2 & 1;
       const uint16_t *row = A2 + (size_t)(32 * jt + i) * kHidden + 32 * ht + 16 * half + 4 * g;
@@ -487,130 +493,122 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_keys_mfma_kernel(
       const u32x2 hi = *reinterpret_cast<const u32x2 *>(row + 8);
       frag[L::F1 + fi][fl] = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
-    for (int j = tid; j < L::NB1 + L::NB2; j += kEncWaves * 64) {
-      const void *bp = j < L::NB1 ? hp.b1 : hp.b2;
-      const int jj = j < L::NB1 ? j : j - L::NB1;
-      bias[j] = bp ? elem<true>(bp, jj) : 0.f;
+    if constexpr (BIAS) {
+      for (int j = tid; j < L::NB1 + L::NB2; j += NWG) {
+        const void *bp = j < L::NB1 ? hp.b1 : hp.b2;
+        const int jj = j < L::NB1 ? j : j - L::NB1;
+        bias[j] = bp ? elem<true>(bp, jj) : 0.f;
+      }
     }
   }
   __syncthreads();
 
-  for (int64_t tile = (int64_t)blockIdx.x * kEncWaves + wave; tile < n_tiles;
-       tile += (int64_t)gridDim.x * kEncWaves) {
-    // X^T fragments of the two 32-token column tiles: lane (i, g) holds token
-    // 64*tile + 32*n + i, elements 64*g .. 64*g + 63 (8 per k-step).
-    bf16x8 xf[2][8];
-    int64_t mem[2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int64_t row = tile * 64 + 32 * n + li;
-      const bool ok = row < total_rows;
-      const int64_t bh = ok ? row / nt : 0;
-      mem[n] = ok ? bh * cap + t0 + (row - bh * nt) : -1;
-      const uint16_t *src = K + (size_t)(ok ? mem[n] : 0) * kHeadDim + 64 * lg;
+  for (int64_t tile = (int64_t)blockIdx.x * L::WAVES + wave; tile < n_tiles;
+       tile += (int64_t)gridDim.x * L::WAVES) {
+    const int64_t row = tile * 32 + li;
+    const bool ok = row < total_rows;
+    const int64_t bh = ok ? row / nt : 0;
+    const int64_t mem = ok ? bh * cap + t0 + (row - bh * nt) : 0;
+    bf16x8 xf[8];
+    {
+      const uint16_t *src = K + (size_t)mem * kHeadDim + 64 * lg;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const u32x4 v = ok ? *reinterpret_cast<const u32x4 *>(src + 8 * ks) : u32x4{0u, 0u, 0u, 0u};
-        xf[n][ks] = __builtin_bit_cast(bf16x8, v);
+        xf[ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
 
-    f32x16 yacc[2][JT];
+    f32x16 yacc[JT];
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int j = 0; j < JT; ++j) yacc[n][j] = f32x16{};
+    for (int j = 0; j < JT; ++j) yacc[j] = f32x16{};
 
     if constexpr (MLP) {
-#pragma unroll 1
-      for (int ht = 0; ht < 8; ++ht) {
-        f32x16 hacc[2] = {f32x16{}, f32x16{}};
+      // H^T tile ht (hidden units 32 ht .. 32 ht + 31) of the first GEMM.
+      auto gemm1 = [&](int ht) {
+        f32x16 h = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, frag[ht * 8 + ks][lane]);
-          hacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[0][ks], hacc[0], 0, 0, 0);
-          hacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[1][ks], hacc[1], 0, 0, 0);
-        }
-        // GELU + bias + bf16 rounding; register r of lane group g is hidden unit
-        // 32*ht + acc_row(r, g).  k-step half h of the second GEMM takes r = 8h .. 8h+7.
-        bf16x8 hb[2][2];
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            u32x4 w;
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
-              const int r0 = 8 * half + 2 * s2, r1 = r0 + 1;
-              const float h0 = gelu(hacc[n][r0] + bias[32 * ht + acc_row(r0, lg)]);
-              const float h1 = gelu(hacc[n][r1] + bias[32 * ht + acc_row(r1, lg)]);
-              w[s2] = bf16_bits(h0) | (bf16_bits(h1) << 16);
-            }
-            hb[n][half] = __builtin_bit_cast(bf16x8, w);
-          }
-        }
+        for (int ks = 0; ks < 8; ++ks)
+          h = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, frag[ht * 8 + ks][lane]),
+                                                      xf[ks], h, 0, 0, 0);
+        return h;
+      };
+      // Bias, GELU and bf16 rounding of H^T tile ht, then its share of the second GEMM.
+      // Register r of lane group g is hidden unit 32 ht + acc_row(r, g); k-step half h
+      // of the second GEMM takes r = 8h .. 8h+7.
+      auto gelu_gemm2 = [&](int ht, const f32x16 &hacc) {
+        bf16x8 hb[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
+          u32x4 w;
 #pragma unroll
-          for (int j = 0; j < JT; ++j) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, frag[L::F1 + j * 16 + 2 * ht + half][lane]);
-            yacc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, hb[0][half], yacc[0][j], 0, 0, 0);
-            yacc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, hb[1][half], yacc[1][j], 0, 0, 0);
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * half + 2 * e;
+            float a0 = hacc[r], a1 = hacc[r + 1];
+            if constexpr (BIAS) {
+              a0 += bias[32 * ht + acc_row(r, lg)];
+              a1 += bias[32 * ht + acc_row(r + 1, lg)];
+            }
+            const bf16x2 pr = {(__bf16)gelu(a0), (__bf16)gelu(a1)};
+            w[e] = __builtin_bit_cast(uint32_t, pr);
           }
+          hb[half] = __builtin_bit_cast(bf16x8, w);
         }
-      }
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int j = 0; j < JT; ++j)
+            yacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, frag[L::F1 + j * 16 + 2 * ht + half][lane]), hb[half],
+                yacc[j], 0, 0, 0);
+      };
+      // Two wavefronts per SIMD overlap one's GELU with the other's products (issuing
+      // the next tile's first GEMM before this tile's GELU, or interleaving them by
+      // scheduling barriers, measured no faster).
+#pragma unroll 1
+      for (int ht = 0; ht < 8; ++ht) gelu_gemm2(ht, gemm1(ht));
     } else {
 #pragma unroll
-      for (int j = 0; j < JT; ++j) {
+      for (int j = 0; j < JT; ++j)
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, frag[j * 8 + ks][lane]);
-          yacc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[0][ks], yacc[0][j], 0, 0, 0);
-          yacc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[1][ks], yacc[1][j], 0, 0, 0);
-        }
-      }
+        for (int ks = 0; ks < 8; ++ks)
+          yacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, frag[j * 8 + ks][lane]),
+                                                            xf[ks], yacc[j], 0, 0, 0);
     }
 
-    // Sign bits.  Lanes li and li+32 hold complementary halves of each word of token
-    // 32*n + li; OR them, then lane (li, lg) stores token 32*lg + li.
-    uint32_t words[2][JT];
+    // Sign bits.  Lanes i and i+32 hold complementary halves of each word of token i;
+    // OR them, then lane group g stores words g*JT/2 .. of token i.
+    uint32_t words[JT];
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
+    for (int j = 0; j < JT; ++j) {
+      uint32_t w = 0;
 #pragma unroll
-      for (int j = 0; j < JT; ++j) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float y = yacc[n][j][r];
-          if constexpr (MLP) y += bias[L::NB1 + 32 * j + acc_row(r, lg)];
-          w |= (y > 0.f ? 1u : 0u) << acc_row(r, lg);
-        }
-        words[n][j] = w | __shfl_xor(w, 32);
+      for (int r = 0; r < 16; ++r) {
+        float y = yacc[j][r];
+        if constexpr (BIAS) y += bias[L::NB1 + 32 * j + acc_row(r, lg)];
+        w |= (y > 0.f ? 1u : 0u) << acc_row(r, lg);
       }
+      words[j] = w | __shfl_xor(w, 32);
     }
-    const int64_t dst_row = lg ? mem[1] : mem[0];
-    if (dst_row >= 0) {
-      uint32_t *dst = codes + (size_t)dst_row * W;
-      if constexpr (W == 4) {
-        *reinterpret_cast<u32x4 *>(dst) = lg ? u32x4{words[1][0], words[1][1], words[1][2], words[1][3]}
-                                             : u32x4{words[0][0], words[0][1], words[0][2], words[0][3]};
-      } else {
-        *reinterpret_cast<u32x2 *>(dst) = lg ? u32x2{words[1][0], words[1][1]} : u32x2{words[0][0], words[0][1]};
-      }
+    if (ok) {
+      uint32_t *dst = codes + (size_t)mem * W + (W / 2) * lg;
+      if constexpr (W == 4)
+        *reinterpret_cast<u32x2 *>(dst) = lg ? u32x2{words[2], words[3]} : u32x2{words[0], words[1]};
+      else
+        *dst = lg ? words[1] : words[0];
     }
   }
 }
 
-template <bool MLP, int BITS>
+template <bool MLP, int BITS, bool BIAS>
 hipError_t mfma_launch(const HashPtrs &hp, const void *k, int64_t nt, int64_t cap, int64_t t0,
                        int64_t total, uint32_t *codes, hipStream_t st) {
-  const int64_t n_tiles = (total + 63) / 64;
-  // One workgroup per CU when the weights fill LDS; more when they are small.
-  const int64_t per_cu = MLP ? 1 : 4;
-  int64_t grid = (n_tiles + kEncWaves - 1) / kEncWaves;
-  if (grid > 256 * per_cu) grid = 256 * per_cu;
-  hipLaunchKernelGGL((encode_keys_mfma_kernel<MLP, BITS>), dim3((unsigned)grid),
-                     dim3(kEncWaves * 64), 0, st, hp, static_cast<const uint16_t *>(k), nt, cap,
+  using L = EncLayout<MLP, BITS>;
+  const int64_t n_tiles = (total + 31) / 32;
+  int64_t grid = (n_tiles + L::WAVES - 1) / L::WAVES;
+  if (grid > 256 * L::PER_CU) grid = 256 * L::PER_CU;
+  hipLaunchKernelGGL((encode_keys_mfma_kernel<MLP, BITS, BIAS>), dim3((unsigned)grid),
+                     dim3(L::WAVES * 64), 0, st, hp, static_cast<const uint16_t *>(k), nt, cap,
                      t0, total, n_tiles, codes);
   return hipGetLastError();
 }
@@ -644,10 +642,15 @@ hipError_t launch_encode_keys(const hk_hash &h, const void *k, int B, int Hkv, i
   if (h.dtype == HK_F32) return valu_dispatch<false>(h, k, total, nt, cap, t0, codes, st);
   const HashPtrs hp{h.R, h.W1, h.b1, h.W2, h.b2};
   const bool mlp = h.kind == HK_HASH_MLP;
-  if (mlp && h.bits == 128) return mfma_launch<true, 128>(hp, k, nt, cap, t0, total, codes, st);
-  if (mlp) return mfma_launch<true, 64>(hp, k, nt, cap, t0, total, codes, st);
-  if (h.bits == 128) return mfma_launch<false, 128>(hp, k, nt, cap, t0, total, codes, st);
-  return mfma_launch<false, 64>(hp, k, nt, cap, t0, total, codes, st);
+  const bool bias = h.b1 != nullptr || h.b2 != nullptr;
+  if (mlp && h.bits == 128)
+    return bias ? mfma_launch<true, 128, true>(hp, k, nt, cap, t0, total, codes, st)
+                : mfma_launch<true, 128, false>(hp, k, nt, cap, t0, total, codes, st);
+  if (mlp)
+    return bias ? mfma_launch<true, 64, true>(hp, k, nt, cap, t0, total, codes, st)
+                : mfma_launch<true, 64, false>(hp, k, nt, cap, t0, total, codes, st);
+  if (h.bits == 128) return mfma_launch<false, 128, false>(hp, k, nt, cap, t0, total, codes, st);
+  return mfma_launch<false, 64, false>(hp, k, nt, cap, t0, total, codes, st);
 }
 
 hipError_t launch_encode_query(const hk_hash &h, const void *q, int B, int Hq, int Hkv,

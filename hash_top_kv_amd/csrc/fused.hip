@@ -97,11 +97,7 @@ __device__ __forceinline__ void emit_attend_body(
       // index list afterwards, in coalesced stores.
       const int4 m0 = smt[0];
       const int first = m0.x + min(m0.y, quota);
-      emit_chunks<LPT, kMaxCpb>([&](int i, int kk) { return sw[i][kk][t]; },
-                                [&](int i) { return smt[i]; }, nch, T, quota,
-                                lo + (int64_t)c0 * CH,
-                                [&](int pos, int32_t tok) { sel[pos - first] = tok; });
-      __syncthreads();
+      emit_chunks_lanes<LPT, kMaxCpb>(sw, smt, nch, T, quota, lo + (int64_t)c0 * CH, first, sel);
       for (int r = t; r < total; r += kScanThreads) out[first + r] = sel[r];
       attend_list(total);
     } else if (total > kListMax) {

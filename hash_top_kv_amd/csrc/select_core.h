@@ -132,4 +132,109 @@ __device__ __forceinline__ void emit_chunks(Word word, Meta meta, int nch, int T
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront: shifts within rows of 16 lanes,
+// then the row totals broadcast to the following rows (DPP row_shr, row_bcast:15/31).
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+// Writes the selected tokens of nch consecutive chunks (nch uniform, at most MAXC) into
+// list[position - first], where first is the head-list position of the first chunk's
+// first selected token.  The chunks' distance stashes are in LDS (sw[chunk][word][thread]
+// as written by the scan), their counts in smt[chunk]; chunk i starts at token
+// tok0 + i*CH.  Called by all threads of the workgroup; ends with the list complete.
+//
+// Thread t takes the LPT consecutive tokens LPT*t .. LPT*t + LPT-1 of every chunk, so
+// tokens ascend with (chunk, thread, bit).  It reads their distances from the stash
+// (they were stashed by LPT different scan threads), and keeps two bit masks per chunk:
+// tokens below the threshold and tokens at it.  One block-wide exclusive scan of the
+// packed per-thread counts (below | at << 16) gives every thread the number of tokens
+// below / at the threshold before its own in the head; a token below the threshold goes
+// to position (below before) + min(at before, quota), a tie with (at before) < quota to
+// (below before) + (at before).  Each thread then visits only its set mask bits.
+template <int LPT, int MAXC>
+__device__ __forceinline__ void emit_chunks_lanes(const uint32_t (*sw)[LPT / 4][kScanThreads],
+                                                  const int4 *smt, int nch, int T, int quota,
+                                                  int64_t tok0, int first, int32_t *list) {
+  constexpr int NW = kScanThreads / 64;
+  constexpr int CH = kScanThreads * LPT;
+  constexpr int TPR = 64 / LPT;                // threads per 64-token row of a wavefront
+  __shared__ uint32_t wtot[NW][MAXC];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  // Scan thread of this thread's first token, and the item (byte) that holds it.
+  const int s0 = (t & ~63) + LPT * (t % TPR);
+  const int item = (t / TPR) % LPT;
+  const int sh = 8 * (item & 3);
+  // All MAXC chunks of sw are read (unused ones hold a copy of a used chunk) so that the
+  // reads issue together; the masks of unused chunks are cleared.
+  uint4 wr[MAXC][LPT / 4];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i)
+#pragma unroll
+    for (int q4 = 0; q4 < LPT / 4; ++q4)
+      wr[i][q4] = *reinterpret_cast<const uint4 *>(&sw[i][item >> 2][s0 + 4 * q4]);
+  uint32_t masks[MAXC], cnt[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    uint32_t mlt = 0, meq = 0;
+#pragma unroll
+    for (int q4 = 0; q4 < LPT / 4; ++q4) {
+      const uint32_t wv[4] = {wr[i][q4].x, wr[i][q4].y, wr[i][q4].z, wr[i][q4].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = (int)((wv[e] >> sh) & 0xFFu);
+        mlt |= (d < T ? 1u : 0u) << (4 * q4 + e);
+        meq |= (d == T ? 1u : 0u) << (4 * q4 + e);
+      }
+    }
+    const uint32_t live = i < nch ? 0xFFFFFFFFu : 0u;
+    mlt &= live;
+    meq &= live;
+    masks[i] = mlt | (meq << 16);
+    cnt[i] = (uint32_t)__popc(mlt) | ((uint32_t)__popc(meq) << 16);
+  }
+  // Block-wide exclusive scan of the packed counts (each half stays below 2^16).
+  uint32_t inc[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) inc[i] = wave_incl_scan_dpp(cnt[i]);
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) wtot[wave][i] = inc[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    if (i >= nch) break;
+    uint32_t before = inc[i] - cnt[i];
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (w < wave) before += wtot[w][i];
+    const int4 mt = smt[i];
+    const int lt0 = mt.x + (int)(before & 0xFFFFu);
+    const int eq0 = mt.y + (int)(before >> 16);
+    const uint32_t mlt = masks[i] & 0xFFFFu, meq = masks[i] >> 16;
+    uint32_t all = mlt | meq;
+    const int32_t tokb = (int32_t)(tok0 + (int64_t)i * CH) + LPT * t;
+    while (all) {
+      const int j = __builtin_ctz(all);
+      all &= all - 1;
+      const uint32_t below = (1u << j) - 1u;
+      const int ltb = lt0 + __popc(mlt & below);
+      const int eqb = eq0 + __popc(meq & below);
+      int pos = -1;
+      if ((mlt >> j) & 1u) pos = ltb + min(eqb, quota);
+      else if (eqb < quota) pos = ltb + eqb;
+      if (pos >= 0) list[pos - first] = tokb + j;
+    }
+  }
+  __syncthreads();
+}
+
 }  // namespace hk

@@ -254,7 +254,7 @@ def test_lse_merge_matches_oracle(P, d):
 
 
 # ----------------------------------------------------------------- encoders
-def _hash_case(kind, bits, dtype, seed, identity=False):
+def _hash_case(kind, bits, dtype, seed, identity=False, bias=False):
     rng = np.random.default_rng(seed)
     d = 128
     if kind == "lsh":
@@ -276,27 +276,33 @@ def _hash_case(kind, bits, dtype, seed, identity=False):
             W2 = (rng.standard_normal((bits, 256)) / 16).astype(np.float32)
         cv = (lambda a: a) if dtype == "f32" else synth.to_bf16_bits
         h = {"kind": "mlp", "bits": bits, "dtype": dtype, "W1": cv(W1), "W2": cv(W2)}
+        if bias:
+            h["b1"] = cv((rng.standard_normal(256) * 0.3).astype(np.float32))
+            h["b2"] = cv((rng.standard_normal(bits) * 0.1).astype(np.float32))
     return h
 
 
+# (kind, bits, dtype, identity weights, biases)
 ENC_CASES = [
-    ("lsh", 128, "f32", False), ("lsh", 64, "f32", False), ("mlp", 128, "f32", False),
-    ("lsh", 128, "bf16", True), ("lsh", 64, "bf16", True), ("mlp", 128, "bf16", True),
-    ("mlp", 64, "bf16", True),
-    ("lsh", 128, "bf16", False), ("lsh", 64, "bf16", False), ("mlp", 128, "bf16", False),
-    ("mlp", 64, "bf16", False),
+    ("lsh", 128, "f32", False, False), ("lsh", 64, "f32", False, False),
+    ("mlp", 128, "f32", False, False), ("mlp", 128, "f32", False, True),
+    ("lsh", 128, "bf16", True, False), ("lsh", 64, "bf16", True, False),
+    ("mlp", 128, "bf16", True, False), ("mlp", 64, "bf16", True, False),
+    ("lsh", 128, "bf16", False, False), ("lsh", 64, "bf16", False, False),
+    ("mlp", 128, "bf16", False, False), ("mlp", 64, "bf16", False, False),
+    ("mlp", 128, "bf16", False, True), ("mlp", 64, "bf16", False, True),
 ]
 
 
 @pytest.mark.parametrize("case", ENC_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_encode_keys_matches_oracle(case):
-    kind, bits, dtype, identity = case
+    kind, bits, dtype, identity, bias = case
     say(f"encode_keys {case}")
     B, Hkv, cap = 2, 3, 1111
     t0, t1 = 5, 1071                                         # ragged range inside the cache
     wl = synth.scaled(synth.WORKLOADS[1], B=B, Hkv=Hkv, Hq=Hkv, N=cap, dtype=dtype)
     kv = synth.make_kv(wl, "k")
-    hnp = _hash_case(kind, bits, dtype, 5, identity)
+    hnp = _hash_case(kind, bits, dtype, 5, identity, bias)
     h = hk.Hash(kind, bits, **synth.hash_to_device(hnp))
     K = synth.to_device(kv["K"], dtype)
     sentinel = 0x5A5A5A5A
@@ -317,15 +323,17 @@ def test_encode_keys_matches_oracle(case):
     say(f"  exempt bits that differ: {flips}")
 
 
-@pytest.mark.parametrize("case", [("lsh", 128, "f32"), ("mlp", 128, "bf16"), ("lsh", 64, "bf16"),
-                                  ("mlp", 64, "f32")], ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("case", [("lsh", 128, "f32", False), ("mlp", 128, "bf16", False),
+                                  ("lsh", 64, "bf16", False), ("mlp", 64, "f32", False),
+                                  ("mlp", 128, "bf16", True), ("mlp", 64, "f32", True)],
+                         ids=lambda c: "-".join(map(str, c)))
 @pytest.mark.parametrize("G", [1, 4, 7])
 def test_encode_query_matches_oracle(case, G):
-    kind, bits, dtype = case
+    kind, bits, dtype, bias = case
     Hkv, B = 4, 3
     wl = synth.scaled(synth.WORKLOADS[1], B=B, Hkv=Hkv, Hq=Hkv * G, dtype=dtype)
     q = synth.make_q(wl)
-    hnp = _hash_case(kind, bits, dtype, 6)
+    hnp = _hash_case(kind, bits, dtype, 6, bias=bias)
     h = hk.Hash(kind, bits, **synth.hash_to_device(hnp))
     qc = hk.encode_query(h, synth.to_device(q, dtype), Hkv)
     torch.cuda.synchronize()
