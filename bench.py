@@ -1,7 +1,7 @@
 """Benchmark of the binary-hash KV retrieval decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--hash i]
-                    [--replicas R] [--no-cpu] [--prefill] [--unfused]
+                    [--replicas R] [--no-cpu] [--prefill] [--evict] [--unfused]
 
 Default workload: retrieval at 512K tokens -- 8 KV heads x 524,288 cached 128-bit codes
 (uniform random bits plus 1% planted near neighbours of the query code), top-1024 per
@@ -43,7 +43,7 @@ KERNEL_SOURCES = ["include/hk.h", "hash_top_kv_amd/csrc/hk_internal.h",
                   "hash_top_kv_amd/csrc/select_core.h", "hash_top_kv_amd/csrc/attend_core.h",
                   "hash_top_kv_amd/csrc/retrieve.hip", "hash_top_kv_amd/csrc/attend.hip",
                   "hash_top_kv_amd/csrc/fused.hip", "hash_top_kv_amd/csrc/encode.hip",
-                  "hash_top_kv_amd/csrc/api.hip"]
+                  "hash_top_kv_amd/csrc/evict.hip", "hash_top_kv_amd/csrc/api.hip"]
 
 
 def source_digest(files=KERNEL_SOURCES) -> str:
@@ -228,7 +228,8 @@ def build_full_case(args, torch, hk, synth):
     else:
         parts = [("encode_query", enc, None), ("hamming_scan", scan, scan_bytes),
                  ("select+attend", rest, gather_bytes)]
-    return parts, check, info, {"wl": wl, "K": K, "h": h, "codes": codes, "spec": spec}
+    return parts, check, info, {"wl": wl, "K": K, "V": V, "h": h, "codes": codes, "spec": spec,
+                                "code_sets": code_sets, "Qs": Qs}
 
 
 def time_prefill(torch, hk, ctx, steps):
@@ -249,6 +250,61 @@ def time_prefill(torch, hk, ctx, steps):
     return {"kernel": f"encode_keys_mfma ({spec.kind}-{spec.bits})", "rows": M, "us": ms * 1e3,
             "tflops": flops / ms / 1e9, "mfma_frac": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
             "hbm_gbs": bytes_ / ms / 1e6}
+
+
+def time_evict(torch, hk, synth, ctx, steps):
+    """HashEvict's eviction step on the same cache (it runs after the decode-step timing:
+    every step overwrites one slot per head).  Parts: the query hash + hk_evict_select
+    (victim per head), the new key's hash + hk_evict_replace, and attention over every
+    cached token; hk_evict_select alone, back to back over the code copies, for its HBM
+    rate (b/8 bytes per candidate)."""
+    from hash_top_kv_amd.step import EvictStep
+    wl, K, V, h, spec = ctx["wl"], ctx["K"], ctx["V"], ctx["h"], ctx["spec"]
+    sets, Qs = ctx["code_sets"], ctx["Qs"]
+    es = [EvictStep(K, V, cs, spec.bits, wl.N, wl.n_sink, wl.n_local, wl.Hq, h) for cs in sets]
+    new = synth.make_kv(synth.scaled(wl, N=1, wid=90))
+    k_new = synth.to_device(np.ascontiguousarray(new["K"][:, :, 0]), wl.dtype)
+    v_new = synth.to_device(np.ascontiguousarray(new["V"][:, :, 0]), wl.dtype)
+    # check: every head has a victim among its candidates (parity is the tests' job)
+    es[0].select(Qs[0])
+    torch.cuda.synchronize()
+    vic = es[0].victim.cpu().numpy()
+    assert ((vic >= wl.n_sink) & (vic < wl.N - wl.n_local)).all()
+    C = wl.N - wl.n_sink - wl.n_local
+    scan_bytes = wl.B * wl.Hkv * C * spec.bits // 8
+    esz = 4 if wl.dtype == "f32" else 2
+    attend_bytes = wl.B * wl.Hkv * wl.N * 2 * 128 * esz
+    R = len(Qs)
+
+    def timed(fn, n):
+        for i in range(4):
+            fn(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    def sel_only(i):
+        e = es[i % len(es)]
+        hk.evict_select(e.codes, e.qcodes, spec.bits, wl.N, wl.n_sink, wl.n_local, e.victim, e.ws_e)
+
+    us_sel = timed(sel_only, max(steps, 50))
+    us_select = timed(lambda i: es[i % len(es)].select(Qs[i % R]), steps)
+    us_replace = timed(lambda i: es[i % len(es)].replace(k_new, v_new), steps)
+    us_attend = timed(lambda i: es[0].attend(Qs[i % R]), min(steps, 20))
+    return {"step": "hk_encode_query + hk_evict_select, hk_encode_query + hk_evict_replace, "
+                    "hk_sparse_decode over all tokens",
+            "hash": f"{spec.kind}-{spec.bits}",
+            "us_query_hash_and_select": round(us_select, 3),
+            "us_key_hash_and_replace": round(us_replace, 3),
+            "us_attend_all_tokens": round(us_attend, 3),
+            "attend_gbs": round(attend_bytes / us_attend / 1e3, 1),
+            "evict_select": {"us_per_launch": round(us_sel, 3), "alg_bytes": scan_bytes,
+                             "gbs": round(scan_bytes / us_sel / 1e3, 1),
+                             "frac_of_peak": round(scan_bytes / us_sel / 1e3 / HBM_PEAK_GBS, 4)}}
 
 
 def cpu_baseline(args, ctx, synth):
@@ -292,6 +348,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prefill", action="store_true", help="also time the key encode of the whole cache")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--evict", action="store_true",
+                    help="also time HashEvict's eviction step on the same cache (last)")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step through the separate calls instead of the fused one")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
@@ -399,6 +457,8 @@ def main():
            "wall_ms_timed_region": round(wall_ms, 3)}
     if args.prefill and args.workload != 2:
         out["prefill"] = time_prefill(torch, hk, ctx, 10)
+    if args.evict and args.workload != 2:
+        out["evict"] = time_evict(torch, hk, synth, ctx, min(args.steps, 200))
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args, ctx, synth)
     print(json.dumps(out), flush=True)

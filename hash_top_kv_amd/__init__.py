@@ -50,6 +50,9 @@ _SIGNATURES = {
                               _P, _P, _P, _SZ, _P]),
     "hk_lse_merge": (_I, [_P, _P, _I, _I64, _I, _P, _P, _P]),
     "hk_retrieve_attend_workspace": (_SZ, [_I, _I, _I, _I, _I64, _I, _I, _I]),
+    "hk_evict_workspace": (_SZ, [_I, _I, _I, _I64, _I, _I]),
+    "hk_evict_select": (_I, [_P, _P, _I, _I, _I, _I64, _I64, _I, _I, _P, _P, _SZ, _P]),
+    "hk_evict_replace": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P]),
     "hk_select_attend": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I64, _I, _I, _I, _F,
                               _P, _P, _P, _P, _P, _SZ, _P]),
     "hk_retrieve_attend": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I64, _I, _I,
@@ -359,3 +362,43 @@ def select_attend(bits, q, k, v, n_ctx, n_sink, n_local, topk, idx, count, o, ls
                                   _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream()),
            "hk_select_attend")
     return o, lse
+
+
+def evict_workspace(bits, B, Hkv, n_ctx, n_sink, n_local) -> int:
+    return int(lib().hk_evict_workspace(bits, B, Hkv, n_ctx, n_sink, n_local))
+
+
+def evict_select(codes, qcodes, bits, n_ctx, n_sink, n_local, victim=None, ws=None):
+    """hk_evict_select: per head, the candidate farthest from the query code (HashEvict's
+    victim), lowest index on ties, -1 without candidates.  Returns victim [B, Hkv] int32."""
+    _need(codes, "codes", dtype=torch.int32)
+    B, Hkv, cap, W = codes.shape
+    _need(qcodes, "qcodes", dtype=torch.int32, shape=(B, Hkv, W))
+    if victim is None:
+        victim = torch.empty((B, Hkv), dtype=torch.int32, device=codes.device)
+    _need(victim, "victim", dtype=torch.int32, shape=(B, Hkv))
+    if ws is None:
+        ws = workspace(evict_workspace(bits, B, Hkv, n_ctx, n_sink, n_local), codes.device)
+    _need(ws, "ws", dtype=torch.uint8)
+    _check(lib().hk_evict_select(_ptr(codes), _ptr(qcodes), bits, B, Hkv, cap, n_ctx, n_sink,
+                                 n_local, _ptr(victim), _ptr(ws), ws.numel(), _stream()),
+           "hk_evict_select")
+    return victim
+
+
+def evict_replace(k_new, v_new, code_new, victim, k, v, codes):
+    """hk_evict_replace: the new token's key, value and key code take the victim's slot
+    of each head.  k_new, v_new [B, Hkv, 128]; code_new [B, Hkv, bits/32]; victim
+    [B, Hkv]; k, v [B, Hkv, cap, 128] and codes [B, Hkv, cap, bits/32] are updated."""
+    B, Hkv, cap, d = k.shape
+    W = codes.shape[-1]
+    _need(k, "k")
+    _need(v, "v", dtype=k.dtype, shape=k.shape)
+    _need(k_new, "k_new", dtype=k.dtype, shape=(B, Hkv, d))
+    _need(v_new, "v_new", dtype=k.dtype, shape=(B, Hkv, d))
+    _need(codes, "codes", dtype=torch.int32, shape=(B, Hkv, cap, W))
+    _need(code_new, "code_new", dtype=torch.int32, shape=(B, Hkv, W))
+    _need(victim, "victim", dtype=torch.int32, shape=(B, Hkv))
+    _check(lib().hk_evict_replace(_ptr(k_new), _ptr(v_new), _ptr(code_new), _dtype_code(k), 32 * W,
+                                  B, Hkv, d, cap, _ptr(victim), _ptr(k), _ptr(v), _ptr(codes),
+                                  _stream()), "hk_evict_replace")

@@ -239,4 +239,40 @@ hk_status hk_lse_merge(const float *o_parts, const float *lse_parts, int P, int6
   return from_hip(launch_lse_merge(o_parts, lse_parts, P, rows, d, o, lse, as_stream(stream)));
 }
 
+size_t hk_evict_workspace(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, int n_local) {
+  if (check_retrieve(bits, B, Hkv, n_ctx, n_ctx, n_sink, n_local, 0) != HK_OK) return 0;
+  return plan_evict(bits, B, Hkv, n_ctx, n_sink, n_local).total;
+}
+
+hk_status hk_evict_select(const uint32_t *codes, const uint32_t *qcodes, int bits, int B, int Hkv,
+                          int64_t cap, int64_t n_ctx, int n_sink, int n_local, int32_t *victim,
+                          void *ws, size_t ws_bytes, void *stream) {
+  hk_status s = check_retrieve(bits, B, Hkv, cap, n_ctx, n_sink, n_local, 0);
+  if (s != HK_OK) return s;
+  const EvictPlan p = plan_evict(bits, B, Hkv, n_ctx, n_sink, n_local);
+  if (p.BH == 0) return HK_OK;
+  if (!victim || !ws || (p.S > 0 && (!codes || !qcodes))) return HK_ERR_INVALID_ARGUMENT;
+  if (p.S > 0 && !aligned(codes, code_align(bits))) return HK_ERR_UNSUPPORTED;
+  if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(launch_evict_select(p, codes, qcodes, cap, victim, ws, as_stream(stream)));
+}
+
+hk_status hk_evict_replace(const void *k_new, const void *v_new, const uint32_t *code_new,
+                           int dtype, int bits, int B, int Hkv, int d, int64_t cap,
+                           const int32_t *victim, void *kc, void *vc, uint32_t *codes,
+                           void *stream) {
+  if (dtype != HK_F32 && dtype != HK_BF16) return HK_ERR_UNSUPPORTED;
+  if (bits != 64 && bits != 128) return HK_ERR_UNSUPPORTED;
+  if (d != kHeadDim) return HK_ERR_UNSUPPORTED;
+  if (B < 0 || Hkv < 0 || cap < 0) return HK_ERR_INVALID_ARGUMENT;
+  if ((int64_t)B * Hkv == 0) return HK_OK;
+  if ((int64_t)B * Hkv > 65535) return HK_ERR_UNSUPPORTED;
+  if (!k_new || !v_new || !code_new || !victim || !kc || !vc || !codes)
+    return HK_ERR_INVALID_ARGUMENT;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kc, 16) || !aligned(vc, 16))
+    return HK_ERR_UNSUPPORTED;
+  return from_hip(launch_evict_replace(k_new, v_new, code_new, dtype == HK_BF16 ? 2 : 4, bits / 32,
+                                       B * Hkv, cap, victim, kc, vc, codes, as_stream(stream)));
+}
+
 }  // extern "C"

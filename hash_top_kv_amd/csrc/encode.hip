@@ -34,8 +34,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // GELU(a) = a Phi(a) = max(a, 0) - |a| Phi(-|a|), with Phi(-|a|) = erfc(|a| / sqrt 2) / 2
 // from the rational approximation of erf in Abramowitz & Stegun 7.1.26 (Hastings):

@@ -15,6 +15,27 @@ constexpr int kMaxGroup = 8;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// One packed code of W words as a vector load, and its Hamming distance to a query code.
+template <int W> struct CodeVec;
+template <> struct CodeVec<4> {
+  using T = u32x4;
+  __device__ static T zero() { return T{0u, 0u, 0u, 0u}; }
+  __device__ static uint32_t dist(const T &v, const uint32_t *q) {
+    return __builtin_popcount(v.x ^ q[0]) + __builtin_popcount(v.y ^ q[1]) +
+           __builtin_popcount(v.z ^ q[2]) + __builtin_popcount(v.w ^ q[3]);
+  }
+};
+template <> struct CodeVec<2> {
+  using T = u32x2;
+  __device__ static T zero() { return T{0u, 0u}; }
+  __device__ static uint32_t dist(const T &v, const uint32_t *q) {
+    return __builtin_popcount(v.x ^ q[0]) + __builtin_popcount(v.y ^ q[1]);
+  }
+};
+
 // ---------------------------------------------------------------- retrieval plan
 // Candidate tokens of each (b, KV head) are cut into S chunks of `ch` tokens; one
 // workgroup scans one chunk.  The workspace holds
@@ -160,5 +181,21 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t *ld
   total = tot;
   return off + inc - v;
 }
+
+// ---------------------------------------------------------------- eviction
+// HashEvict's victim per head: the candidate [n_sink, n_ctx - n_local) with the largest
+// Hamming distance to the query code, ties to the lowest token.  The workspace holds
+// one 64-bit key (distance << 32 | ~token) per chunk of 2048 candidates.
+struct EvictPlan {
+  int W = 0, BH = 0, S = 0;
+  int64_t lo = 0, C = 0;
+  size_t total = 0;
+};
+EvictPlan plan_evict(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, int n_local);
+hipError_t launch_evict_select(const EvictPlan &p, const uint32_t *codes, const uint32_t *qcodes,
+                               int64_t cap, int32_t *victim, void *ws, hipStream_t st);
+hipError_t launch_evict_replace(const void *k_new, const void *v_new, const uint32_t *code_new,
+                                int elem_bytes, int W, int BH, int64_t cap, const int32_t *victim,
+                                void *kc, void *vc, uint32_t *codes, hipStream_t st);
 
 }  // namespace hk

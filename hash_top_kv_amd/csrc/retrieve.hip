@@ -22,27 +22,6 @@
 namespace hk {
 namespace {
 
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-template <int W> struct CodeVec;
-template <> struct CodeVec<4> {
-  using T = u32x4;
-  __device__ static T zero() { return T{0u, 0u, 0u, 0u}; }
-  __device__ static uint32_t dist(const T &v, const uint32_t *q) {
-    return __builtin_popcount(v.x ^ q[0]) + __builtin_popcount(v.y ^ q[1]) +
-           __builtin_popcount(v.z ^ q[2]) + __builtin_popcount(v.w ^ q[3]);
-  }
-};
-template <> struct CodeVec<2> {
-  using T = u32x2;
-  __device__ static T zero() { return T{0u, 0u}; }
-  __device__ static uint32_t dist(const T &v, const uint32_t *q) {
-    return __builtin_popcount(v.x ^ q[0]) + __builtin_popcount(v.y ^ q[1]);
-  }
-};
-
 // grid (S, BH); chunk c of head bh covers candidate offsets [c*CH, (c+1)*CH).  The
 // histogram of the chunk goes to hist[bh][c]: bins 0 .. 32W-1, then 4W "superbins", each
 // the count of 8 consecutive distances (the count at distance 32W follows from the

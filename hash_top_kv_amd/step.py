@@ -19,9 +19,10 @@ import math
 
 import torch
 
-from . import (Hash, encode_query, hamming_scan, lse_merge, retrieve_attend_workspace,
-               retrieve_topk_workspace, select_attend, sparse_decode, sparse_decode_workspace,
-               window_indices, workspace, _check, _ptr, _stream, lib)
+from . import (Hash, encode_query, evict_replace, evict_select, evict_workspace, hamming_scan,
+               lse_merge, retrieve_attend_workspace, retrieve_topk_workspace, select_attend,
+               sparse_decode, sparse_decode_workspace, window_indices, workspace, _check, _ptr,
+               _stream, lib)
 
 
 class DecodeStep:
@@ -93,3 +94,52 @@ class DecodeStep:
         sparse_decode(q, self.K, self.V, self.win, self.n_win, idx_stride=0, scale=self.scale,
                       o=self.o_parts[1], lse=self.lse_parts[1], ws=self.ws_d)
         return lse_merge(self.o_parts, self.lse_parts, self.o, self.lse)
+
+
+class EvictStep:
+    """One HashEvict decode step over a fixed-budget cache (HashEvict: Abstract):
+
+        hk_encode_query (the query)  -> hk_evict_select (victim per KV head)
+        hk_encode_query (the new key, G = 1) -> hk_evict_replace (into the victim's slot)
+        hk_sparse_decode over all n_ctx cached tokens
+
+    Buffers are allocated once; a head without candidates evicts nothing and does not
+    cache the current token."""
+
+    def __init__(self, K: torch.Tensor, V: torch.Tensor, codes: torch.Tensor, bits: int,
+                 n_ctx: int, n_sink: int, n_local: int, Hq: int, hash: Hash):
+        self.K, self.V, self.codes, self.bits, self.hash = K, V, codes, bits, hash
+        B, Hkv, cap, d = K.shape
+        self.B, self.Hkv, self.cap, self.d, self.Hq = B, Hkv, cap, d, Hq
+        self.n_ctx, self.n_sink, self.n_local = n_ctx, n_sink, n_local
+        dev = K.device
+        W = bits // 32
+        self.qcodes = torch.empty((B, Hkv, W), dtype=torch.int32, device=dev)
+        self.code_new = torch.empty((B, Hkv, W), dtype=torch.int32, device=dev)
+        self.victim = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+        self.ws_e = workspace(evict_workspace(bits, B, Hkv, n_ctx, n_sink, n_local), dev)
+        self.every = torch.arange(max(n_ctx, 1), dtype=torch.int32, device=dev)
+        self.ws_d = workspace(sparse_decode_workspace(B, Hq, Hkv, n_ctx, d), dev)
+        self.o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        self.scale = 1.0 / math.sqrt(d)
+
+    def select(self, q):
+        encode_query(self.hash, q, self.Hkv, self.qcodes)
+        return evict_select(self.codes, self.qcodes, self.bits, self.n_ctx, self.n_sink,
+                            self.n_local, self.victim, self.ws_e)
+
+    def replace(self, k_new, v_new):
+        encode_query(self.hash, k_new, self.Hkv, self.code_new)
+        evict_replace(k_new, v_new, self.code_new, self.victim, self.K, self.V, self.codes)
+
+    def attend(self, q):
+        return sparse_decode(q, self.K, self.V, self.every, self.n_ctx, idx_stride=0,
+                             scale=self.scale, o=self.o, lse=self.lse, ws=self.ws_d)
+
+    def __call__(self, q, k_new, v_new):
+        """Returns (o [B, Hq, d], lse [B, Hq], victim [B, Hkv])."""
+        self.select(q)
+        self.replace(k_new, v_new)
+        o, lse = self.attend(q)
+        return o, lse, self.victim

@@ -219,6 +219,38 @@ hk_status hk_sparse_decode(const void *q, const void *k, const void *v, int dtyp
 hk_status hk_lse_merge(const float *o_parts, const float *lse_parts, int P, int64_t rows,
                        int d, float *o, float *lse, void *stream);
 
+/* Workspace bytes needed by hk_evict_select (8 bytes per chunk of 2048 candidates). */
+size_t hk_evict_workspace(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, int n_local);
+
+/* HashEvict's victim of one decode step (HashEvict: Abstract): per (b, head), the
+ * candidate n_sink <= t < n_ctx - n_local whose key code is farthest from the query code
+ * in Hamming distance -- the token least similar to the current query, expected to get
+ * the lowest attention score -- with ties going to the lowest token index.
+ *   codes, qcodes, bits, cap, n_ctx, n_sink, n_local: as in hk_retrieve_topk.
+ *   victim  device int32 [B][Hkv] (written): the victim's token index, or -1 when the
+ *           head has no candidate.
+ *   ws      device workspace of hk_evict_workspace(...) bytes, 256-byte aligned.
+ * Errors: as hk_retrieve_topk. */
+hk_status hk_evict_select(const uint32_t *codes, const uint32_t *qcodes, int bits, int B, int Hkv,
+                          int64_t cap, int64_t n_ctx, int n_sink, int n_local, int32_t *victim,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* The current token takes the victim's slot (HashEvict: Abstract): for every (b, head)
+ * with 0 <= victim < cap, K[b][head][victim] = k_new[b][head], V[...] = v_new[b][head]
+ * and codes[b][head][victim] = code_new[b][head]; heads with any other victim are left
+ * unchanged.  code_new is the new key's code, e.g. from hk_encode_query with Hq = Hkv
+ * (G = 1, the code of the key itself).
+ *   k_new, v_new  device [B][Hkv][d], element type dtype.
+ *   code_new      device uint32 [B][Hkv][bits/32].
+ *   victim        device int32 [B][Hkv], e.g. from hk_evict_select.
+ *   kc, vc        device [B][Hkv][cap][d]; codes device uint32 [B][Hkv][cap][bits/32].
+ * Errors: d != 128, bits not 64/128 -> UNSUPPORTED; negative sizes, NULL pointers ->
+ * INVALID_ARGUMENT. */
+hk_status hk_evict_replace(const void *k_new, const void *v_new, const uint32_t *code_new,
+                           int dtype, int bits, int B, int Hkv, int d, int64_t cap,
+                           const int32_t *victim, void *kc, void *vc, uint32_t *codes,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

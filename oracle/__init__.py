@@ -39,7 +39,7 @@ __all__ = [
     "widen", "round_bf16", "gelu", "prepare_hash", "project", "pack_bits", "unpack_bits",
     "encode", "group_mean_query", "encode_query", "candidate_range", "window_indices",
     "hamming", "select_topk", "attend", "sparse_attention", "lse_merge", "decode_step",
-    "near_zero_mask", "evict_victim", "exact_topk",
+    "near_zero_mask", "evict_victim", "evict_step", "exact_topk",
 ]
 
 NEAR_ZERO = 1e-3   # |pre-sign value| below which a code bit may legitimately differ
@@ -345,6 +345,34 @@ def evict_victim(codes, qcode, n_ctx: int, n_sink: int, n_local: int) -> int:
         return -1
     dist = hamming(np.asarray(codes)[cand], qcode)
     return int(cand[int(np.argmax(dist))])        # argmax returns the first maximum
+
+
+def evict_step(q, K, V, key_codes, qcodes, k_new, v_new, code_new, n_ctx: int,
+               n_sink: int, n_local: int, scale: float | None = None):
+    """One HashEvict decode step of one batch (HashEvict: Abstract): per KV head, the
+    victim (evict_victim) has its key, value and key code replaced by the current
+    token's, then every query head attends over all n_ctx cached tokens.  A head with no
+    candidate evicts nothing and does not cache the current token.
+
+    q [Hq, d]; K, V [Hkv, >= n_ctx, d] float64; key_codes [Hkv, >= n_ctx, W]; qcodes
+    [Hkv, W]; k_new, v_new [Hkv, d]; code_new [Hkv, W].  The inputs are not modified.
+    Returns dict(victim [Hkv], K, V, codes (updated copies), o [Hq, d], lse [Hq]).
+    """
+    Hq, d = q.shape
+    Hkv = K.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    K, V = np.array(K, dtype=np.float64), np.array(V, dtype=np.float64)
+    codes = np.array(key_codes, dtype=np.uint32)
+    victim = np.full(Hkv, -1, dtype=np.int64)
+    for h in range(Hkv):
+        j = evict_victim(codes[h], qcodes[h], n_ctx, n_sink, n_local)
+        victim[h] = j
+        if j >= 0:
+            K[h, j], V[h, j], codes[h, j] = k_new[h], v_new[h], code_new[h]
+    every = np.arange(n_ctx, dtype=np.int64)
+    o, lse = sparse_attention(q, K, V, [every] * Hkv, scale)
+    return {"victim": victim, "K": K, "V": V, "codes": codes, "o": o, "lse": lse}
 
 
 def exact_topk(q, k_rows, k: int, first: int = 0) -> np.ndarray:

@@ -102,6 +102,23 @@ def test_host_validation_without_gpu(hk):
         == hk.HK_ERR_UNSUPPORTED
     assert L.hk_sparse_decode(dummy, odd, dummy, hk.HK_BF16, 1, 8, 4, 128, 10, dummy, 4, P, 4, f,
                               dummy, dummy, dummy, 1 << 30, P) == hk.HK_ERR_UNSUPPORTED
+    # eviction: bad width / sizes, missing buffers, small workspace, misaligned rows
+    assert L.hk_evict_select(P, P, 96, 1, 1, 10, 10, 0, 0, P, P, 0, P) == hk.HK_ERR_UNSUPPORTED
+    assert L.hk_evict_select(P, P, 128, 1, 1, 10, 11, 0, 0, P, P, 0, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_evict_select(P, P, 128, 1, 1, 10, 10, 0, 0, P, P, 0, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_evict_select(dummy, dummy, 128, 1, 1, 5000, 5000, 0, 0, dummy, dummy, 1, P) \
+        == hk.HK_ERR_WORKSPACE_TOO_SMALL
+    assert L.hk_evict_select(odd, dummy, 128, 1, 1, 5000, 5000, 0, 0, dummy, dummy, 1 << 20, P) \
+        == hk.HK_ERR_UNSUPPORTED
+    assert L.hk_evict_select(P, P, 128, 0, 4, 10, 10, 0, 0, P, P, 0, P) == hk.HK_OK
+    assert L.hk_evict_workspace(64, 4, 4, 262144, 4, 64) == 16 * 128 * 8
+    assert L.hk_evict_replace(dummy, dummy, dummy, hk.HK_BF16, 128, 1, 1, 64, 10, dummy, dummy,
+                              dummy, dummy, P) == hk.HK_ERR_UNSUPPORTED
+    assert L.hk_evict_replace(dummy, dummy, P, hk.HK_BF16, 128, 1, 1, 128, 10, dummy, dummy,
+                              dummy, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_evict_replace(odd, dummy, dummy, hk.HK_BF16, 128, 1, 1, 128, 10, dummy, dummy,
+                              dummy, dummy, P) == hk.HK_ERR_UNSUPPORTED
+    assert L.hk_evict_replace(P, P, P, hk.HK_BF16, 128, 0, 1, 128, 10, P, P, P, P, P) == hk.HK_OK
     n = ctypes.c_int32(-1)
     assert L.hk_window_indices(100, 4, 64, P, ctypes.byref(n), P) == hk.HK_OK and n.value == 68
     assert L.hk_window_indices(-1, 4, 64, P, ctypes.byref(n), P) == hk.HK_ERR_INVALID_ARGUMENT

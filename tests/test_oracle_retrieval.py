@@ -184,3 +184,43 @@ def test_evict_victim_brute_force():
             dist = {j: bin(_as_int(codes[j]) ^ _as_int(q)).count("1") for j in cand}
             want = sorted(cand, key=lambda j: (-dist[j], j))[0]
         assert oracle.evict_victim(codes, q, n, s, w) == want
+
+
+def test_evict_step_is_slot_replacement_then_full_softmax():
+    """The eviction step against a separate construction: the victim chosen by brute
+    force over (distance desc, index asc), the cache rebuilt as Python lists with the
+    victim's entries replaced, and attention from scipy's softmax / logsumexp over every
+    cached token."""
+    from scipy.special import logsumexp, softmax
+    rng = np.random.default_rng(31)
+    for n, s, w, Hkv, G in [(40, 2, 5, 2, 3), (9, 4, 5, 1, 2), (30, 0, 0, 3, 1)]:
+        d, W = 8, 2
+        K = rng.standard_normal((Hkv, n, d))
+        V = rng.standard_normal((Hkv, n, d))
+        codes = rng.integers(0, 4, size=(Hkv, n, W)).astype(np.uint32)   # many ties
+        qcodes = rng.integers(0, 4, size=(Hkv, W)).astype(np.uint32)
+        q = rng.standard_normal((Hkv * G, d))
+        k_new, v_new = rng.standard_normal((Hkv, d)), rng.standard_normal((Hkv, d))
+        code_new = rng.integers(0, 2 ** 32, size=(Hkv, W), dtype=np.uint32)
+        K0, codes0 = K.copy(), codes.copy()
+        got = oracle.evict_step(q, K, V, codes, qcodes, k_new, v_new, code_new, n, s, w, 0.5)
+        assert np.array_equal(K, K0) and np.array_equal(codes, codes0)   # inputs untouched
+        for h in range(Hkv):
+            cand = [j for j in range(n) if s <= j < n - w]
+            want = -1
+            if cand:
+                dist = {j: sum(bin(int(codes[h, j, x]) ^ int(qcodes[h, x])).count("1")
+                               for x in range(W)) for j in cand}
+                want = sorted(cand, key=lambda j: (-dist[j], j))[0]
+            assert got["victim"][h] == want
+            krows, vrows, crows = list(K[h]), list(V[h]), list(codes[h])
+            if want >= 0:
+                krows[want], vrows[want], crows[want] = k_new[h], v_new[h], code_new[h]
+            assert np.array_equal(got["K"][h], np.array(krows))
+            assert np.array_equal(got["V"][h], np.array(vrows))
+            assert np.array_equal(got["codes"][h], np.array(crows))
+            for g in range(G):
+                logits = 0.5 * (np.array(krows) @ q[h * G + g])
+                assert np.allclose(got["o"][h * G + g], softmax(logits) @ np.array(vrows),
+                                   atol=1e-12, rtol=0)
+                assert abs(got["lse"][h * G + g] - logsumexp(logits)) < 1e-12
