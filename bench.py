@@ -1,7 +1,8 @@
 """Benchmark of the binary-hash KV retrieval decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--hash i]
-                    [--replicas R] [--no-cpu] [--prefill] [--evict] [--unfused]
+                    [--replicas R] [--no-cpu] [--prefill] [--exact] [--evict]
+                    [--unfused]
 
 Default workload: retrieval at 512K tokens -- 8 KV heads x 524,288 cached 128-bit codes
 (uniform random bits plus 1% planted near neighbours of the query code), top-1024 per
@@ -43,7 +44,8 @@ KERNEL_SOURCES = ["include/hk.h", "hash_top_kv_amd/csrc/hk_internal.h",
                   "hash_top_kv_amd/csrc/select_core.h", "hash_top_kv_amd/csrc/attend_core.h",
                   "hash_top_kv_amd/csrc/retrieve.hip", "hash_top_kv_amd/csrc/attend.hip",
                   "hash_top_kv_amd/csrc/fused.hip", "hash_top_kv_amd/csrc/encode.hip",
-                  "hash_top_kv_amd/csrc/evict.hip", "hash_top_kv_amd/csrc/api.hip"]
+                  "hash_top_kv_amd/csrc/evict.hip", "hash_top_kv_amd/csrc/exact.hip",
+                  "hash_top_kv_amd/csrc/api.hip"]
 
 
 def source_digest(files=KERNEL_SOURCES) -> str:
@@ -229,7 +231,7 @@ def build_full_case(args, torch, hk, synth):
         parts = [("encode_query", enc, None), ("hamming_scan", scan, scan_bytes),
                  ("select+attend", rest, gather_bytes)]
     return parts, check, info, {"wl": wl, "K": K, "V": V, "h": h, "codes": codes, "spec": spec,
-                                "code_sets": code_sets, "Qs": Qs}
+                                "code_sets": code_sets, "Qs": Qs, "steps": steps}
 
 
 def time_prefill(torch, hk, ctx, steps):
@@ -307,6 +309,39 @@ def time_evict(torch, hk, synth, ctx, steps):
                              "frac_of_peak": round(scan_bytes / us_sel / 1e3 / HBM_PEAK_GBS, 4)}}
 
 
+def time_exact(torch, hk, ctx, steps):
+    """Exact top-k by logit (the "oracle top-k") on the same cache and query: its time and
+    HBM rate (every candidate's K row read once), and the retrieval IoU of the hash top-k
+    against it, per (batch, KV head)."""
+    wl, K = ctx["wl"], ctx["K"]
+    st, Q = ctx["steps"][0], ctx["Qs"][0]
+    st(Q)
+    idx_e, cnt_e = hk.exact_topk(Q, K, wl.N, wl.n_sink, wl.n_local, wl.k)
+    ws = hk.workspace(hk.exact_topk_workspace(wl.B, wl.Hkv, wl.N, wl.n_sink, wl.n_local, wl.k))
+    inter = hk.topk_intersect(st.idx, st.count, idx_e, cnt_e)
+    torch.cuda.synchronize()
+    i, a, b = (x.cpu().numpy().reshape(-1).astype(np.float64) for x in (inter, st.count, cnt_e))
+    union = a + b - i
+    iou = np.where(union > 0, i / np.maximum(union, 1), 1.0)
+    n = max(5, min(steps, 50))
+    for _ in range(3):
+        hk.exact_topk(Q, K, wl.N, wl.n_sink, wl.n_local, wl.k, idx_e, cnt_e, ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        hk.exact_topk(Q, K, wl.N, wl.n_sink, wl.n_local, wl.k, idx_e, cnt_e, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    esz = 4 if wl.dtype == "f32" else 2
+    nbytes = wl.B * wl.Hkv * (wl.N - wl.n_sink - wl.n_local) * 128 * esz
+    return {"call": "hk_exact_topk", "us": round(us, 3), "alg_bytes": nbytes,
+            "gbs": round(nbytes / us / 1e3, 1), "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+            "hash": ctx["spec"].kind + "-" + str(ctx["spec"].bits),
+            "iou_hash_vs_exact": {"mean": round(float(iou.mean()), 4), "min": round(float(iou.min()), 4),
+                                  "max": round(float(iou.max()), 4), "heads": int(iou.size)}}
+
+
 def cpu_baseline(args, ctx, synth):
     """The CPU oracle on a bounded sample: whole decode steps of the same workload."""
     import oracle
@@ -348,6 +383,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prefill", action="store_true", help="also time the key encode of the whole cache")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--exact", action="store_true",
+                    help="also time the exact top-k by logit and report the hash top-k's IoU with it")
     ap.add_argument("--evict", action="store_true",
                     help="also time HashEvict's eviction step on the same cache (last)")
     ap.add_argument("--unfused", action="store_true",
@@ -457,6 +494,8 @@ def main():
            "wall_ms_timed_region": round(wall_ms, 3)}
     if args.prefill and args.workload != 2:
         out["prefill"] = time_prefill(torch, hk, ctx, 10)
+    if args.exact and args.workload != 2:
+        out["exact_topk"] = time_exact(torch, hk, ctx, args.steps)
     if args.evict and args.workload != 2:
         out["evict"] = time_evict(torch, hk, synth, ctx, min(args.steps, 200))
     if not args.no_cpu:

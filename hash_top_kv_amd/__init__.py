@@ -51,6 +51,9 @@ _SIGNATURES = {
     "hk_lse_merge": (_I, [_P, _P, _I, _I64, _I, _P, _P, _P]),
     "hk_retrieve_attend_workspace": (_SZ, [_I, _I, _I, _I, _I64, _I, _I, _I]),
     "hk_evict_workspace": (_SZ, [_I, _I, _I, _I64, _I, _I]),
+    "hk_exact_topk_workspace": (_SZ, [_I, _I, _I64, _I, _I, _I]),
+    "hk_exact_topk": (_I, [_P, _P, _I, _I, _I, _I, _I, _I64, _I64, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "hk_topk_intersect": (_I, [_P, _P, _I64, _P, _P, _I64, _I, _P, _P]),
     "hk_evict_select": (_I, [_P, _P, _I, _I, _I, _I64, _I64, _I, _I, _P, _P, _SZ, _P]),
     "hk_evict_replace": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _P, _P, _P, _P]),
     "hk_select_attend": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I64, _I, _I, _I, _F,
@@ -402,3 +405,39 @@ def evict_replace(k_new, v_new, code_new, victim, k, v, codes):
     _check(lib().hk_evict_replace(_ptr(k_new), _ptr(v_new), _ptr(code_new), _dtype_code(k), 32 * W,
                                   B, Hkv, d, cap, _ptr(victim), _ptr(k), _ptr(v), _ptr(codes),
                                   _stream()), "hk_evict_replace")
+
+
+def exact_topk_workspace(B, Hkv, n_ctx, n_sink, n_local, k) -> int:
+    return int(lib().hk_exact_topk_workspace(B, Hkv, n_ctx, n_sink, n_local, k))
+
+
+def exact_topk(q, k, n_ctx, n_sink, n_local, topk, idx=None, count=None, ws=None):
+    """hk_exact_topk: per KV head, the top-k candidates by the group's summed logit (the
+    exact "oracle top-k"), ascending.  q [B, Hq, 128], k [B, Hkv, cap, 128].  Returns
+    (idx [B, Hkv, topk], count [B, Hkv])."""
+    _need(q, "q")
+    _need(k, "k", dtype=q.dtype)
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    wsb = exact_topk_workspace(B, Hkv, n_ctx, n_sink, n_local, topk)
+    idx, count, ws = _topk_buffers(B, Hkv, topk, q.device, idx, count, ws, wsb)
+    _check(lib().hk_exact_topk(_ptr(q), _ptr(k), _dtype_code(q), B, Hq, Hkv, d, cap, n_ctx,
+                               n_sink, n_local, topk, _ptr(idx), _ptr(count), _ptr(ws), ws.numel(),
+                               _stream()), "hk_exact_topk")
+    return idx, count
+
+
+def topk_intersect(a, count_a, b, count_b, inter=None):
+    """hk_topk_intersect: |A_l n B_l| for the ascending lists a[..., l, :count_a] and
+    b[..., l, :count_b] (leading dimensions flattened into lists).  Returns int32 [lists]."""
+    for t, n in ((a, "a"), (count_a, "count_a"), (b, "b"), (count_b, "count_b")):
+        _need(t, n, dtype=torch.int32)
+    n = count_a.numel()
+    if count_b.numel() != n or a.numel() != n * a.shape[-1] or b.numel() != n * b.shape[-1]:
+        raise ValueError("a, b, count_a and count_b must describe the same number of lists")
+    if inter is None:
+        inter = torch.empty(n, dtype=torch.int32, device=a.device)
+    _need(inter, "inter", dtype=torch.int32, shape=(n,))
+    _check(lib().hk_topk_intersect(_ptr(a), _ptr(count_a), a.shape[-1], _ptr(b), _ptr(count_b),
+                                   b.shape[-1], n, _ptr(inter), _stream()), "hk_topk_intersect")
+    return inter

@@ -275,4 +275,38 @@ hk_status hk_evict_replace(const void *k_new, const void *v_new, const uint32_t 
                                        B * Hkv, cap, victim, kc, vc, codes, as_stream(stream)));
 }
 
+size_t hk_exact_topk_workspace(int B, int Hkv, int64_t n_ctx, int n_sink, int n_local, int k) {
+  if (check_retrieve(128, B, Hkv, n_ctx, n_ctx, n_sink, n_local, k) != HK_OK) return 0;
+  return plan_exact(B, Hkv, n_ctx, n_sink, n_local, k).total;
+}
+
+hk_status hk_exact_topk(const void *q, const void *kc, int dtype, int B, int Hq, int Hkv, int d,
+                        int64_t cap, int64_t n_ctx, int n_sink, int n_local, int k, int32_t *idx,
+                        int32_t *count, void *ws, size_t ws_bytes, void *stream) {
+  hk_status s = check_retrieve(128, B, Hkv, cap, n_ctx, n_sink, n_local, k);
+  if (s != HK_OK) return s;
+  if (dtype != HK_F32 && dtype != HK_BF16) return HK_ERR_UNSUPPORTED;
+  if (d != kHeadDim) return HK_ERR_UNSUPPORTED;
+  if (Hq < 0 || (Hkv > 0 && Hq % Hkv != 0) || (Hkv == 0 && Hq != 0)) return HK_ERR_INVALID_ARGUMENT;
+  if (Hkv > 0 && Hq / Hkv > kMaxGroup) return HK_ERR_UNSUPPORTED;
+  const ExactPlan p = plan_exact(B, Hkv, n_ctx, n_sink, n_local, k);
+  if (p.BH == 0) return HK_OK;
+  if (!count || !ws || (p.keff > 0 && (!idx || !q || !kc))) return HK_ERR_INVALID_ARGUMENT;
+  if (p.keff > 0 && !aligned(kc, 16)) return HK_ERR_UNSUPPORTED;
+  if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(launch_exact_topk(p, q, kc, dtype, Hq, Hkv, cap, k, idx, count, ws,
+                                    as_stream(stream)));
+}
+
+hk_status hk_topk_intersect(const int32_t *a, const int32_t *count_a, int64_t stride_a,
+                            const int32_t *b, const int32_t *count_b, int64_t stride_b,
+                            int n_lists, int32_t *inter, void *stream) {
+  if (n_lists < 0 || stride_a < 0 || stride_b < 0) return HK_ERR_INVALID_ARGUMENT;
+  if (n_lists == 0) return HK_OK;
+  if (n_lists > INT32_MAX / 2) return HK_ERR_UNSUPPORTED;
+  if (!a || !count_a || !b || !count_b || !inter) return HK_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_intersect(a, count_a, stride_a, b, count_b, stride_b, n_lists, inter,
+                                   as_stream(stream)));
+}
+
 }  // extern "C"

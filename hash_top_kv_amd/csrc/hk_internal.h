@@ -198,4 +198,20 @@ hipError_t launch_evict_replace(const void *k_new, const void *v_new, const uint
                                 int elem_bytes, int W, int BH, int64_t cap, const int32_t *victim,
                                 void *kc, void *vc, uint32_t *codes, hipStream_t st);
 
+// ---------------------------------------------------------------- exact top-k
+// Candidates cut into S chunks of 1024.  Workspace: keys [BH][S*1024] uint32 (logit order
+// keys), hist [BH][S][256] uint32, cnt [BH][S] uint2, meta [BH][S] int4, state [BH] uint2.
+struct ExactPlan {
+  int BH = 0, S = 0, keff = 0;
+  int64_t lo = 0, C = 0;
+  size_t off_keys = 0, off_hist = 0, off_cnt = 0, off_meta = 0, off_state = 0, total = 0;
+};
+ExactPlan plan_exact(int B, int Hkv, int64_t n_ctx, int n_sink, int n_local, int k);
+hipError_t launch_exact_topk(const ExactPlan &p, const void *q, const void *kc, int dtype, int Hq,
+                             int Hkv, int64_t cap, int k, int32_t *idx, int32_t *count, void *ws,
+                             hipStream_t st);
+hipError_t launch_intersect(const int32_t *a, const int32_t *ca, int64_t sa, const int32_t *b,
+                            const int32_t *cb, int64_t sb, int n_lists, int32_t *inter,
+                            hipStream_t st);
+
 }  // namespace hk

@@ -251,6 +251,33 @@ hk_status hk_evict_replace(const void *k_new, const void *v_new, const uint32_t 
                            const int32_t *victim, void *kc, void *vc, uint32_t *codes,
                            void *stream);
 
+/* Workspace bytes needed by hk_exact_topk (about 4 bytes per candidate). */
+size_t hk_exact_topk_workspace(int B, int Hkv, int64_t n_ctx, int n_sink, int n_local, int k);
+
+/* Exact top-k by attention logit: the "oracle top-k" that Spotlight Attention measures
+ * its hash retrieval against (Key results) and the exact Flat search of
+ * RetrievalAttention (atlas summary: Results).  Per (b, KV head g), the candidates
+ * n_sink <= t < n_ctx - n_local are ranked by the group's summed logit
+ * sum_{h in group g} q_h . K[b][g][t] (computed in fp32), largest first, ties to the
+ * lower token; k_eff = min(k, number of candidates) are selected.
+ *   q, kc, dtype, B, Hq, Hkv, d, cap: as hk_sparse_decode (q, k).
+ *   idx, count, ws: as hk_retrieve_topk (ascending token order; ws of
+ *                   hk_exact_topk_workspace(...) bytes).
+ * Errors: as hk_retrieve_topk and hk_sparse_decode. */
+hk_status hk_exact_topk(const void *q, const void *kc, int dtype, int B, int Hq, int Hkv, int d,
+                        int64_t cap, int64_t n_ctx, int n_sink, int n_local, int k, int32_t *idx,
+                        int32_t *count, void *ws, size_t ws_bytes, void *stream);
+
+/* Sizes of the intersections of n_lists pairs of ascending token lists: list l of a is
+ * a + l*stride_a with count_a[l] entries (clamped to [0, stride_a]), likewise for b;
+ * inter[l] = |A_l n B_l|.  With |A_l u B_l| = count_a[l] + count_b[l] - inter[l] this
+ * gives the retrieval IoU of Spotlight Attention (Key results).
+ *   a, count_a, b, count_b  device int32; inter device int32 [n_lists] (written).
+ * Errors: negative sizes, NULL pointers -> INVALID_ARGUMENT. */
+hk_status hk_topk_intersect(const int32_t *a, const int32_t *count_a, int64_t stride_a,
+                            const int32_t *b, const int32_t *count_b, int64_t stride_b,
+                            int n_lists, int32_t *inter, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,7 +39,7 @@ __all__ = [
     "widen", "round_bf16", "gelu", "prepare_hash", "project", "pack_bits", "unpack_bits",
     "encode", "group_mean_query", "encode_query", "candidate_range", "window_indices",
     "hamming", "select_topk", "attend", "sparse_attention", "lse_merge", "decode_step",
-    "near_zero_mask", "evict_victim", "evict_step", "exact_topk",
+    "near_zero_mask", "evict_victim", "evict_step", "exact_topk", "exact_topk_group", "iou",
 ]
 
 NEAR_ZERO = 1e-3   # |pre-sign value| below which a code bit may legitimately differ
@@ -373,6 +373,26 @@ def evict_step(q, K, V, key_codes, qcodes, k_new, v_new, code_new, n_ctx: int,
     every = np.arange(n_ctx, dtype=np.int64)
     o, lse = sparse_attention(q, K, V, [every] * Hkv, scale)
     return {"victim": victim, "K": K, "V": V, "codes": codes, "o": o, "lse": lse}
+
+
+def iou(a, b) -> float:
+    """Retrieval IoU of two token sets (Spotlight Attention: Key results): |A n B| /
+    |A u B|; two empty sets give 1."""
+    sa, sb = set(np.asarray(a).tolist()), set(np.asarray(b).tolist())
+    union = len(sa | sb)
+    return 1.0 if union == 0 else len(sa & sb) / union
+
+
+def exact_topk_group(q_rows, K, n_ctx: int, n_sink: int, n_local: int, k: int) -> np.ndarray:
+    """Exact top-k of one (batch, KV head) by the group's summed logit sum_g q_g . k_j over
+    the candidates [n_sink, n_ctx - n_local): the exact counterpart of the hash
+    retrieval, whose group-mean query ranks keys the same way.  q_rows [G, d], K [>= n_ctx,
+    d].  Ascending token order."""
+    cand = candidate_range(n_ctx, n_sink, n_local)
+    if cand.size == 0:
+        return np.zeros(0, dtype=np.int64)
+    qsum = np.asarray(q_rows, dtype=np.float64).sum(axis=0)
+    return exact_topk(qsum, np.asarray(K, dtype=np.float64)[cand], k, first=int(cand[0]))
 
 
 def exact_topk(q, k_rows, k: int, first: int = 0) -> np.ndarray:

@@ -119,6 +119,20 @@ def test_host_validation_without_gpu(hk):
     assert L.hk_evict_replace(odd, dummy, dummy, hk.HK_BF16, 128, 1, 1, 128, 10, dummy, dummy,
                               dummy, dummy, P) == hk.HK_ERR_UNSUPPORTED
     assert L.hk_evict_replace(P, P, P, hk.HK_BF16, 128, 0, 1, 128, 10, P, P, P, P, P) == hk.HK_OK
+    # exact top-k and list intersection
+    assert L.hk_exact_topk(dummy, dummy, hk.HK_BF16, 1, 8, 4, 64, 10, 10, 0, 0, 3, dummy, dummy,
+                           dummy, 1 << 20, P) == hk.HK_ERR_UNSUPPORTED
+    assert L.hk_exact_topk(dummy, dummy, hk.HK_BF16, 1, 7, 4, 128, 10, 10, 0, 0, 3, dummy, dummy,
+                           dummy, 1 << 20, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_exact_topk(dummy, dummy, hk.HK_BF16, 1, 8, 4, 128, 5000, 5000, 0, 0, 3, dummy,
+                           dummy, dummy, 1, P) == hk.HK_ERR_WORKSPACE_TOO_SMALL
+    assert L.hk_exact_topk(dummy, odd, hk.HK_BF16, 1, 8, 4, 128, 5000, 5000, 0, 0, 3, dummy,
+                           dummy, dummy, 1 << 30, P) == hk.HK_ERR_UNSUPPORTED
+    assert L.hk_exact_topk(P, P, hk.HK_BF16, 0, 8, 4, 128, 10, 10, 0, 0, 3, P, P, P, 0, P) == hk.HK_OK
+    assert L.hk_exact_topk_workspace(1, 8, 5000, 0, 0, 3) >= 8 * 5000 * 4
+    assert L.hk_topk_intersect(dummy, dummy, 4, dummy, dummy, 4, -1, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_topk_intersect(P, dummy, 4, dummy, dummy, 4, 3, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_topk_intersect(P, P, 4, P, P, 4, 0, P, P) == hk.HK_OK
     n = ctypes.c_int32(-1)
     assert L.hk_window_indices(100, 4, 64, P, ctypes.byref(n), P) == hk.HK_OK and n.value == 68
     assert L.hk_window_indices(-1, 4, 64, P, ctypes.byref(n), P) == hk.HK_ERR_INVALID_ARGUMENT

@@ -144,3 +144,30 @@ def test_exact_topk_brute_force():
     want = sorted(sorted(range(30), key=lambda j: (-s[j], j))[:7])
     assert oracle.exact_topk(q, K, 7).tolist() == want
     assert oracle.exact_topk(q, K, 7, first=4).tolist() == [w + 4 for w in want]
+
+
+def test_exact_topk_group_brute_force():
+    """Group ranking by the summed logit, over the candidate range only, with ties."""
+    rng = np.random.default_rng(53)
+    G, d, N, s, w = 3, 8, 40, 3, 5
+    qs = rng.standard_normal((G, d))
+    pool = rng.standard_normal((4, d))
+    K = pool[rng.integers(0, 4, size=N)]                      # many exact ties
+    for k in (0, 1, 6, N - s - w, N + 3):
+        score = {j: sum(float(np.dot(qs[g], K[j])) for g in range(G)) for j in range(s, N - w)}
+        want = sorted(sorted(score, key=lambda j: (-score[j], j))[:k])
+        assert oracle.exact_topk_group(qs, K, N, s, w, k).tolist() == want
+    assert oracle.exact_topk_group(qs, K, 7, 4, 4, 3).size == 0
+
+
+def test_iou_definition():
+    assert oracle.iou([1, 2, 3], [2, 3, 4]) == 2 / 4
+    assert oracle.iou([], []) == 1.0
+    assert oracle.iou([5], []) == 0.0
+    rng = np.random.default_rng(55)
+    for _ in range(20):
+        a = rng.choice(100, size=int(rng.integers(0, 30)), replace=False)
+        b = rng.choice(100, size=int(rng.integers(0, 30)), replace=False)
+        inter = sum(1 for x in a if x in list(b))
+        union = len(a) + len(b) - inter
+        assert oracle.iou(a, b) == (1.0 if union == 0 else inter / union)
