@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--hash i]
                     [--replicas R] [--no-cpu] [--prefill] [--exact] [--evict]
-                    [--unfused]
+                    [--unfused | --qheads]
 
 Default workload: retrieval at 512K tokens -- 8 KV heads x 524,288 cached 128-bit codes
 (uniform random bits plus 1% planted near neighbours of the query code), top-1024 per
@@ -174,7 +174,7 @@ def build_retrieval_case(args, torch, hk, synth):
 def build_full_case(args, torch, hk, synth):
     """Workloads 0, 1, 3, 4: hk_encode_query + hk_hamming_scan + hk_select_attend (the
     whole step after the keys were encoded), or with --unfused the separate calls."""
-    from hash_top_kv_amd.step import DecodeStep
+    from hash_top_kv_amd.step import DecodeStep, QHeadStep
     wl = synth.WORKLOADS[args.workload]
     spec = wl.hashes[args.hash]
     R = args.replicas
@@ -195,6 +195,8 @@ def build_full_case(args, torch, hk, synth):
     code_sets = [codes] + [codes.clone() for _ in range(ncopies - 1)]
     steps = [DecodeStep(K, V, cs, spec.bits, wl.N, wl.n_sink, wl.n_local, wl.k, wl.Hq, h)
              for cs in code_sets]
+    qsteps = ([QHeadStep(K, V, cs, spec.bits, wl.N, wl.n_sink, wl.n_local, wl.k, wl.Hq, h)
+               for cs in code_sets] if args.qheads else [])
     Qs = [synth.to_device(synth.make_q(wl, replica=r), wl.dtype) for r in range(R)]
 
     def st(i):
@@ -212,10 +214,26 @@ def build_full_case(args, torch, hk, synth):
     def unfused(i):
         st(i).unfused(Qs[i % R])
 
+    def qst(i):
+        return qsteps[i % len(qsteps)]
+
+    def q_enc(i):
+        qst(i).encode(Qs[i % R])
+
+    def q_ret(i):
+        qst(i).retrieve(qst(i).qcodes)
+
+    def q_att(i):
+        qst(i).attend(Qs[i % R])
+
     def check():
         st(0)(Qs[0])
         torch.cuda.synchronize()
         assert bool((st(0).count == st(0).keff).all())
+        if qsteps:
+            qst(0)(Qs[0])
+            torch.cuda.synchronize()
+            assert bool((qst(0).count == qst(0).keff).all())
 
     esz = 4 if wl.dtype == "f32" else 2
     s0 = steps[0]
@@ -224,9 +242,17 @@ def build_full_case(args, torch, hk, synth):
             "n_sink": wl.n_sink, "n_local": wl.n_local, "hash": f"{spec.kind}-{spec.bits}",
             "kv_dtype": wl.dtype, "replicas": R, "code_copies": ncopies,
             "step": ("hk_encode_query + hk_retrieve_topk + 2 x hk_sparse_decode + hk_lse_merge"
-                     if args.unfused else "hk_encode_query + hk_hamming_scan + hk_select_attend")}
+                     if args.unfused else
+                     "hk_encode_query (per query head) + hk_retrieve_topk_qheads + "
+                     "hk_sparse_decode_qheads + hk_sparse_decode (window) + hk_lse_merge"
+                     if args.qheads else "hk_encode_query + hk_hamming_scan + hk_select_attend")}
     if args.unfused:
         parts = [("decode_step", unfused, None)]
+    elif args.qheads:
+        parts = [("encode_query", q_enc, None),
+                 ("retrieve_topk_qheads", q_ret, scan_bytes),
+                 ("attend_qheads+window+merge", q_att,
+                  wl.B * wl.Hq * (s0.keff + s0.n_win) * 2 * 128 * esz)]
     else:
         parts = [("encode_query", enc, None), ("hamming_scan", scan, scan_bytes),
                  ("select+attend", rest, gather_bytes)]
@@ -383,6 +409,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prefill", action="store_true", help="also time the key encode of the whole cache")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--qheads", action="store_true",
+                    help="time the per-query-head selection variant of the step instead")
     ap.add_argument("--exact", action="store_true",
                     help="also time the exact top-k by logit and report the hash top-k's IoU with it")
     ap.add_argument("--evict", action="store_true",

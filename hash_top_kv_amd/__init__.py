@@ -52,6 +52,10 @@ _SIGNATURES = {
     "hk_retrieve_attend_workspace": (_SZ, [_I, _I, _I, _I, _I64, _I, _I, _I]),
     "hk_evict_workspace": (_SZ, [_I, _I, _I, _I64, _I, _I]),
     "hk_exact_topk_workspace": (_SZ, [_I, _I, _I64, _I, _I, _I]),
+    "hk_retrieve_topk_qheads": (_I, [_P, _P, _I, _I, _I, _I, _I64, _I64, _I, _I, _I, _P, _P, _P,
+                                     _SZ, _P]),
+    "hk_sparse_decode_qheads": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _I64, _P, _I, _F,
+                                     _P, _P, _P, _SZ, _P]),
     "hk_exact_topk": (_I, [_P, _P, _I, _I, _I, _I, _I, _I64, _I64, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "hk_topk_intersect": (_I, [_P, _P, _I64, _P, _P, _I64, _I, _P, _P]),
     "hk_evict_select": (_I, [_P, _P, _I, _I, _I, _I64, _I64, _I, _I, _P, _P, _SZ, _P]),
@@ -441,3 +445,51 @@ def topk_intersect(a, count_a, b, count_b, inter=None):
     _check(lib().hk_topk_intersect(_ptr(a), _ptr(count_a), a.shape[-1], _ptr(b), _ptr(count_b),
                                    b.shape[-1], n, _ptr(inter), _stream()), "hk_topk_intersect")
     return inter
+
+
+def retrieve_topk_qheads(codes, qcodes, bits, n_ctx, n_sink, n_local, k, idx=None, count=None,
+                         ws=None):
+    """hk_retrieve_topk_qheads: one top-k set per query head.  codes [B, Hkv, cap, W],
+    qcodes [B, Hq, W] (each query head's own code).  Returns (idx [B, Hq, k], count [B, Hq])."""
+    _need(codes, "codes", dtype=torch.int32)
+    B, Hkv, cap, W = codes.shape
+    _need(qcodes, "qcodes", dtype=torch.int32)
+    Hq = qcodes.shape[1]
+    if tuple(qcodes.shape) != (B, Hq, W):
+        raise ValueError("qcodes must be [B, Hq, bits/32]")
+    wsb = retrieve_topk_workspace(bits, B, Hq, n_ctx, n_sink, n_local, k)
+    idx, count, ws = _topk_buffers(B, Hq, k, codes.device, idx, count, ws, wsb)
+    _check(lib().hk_retrieve_topk_qheads(_ptr(codes), _ptr(qcodes), bits, B, Hq, Hkv, cap, n_ctx,
+                                         n_sink, n_local, k, _ptr(idx), _ptr(count), _ptr(ws),
+                                         ws.numel(), _stream()), "hk_retrieve_topk_qheads")
+    return idx, count
+
+
+def sparse_decode_qheads(q, k, v, idx, max_count, count=None, scale=None, o=None, lse=None,
+                         ws=None):
+    """hk_sparse_decode_qheads: query head h attends over its own list idx[b, h, :count]
+    with the rows of KV head h // G.  Returns (o [B, Hq, 128], lse [B, Hq])."""
+    dt = _dtype_code(q)
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    _need(q, "q")
+    _need(k, "k", dtype=q.dtype)
+    _need(v, "v", dtype=q.dtype, shape=k.shape)
+    _need(idx, "idx", dtype=torch.int32)
+    if idx.shape[:2] != (B, Hq):
+        raise ValueError("idx must be [B, Hq, n]")
+    if count is not None:
+        _need(count, "count", dtype=torch.int32, shape=(B, Hq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(sparse_decode_workspace(B, Hq, Hq, max_count, d), q.device)
+    _check(lib().hk_sparse_decode_qheads(_ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, d, cap,
+                                         _ptr(idx), idx.shape[-1], _ptr(count), max_count,
+                                         float(scale), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
+                                         _stream()), "hk_sparse_decode_qheads")
+    return o, lse

@@ -309,4 +309,47 @@ hk_status hk_topk_intersect(const int32_t *a, const int32_t *count_a, int64_t st
                                    as_stream(stream)));
 }
 
+hk_status hk_retrieve_topk_qheads(const uint32_t *codes, const uint32_t *qcodes, int bits, int B,
+                                  int Hq, int Hkv, int64_t cap, int64_t n_ctx, int n_sink,
+                                  int n_local, int k, int32_t *idx, int32_t *count, void *ws,
+                                  size_t ws_bytes, void *stream) {
+  if (Hkv <= 0 || Hq < Hkv || Hq % Hkv != 0) return HK_ERR_INVALID_ARGUMENT;
+  if (Hq / Hkv > kMaxGroup) return HK_ERR_UNSUPPORTED;
+  hk_status s = check_retrieve(bits, B, Hq, cap, n_ctx, n_sink, n_local, k);
+  if (s != HK_OK) return s;
+  const RetrievePlan p = plan_retrieve(bits, B, Hq, n_ctx, n_sink, n_local, k);
+  if (p.BH == 0) return HK_OK;
+  if (!count || !ws || (p.keff > 0 && !idx) || (p.S > 0 && (!codes || !qcodes)))
+    return HK_ERR_INVALID_ARGUMENT;
+  if (p.S > 0 && !aligned(codes, code_align(bits))) return HK_ERR_UNSUPPORTED;
+  if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = as_stream(stream);
+  hipError_t e = launch_hamming_scan_qheads(p, Hq / Hkv, codes, qcodes, cap, ws, st);
+  if (e != hipSuccess) return HK_ERR_HIP;
+  return from_hip(launch_topk_select(p, k, idx, count, ws, st));
+}
+
+hk_status hk_sparse_decode_qheads(const void *q, const void *k, const void *v, int dtype, int B,
+                                  int Hq, int Hkv, int d, int64_t cap, const int32_t *idx,
+                                  int64_t idx_stride, const int32_t *count, int max_count,
+                                  float scale, float *o, float *lse, void *ws, size_t ws_bytes,
+                                  void *stream) {
+  if (dtype != HK_F32 && dtype != HK_BF16) return HK_ERR_UNSUPPORTED;
+  if (d != kHeadDim) return HK_ERR_UNSUPPORTED;
+  if (B < 0 || Hq < 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq < Hkv || cap < 0 || max_count < 0 ||
+      idx_stride < 0)
+    return HK_ERR_INVALID_ARGUMENT;
+  if ((int64_t)B * Hq > 65535) return HK_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq == 0) return HK_OK;
+  if (!q || !o || !lse) return HK_ERR_INVALID_ARGUMENT;
+  if (max_count > 0 && (!k || !v || !idx)) return HK_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return HK_ERR_UNSUPPORTED;
+  const DecodePlan p = plan_decode(B, Hq, Hq, max_count);
+  if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
+  if (p.total > 0 && !ws) return HK_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_sparse_decode(p, q, k, v, dtype, B, Hq, Hq, cap, idx, idx_stride, count,
+                                       max_count, scale, o, lse, ws, as_stream(stream),
+                                       Hq / Hkv));
+}
+
 }  // extern "C"

@@ -19,12 +19,15 @@ constexpr int kMaxSliceRows = 256;         // rows_per_split never exceeds this
 
 // grid (P, B*Hkv).  Writes either the final (o, lse) of its query heads (P == 1) or the
 // normalised partial of slice p into out_o + p*rows*d, out_lse + p*rows.
+// kv_group: 1 for lists per KV head; G for lists per query head, where the launch's
+// "KV heads" are the query heads (Hkv = Hq, G = 1 here) and list bh reads the rows of KV
+// head bh / kv_group.
 template <bool BF16, int G>
 __global__ __launch_bounds__(kAttThreads) void sparse_decode_kernel(
     const void *__restrict__ q, const void *__restrict__ kc, const void *__restrict__ vc,
     int Hq, int Hkv, int64_t cap, const int32_t *__restrict__ idx, int64_t idx_stride,
     const int32_t *__restrict__ count, int max_count, int rows_per_split, float scale_log2,
-    float *__restrict__ out_o, float *__restrict__ out_lse, int64_t rows) {
+    float *__restrict__ out_o, float *__restrict__ out_lse, int64_t rows, int kv_group) {
   const int p = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / Hkv;
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(kAttThreads) void sparse_decode_kernel(
   typename AttentionCore<BF16, G>::type ga;
   ga.init(q, row0, scale_log2);
   __syncthreads();
-  ga.run_block(kc, vc, (size_t)bh * (size_t)cap, len, [&](int r) { return s_idx[r]; });
+  ga.run_block(kc, vc, (size_t)(bh / kv_group) * (size_t)cap, len, [&](int r) { return s_idx[r]; });
   ga.combine_store(out_o + ((int64_t)p * rows + row0) * kHeadDim, out_lse + (int64_t)p * rows + row0);
 }
 
@@ -204,21 +207,21 @@ template <bool BF16, int G>
 void decode_launch(const DecodePlan &pl, const void *q, const void *k, const void *v, int B,
                    int Hq, int Hkv, int64_t cap, const int32_t *idx, int64_t idx_stride,
                    const int32_t *count, int max_count, float scale_log2, float *o_dst,
-                   float *lse_dst, hipStream_t st) {
+                   float *lse_dst, int kv_group, hipStream_t st) {
   hipLaunchKernelGGL((sparse_decode_kernel<BF16, G>), dim3(pl.P, B * Hkv), dim3(kAttThreads),
                      0, st, q, k, v, Hq, Hkv, cap, idx, idx_stride, count, max_count,
-                     pl.rows_per_split, scale_log2, o_dst, lse_dst, (int64_t)B * Hq);
+                     pl.rows_per_split, scale_log2, o_dst, lse_dst, (int64_t)B * Hq, kv_group);
 }
 
 template <bool BF16>
 void decode_dispatch(const DecodePlan &pl, const void *q, const void *k, const void *v, int B,
                      int Hq, int Hkv, int64_t cap, const int32_t *idx, int64_t idx_stride,
                      const int32_t *count, int max_count, float scale_log2, float *o_dst,
-                     float *lse_dst, hipStream_t st) {
+                     float *lse_dst, int kv_group, hipStream_t st) {
 #define HK_DEC_CASE(GG)                                                                    \
   case GG:                                                                                 \
     decode_launch<BF16, GG>(pl, q, k, v, B, Hq, Hkv, cap, idx, idx_stride, count,          \
-                            max_count, scale_log2, o_dst, lse_dst, st);                    \
+                            max_count, scale_log2, o_dst, lse_dst, kv_group, st);          \
     break;
   switch (pl.G) {
     HK_DEC_CASE(1) HK_DEC_CASE(2) HK_DEC_CASE(3) HK_DEC_CASE(4)
@@ -263,7 +266,7 @@ hipError_t launch_sparse_decode(const DecodePlan &pl, const void *q, const void 
                                 const void *v, int dtype, int B, int Hq, int Hkv,
                                 int64_t cap, const int32_t *idx, int64_t idx_stride,
                                 const int32_t *count, int max_count, float scale, float *o,
-                                float *lse, void *ws, hipStream_t st) {
+                                float *lse, void *ws, hipStream_t st, int kv_group) {
   if ((int64_t)B * Hq == 0) return hipSuccess;
   const float scale_log2 = scale * kLog2e;
   uint8_t *w8 = static_cast<uint8_t *>(ws);
@@ -271,10 +274,10 @@ hipError_t launch_sparse_decode(const DecodePlan &pl, const void *q, const void 
   float *lse_dst = pl.P > 1 ? reinterpret_cast<float *>(w8 + pl.off_lse) : lse;
   if (dtype == HK_BF16)
     decode_dispatch<true>(pl, q, k, v, B, Hq, Hkv, cap, idx, idx_stride, count, max_count,
-                          scale_log2, o_dst, lse_dst, st);
+                          scale_log2, o_dst, lse_dst, kv_group, st);
   else
     decode_dispatch<false>(pl, q, k, v, B, Hq, Hkv, cap, idx, idx_stride, count, max_count,
-                           scale_log2, o_dst, lse_dst, st);
+                           scale_log2, o_dst, lse_dst, kv_group, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.P == 1) return e;
   return launch_lse_merge(o_dst, lse_dst, pl.P, (int64_t)B * Hq, kHeadDim, o, lse, st);

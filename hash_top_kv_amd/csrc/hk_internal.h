@@ -54,6 +54,11 @@ RetrievePlan plan_retrieve(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, 
 hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
                                const uint32_t *qcodes, int64_t cap, void *ws,
                                hipStream_t st);
+// Per-query-head retrieval: p planned with B*Hq heads; each code is read once and
+// compared with the G query codes of its KV head.
+hipError_t launch_hamming_scan_qheads(const RetrievePlan &p, int G, const uint32_t *codes,
+                                      const uint32_t *qcodes, int64_t cap, void *ws,
+                                      hipStream_t st);
 hipError_t launch_topk_select(const RetrievePlan &p, int k, int32_t *idx, int32_t *count,
                               void *ws, hipStream_t st);
 hipError_t launch_topk_threshold(const RetrievePlan &p, int32_t *count, void *ws,
@@ -74,7 +79,7 @@ hipError_t launch_sparse_decode(const DecodePlan &p, const void *q, const void *
                                 const void *v, int dtype, int B, int Hq, int Hkv,
                                 int64_t cap, const int32_t *idx, int64_t idx_stride,
                                 const int32_t *count, int max_count, float scale, float *o,
-                                float *lse, void *ws, hipStream_t st);
+                                float *lse, void *ws, hipStream_t st, int kv_group = 1);
 hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int P,
                             int64_t rows, int d, float *o, float *lse, hipStream_t st);
 // Same kernel, also for P == 0 (every row empty: o = 0, lse = -inf).

@@ -303,6 +303,98 @@ __global__ void window_indices_kernel(int32_t n_sinks, int64_t local0, int32_t n
   if (i < n) idx[i] = (i < n_sinks) ? i : (int32_t)(local0 + (i - n_sinks));
 }
 
+// grid (S, B*Hkv): as hamming_scan_kernel, for the G query codes of one KV head at once
+// (per-query-head selection): each code is read once and compared with every query code
+// of the group; query head g of the group gets its own distance stash and histograms,
+// laid out as if it were a head of its own (head index bh*G + g).
+template <int W, int LPT, int G>
+__global__ __launch_bounds__(kScanThreads) void hamming_scan_group_kernel(
+    const uint32_t *__restrict__ codes, const uint32_t *__restrict__ qcodes, int64_t cap,
+    int64_t lo, int64_t C, int S, uint32_t *__restrict__ stash, uint32_t *__restrict__ hist_out) {
+  constexpr int BINS = 32 * W;
+  constexpr int NBP = BINS + 4;
+  constexpr int CH = kScanThreads * LPT;
+  constexpr int NSB = BINS / 8;
+  using CV = CodeVec<W>;
+  using V = typename CV::T;
+  __shared__ uint32_t hist[G][kScanThreads / 64][NBP];
+
+  const int c = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+  for (int i = t; i < G * (kScanThreads / 64) * NBP; i += kScanThreads) (&hist[0][0][0])[i] = 0u;
+  uint32_t q[G][W];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int w = 0; w < W; ++w) q[g][w] = qcodes[((int64_t)bh * G + g) * W + w];
+  __syncthreads();
+
+  const int64_t p0 = (int64_t)c * CH;
+  const int64_t pw = p0 + (int64_t)wave * (64 * LPT) + (t & 63);
+  const V *base = reinterpret_cast<const V *>(codes + ((int64_t)bh * cap + lo) * W);
+  V v[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int64_t p = pw + 64 * i;
+    v[i] = (p < C) ? __builtin_nontemporal_load(base + p) : CV::zero();
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    uint32_t *st = stash + (((int64_t)bh * G + g) * S + c) * stash_words_per_chunk<LPT>();
+#pragma unroll
+    for (int i4 = 0; i4 < LPT / 4; ++i4) {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * i4 + j;
+        const int64_t p = pw + 64 * i;
+        uint32_t d = 0xFFu;
+        if (p < C) {
+          d = CV::dist(v[i], q[g]);
+          atomicAdd(&hist[g][wave][d], 1u);
+        }
+        packed |= d << (8 * j);
+      }
+      st[i4 * kScanThreads + t] = packed;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    uint32_t *out = hist_out + (((int64_t)bh * G + g) * S + c) * (BINS + NSB);
+    if (t < BINS) {
+      uint32_t sum = 0;
+#pragma unroll
+      for (int w = 0; w < kScanThreads / 64; ++w) sum += hist[g][w][t];
+      out[t] = sum;
+    } else if (t < BINS + NSB) {
+      const int b0 = 8 * (t - BINS);
+      uint32_t sum = 0;
+#pragma unroll
+      for (int w = 0; w < kScanThreads / 64; ++w)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += hist[g][w][b0 + e];
+      out[t] = sum;
+    }
+  }
+}
+
+template <int W, int LPT>
+void scan_group_launch(const RetrievePlan &p, int G, const uint32_t *codes,
+                       const uint32_t *qcodes, int64_t cap, uint32_t *stash, uint32_t *hist,
+                       hipStream_t st) {
+  const dim3 grid(p.S, p.BH / G), blk(kScanThreads);
+#define HK_GS(GG)                                                                            \
+  case GG:                                                                                   \
+    hipLaunchKernelGGL((hamming_scan_group_kernel<W, LPT, GG>), grid, blk, 0, st, codes,     \
+                       qcodes, cap, p.lo, p.C, p.S, stash, hist);                            \
+    break;
+  switch (G) { HK_GS(2) HK_GS(3) HK_GS(4) HK_GS(5) HK_GS(6) HK_GS(7) HK_GS(8) default: break; }
+#undef HK_GS
+}
+
 template <int W, int LPT>
 void scan_launch(const RetrievePlan &p, const uint32_t *codes, const uint32_t *qcodes,
                  int64_t cap, uint32_t *stash, uint32_t *hist, hipStream_t st) {
@@ -356,6 +448,24 @@ hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
   } else {
     if (p.lpt == 8) scan_launch<2, 8>(p, codes, qcodes, cap, stash, hist, st);
     else scan_launch<2, 4>(p, codes, qcodes, cap, stash, hist, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_hamming_scan_qheads(const RetrievePlan &p, int G, const uint32_t *codes,
+                                      const uint32_t *qcodes, int64_t cap, void *ws,
+                                      hipStream_t st) {
+  if (G == 1) return launch_hamming_scan(p, codes, qcodes, cap, ws, st);
+  if (p.BH == 0 || p.S == 0) return hipSuccess;
+  uint8_t *w8 = static_cast<uint8_t *>(ws);
+  uint32_t *stash = reinterpret_cast<uint32_t *>(w8 + p.off_stash);
+  uint32_t *hist = reinterpret_cast<uint32_t *>(w8 + p.off_hist);
+  if (p.W == 4) {
+    if (p.lpt == 8) scan_group_launch<4, 8>(p, G, codes, qcodes, cap, stash, hist, st);
+    else scan_group_launch<4, 4>(p, G, codes, qcodes, cap, stash, hist, st);
+  } else {
+    if (p.lpt == 8) scan_group_launch<2, 8>(p, G, codes, qcodes, cap, stash, hist, st);
+    else scan_group_launch<2, 4>(p, G, codes, qcodes, cap, stash, hist, st);
   }
   return hipGetLastError();
 }

@@ -20,9 +20,9 @@ import math
 import torch
 
 from . import (Hash, encode_query, evict_replace, evict_select, evict_workspace, hamming_scan,
-               lse_merge, retrieve_attend_workspace, retrieve_topk_workspace, select_attend,
-               sparse_decode, sparse_decode_workspace, window_indices, workspace, _check, _ptr,
-               _stream, lib)
+               lse_merge, retrieve_attend_workspace, retrieve_topk_qheads, retrieve_topk_workspace,
+               select_attend, sparse_decode, sparse_decode_qheads, sparse_decode_workspace,
+               window_indices, workspace, _check, _ptr, _stream, lib)
 
 
 class DecodeStep:
@@ -143,3 +143,59 @@ class EvictStep:
         self.replace(k_new, v_new)
         o, lse = self.attend(q)
         return o, lse, self.victim
+
+
+class QHeadStep:
+    """The decode step with one selection per query head (RetrievalAttention's GQA
+    choice, elamur summary: Summary):
+
+        hk_encode_query with Hkv = Hq (each query head's own code)
+        -> hk_retrieve_topk_qheads -> hk_sparse_decode_qheads (each head over its list)
+        -> hk_sparse_decode over the sink + local window -> hk_lse_merge
+    """
+
+    def __init__(self, K, V, codes, bits, n_ctx, n_sink, n_local, k, Hq, hash: Hash):
+        self.K, self.V, self.codes, self.bits, self.hash = K, V, codes, bits, hash
+        B, Hkv, cap, d = K.shape
+        self.B, self.Hkv, self.cap, self.d, self.Hq = B, Hkv, cap, d, Hq
+        self.n_ctx, self.n_sink, self.n_local, self.k = n_ctx, n_sink, n_local, k
+        dev = K.device
+        self.keff = max(0, min(k, n_ctx - n_sink - n_local))
+        W = bits // 32
+        self.qcodes = torch.empty((B, Hq, W), dtype=torch.int32, device=dev)
+        self.idx = torch.zeros((B, Hq, max(k, 1)), dtype=torch.int32, device=dev)
+        self.count = torch.zeros((B, Hq), dtype=torch.int32, device=dev)
+        self.win = window_indices(n_ctx, n_sink, n_local, dev)
+        self.n_win = int(self.win.numel())
+        self.ws_r = workspace(retrieve_topk_workspace(bits, B, Hq, n_ctx, n_sink, n_local, k), dev)
+        self.ws_q = workspace(sparse_decode_workspace(B, Hq, Hq, self.keff, d), dev)
+        self.ws_w = workspace(sparse_decode_workspace(B, Hq, Hkv, self.n_win, d), dev)
+        self.o_parts = torch.empty((2, B, Hq, d), dtype=torch.float32, device=dev)
+        self.lse_parts = torch.empty((2, B, Hq), dtype=torch.float32, device=dev)
+        self.o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        self.scale = 1.0 / math.sqrt(d)
+
+    def encode(self, q):
+        return encode_query(self.hash, q, self.Hq, self.qcodes)
+
+    def retrieve(self, qcodes):
+        retrieve_topk_qheads(self.codes, qcodes, self.bits, self.n_ctx, self.n_sink, self.n_local,
+                             self.k, self.idx, self.count, self.ws_r)
+
+    def attend(self, q):
+        sparse_decode_qheads(q, self.K, self.V, self.idx, self.keff, count=self.count,
+                             scale=self.scale, o=self.o_parts[0], lse=self.lse_parts[0], ws=self.ws_q)
+        if self.n_win == 0:
+            return self.o_parts[0], self.lse_parts[0]
+        sparse_decode(q, self.K, self.V, self.win, self.n_win, idx_stride=0, scale=self.scale,
+                      o=self.o_parts[1], lse=self.lse_parts[1], ws=self.ws_w)
+        return lse_merge(self.o_parts, self.lse_parts, self.o, self.lse)
+
+    def __call__(self, q, qcodes=None):
+        """Returns (o [B, Hq, d], lse [B, Hq]); with qcodes [B, Hq, W] given the query is
+        not hashed."""
+        if qcodes is None:
+            qcodes = self.encode(q)
+        self.retrieve(qcodes)
+        return self.attend(q)

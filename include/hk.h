@@ -278,6 +278,32 @@ hk_status hk_topk_intersect(const int32_t *a, const int32_t *count_a, int64_t st
                             const int32_t *b, const int32_t *count_b, int64_t stride_b,
                             int n_lists, int32_t *inter, void *stream);
 
+/* Per-query-head retrieval, the GQA choice of RetrievalAttention (elamur summary:
+ * Summary -- an index per query head): one top-k set per query head instead of one per
+ * KV head.  Query head h (of KV head h / G, G = Hq / Hkv) compares its own code
+ * qcodes[b][h] with the codes of its KV head; selection as hk_retrieve_topk.  Each
+ * cached code is read once for the whole group.
+ *   codes   device [B][Hkv][cap][bits/32]; qcodes device [B][Hq][bits/32], e.g. from
+ *           hk_encode_query with Hkv = Hq (each head's own query).
+ *   idx     device int32 [B][Hq][k]; count device int32 [B][Hq].
+ *   ws      hk_retrieve_topk_workspace(bits, B, Hq, ...) bytes (the workspace of Hq heads).
+ * Errors: as hk_retrieve_topk; Hq % Hkv != 0 -> INVALID_ARGUMENT; G > 8 -> UNSUPPORTED. */
+hk_status hk_retrieve_topk_qheads(const uint32_t *codes, const uint32_t *qcodes, int bits, int B,
+                                  int Hq, int Hkv, int64_t cap, int64_t n_ctx, int n_sink,
+                                  int n_local, int k, int32_t *idx, int32_t *count, void *ws,
+                                  size_t ws_bytes, void *stream);
+
+/* Attention of every query head over its own token list (per-query-head selection):
+ * as hk_sparse_decode, except that the list of query head h of batch b starts at
+ * idx + (b*Hq + h) * idx_stride with count[b][h] entries, and is scored against the K/V
+ * rows of KV head h / G.  ws: hk_sparse_decode_workspace(B, Hq, Hq, d, max_count) bytes.
+ * Errors: as hk_sparse_decode. */
+hk_status hk_sparse_decode_qheads(const void *q, const void *k, const void *v, int dtype, int B,
+                                  int Hq, int Hkv, int d, int64_t cap, const int32_t *idx,
+                                  int64_t idx_stride, const int32_t *count, int max_count,
+                                  float scale, float *o, float *lse, void *ws, size_t ws_bytes,
+                                  void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,7 @@ __all__ = [
     "widen", "round_bf16", "gelu", "prepare_hash", "project", "pack_bits", "unpack_bits",
     "encode", "group_mean_query", "encode_query", "candidate_range", "window_indices",
     "hamming", "select_topk", "attend", "sparse_attention", "lse_merge", "decode_step",
+    "decode_step_qheads",
     "near_zero_mask", "evict_victim", "evict_step", "exact_topk", "exact_topk_group", "iou",
 ]
 
@@ -331,6 +332,37 @@ def decode_step(q, K, V, key_codes, hp: dict, n_ctx: int, n_sink: int, n_local: 
         o[h], lse[h] = lse_merge(np.stack([o1[h], o2[h]]), np.array([l1[h], l2[h]]))
     return {"o": o, "lse": lse, "idx": idx_lists, "qcodes": qcodes, "qy": qy,
             "o_topk": o1, "lse_topk": l1, "o_win": o2, "lse_win": l2, "G": G}
+
+
+def decode_step_qheads(q, K, V, key_codes, hp: dict, n_ctx: int, n_sink: int, n_local: int,
+                       k: int, scale: float | None = None, qcodes=None):
+    """The decode step with one selection per query head (RetrievalAttention (elamur
+    summary): Summary, an index per query head): query head h hashes its own query,
+    selects the top-k of KV head h // G's codes by Hamming distance, attends over them
+    and over the window, and the two partials are merged.
+
+    q [Hq, d], K, V [Hkv, >= n_ctx, d], key_codes [Hkv, >= n_ctx, W]; ``qcodes`` [Hq, W]
+    replaces the query hash when given.  Returns dict(o, lse, idx per query head, qcodes).
+    """
+    Hq, d = q.shape
+    Hkv = K.shape[0]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if qcodes is None:
+        qcodes, _ = encode(q, hp)
+    win = window_indices(n_ctx, n_sink, n_local)
+    o = np.zeros((Hq, d))
+    lse = np.zeros(Hq)
+    idx = []
+    for h in range(Hq):
+        kv = h // G
+        sel = select_topk(key_codes[kv], qcodes[h], n_ctx, n_sink, n_local, k)
+        idx.append(sel)
+        o1, l1 = attend(q[h], K[kv][sel], V[kv][sel], scale)
+        o2, l2 = attend(q[h], K[kv][win], V[kv][win], scale)
+        o[h], lse[h] = lse_merge(np.stack([o1, o2]), np.array([l1, l2]))
+    return {"o": o, "lse": lse, "idx": idx, "qcodes": qcodes}
 
 
 # ---------------------------------------------------------------------------------

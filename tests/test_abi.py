@@ -133,6 +133,18 @@ def test_host_validation_without_gpu(hk):
     assert L.hk_topk_intersect(dummy, dummy, 4, dummy, dummy, 4, -1, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
     assert L.hk_topk_intersect(P, dummy, 4, dummy, dummy, 4, 3, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
     assert L.hk_topk_intersect(P, P, 4, P, P, 4, 0, P, P) == hk.HK_OK
+    # per-query-head retrieval and attention
+    assert L.hk_retrieve_topk_qheads(P, P, 128, 1, 6, 4, 10, 10, 0, 0, 3, P, P, P, 0, P) \
+        == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_retrieve_topk_qheads(P, P, 128, 1, 36, 4, 10, 10, 0, 0, 3, P, P, P, 0, P) \
+        == hk.HK_ERR_UNSUPPORTED
+    assert L.hk_retrieve_topk_qheads(dummy, dummy, 128, 1, 8, 4, 5000, 5000, 0, 0, 3, dummy,
+                                     dummy, dummy, 1, P) == hk.HK_ERR_WORKSPACE_TOO_SMALL
+    assert L.hk_retrieve_topk_qheads(P, P, 128, 0, 8, 4, 10, 10, 0, 0, 3, P, P, P, 0, P) == hk.HK_OK
+    assert L.hk_sparse_decode_qheads(dummy, dummy, dummy, hk.HK_BF16, 1, 30, 4, 128, 10, dummy, 4,
+                                     P, 4, f, dummy, dummy, dummy, 1 << 30, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_sparse_decode_qheads(dummy, odd, dummy, hk.HK_BF16, 1, 8, 4, 128, 10, dummy, 4,
+                                     P, 4, f, dummy, dummy, dummy, 1 << 30, P) == hk.HK_ERR_UNSUPPORTED
     n = ctypes.c_int32(-1)
     assert L.hk_window_indices(100, 4, 64, P, ctypes.byref(n), P) == hk.HK_OK and n.value == 68
     assert L.hk_window_indices(-1, 4, 64, P, ctypes.byref(n), P) == hk.HK_ERR_INVALID_ARGUMENT

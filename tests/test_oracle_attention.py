@@ -171,3 +171,38 @@ def test_iou_definition():
         inter = sum(1 for x in a if x in list(b))
         union = len(a) + len(b) - inter
         assert oracle.iou(a, b) == (1.0 if union == 0 else inter / union)
+
+
+def test_decode_step_qheads_is_per_head_hamming_topk_then_softmax():
+    """Per-query-head selection against a separate construction: each query head's own
+    code (its sign pattern under R), its top-k by (bit-count distance, index) over its
+    KV head (h // G) built with Python sets of bits, and scipy's softmax over the union
+    with the window.  With G = 1 it coincides with the per-KV-head step."""
+    rng = np.random.default_rng(57)
+    Hq, Hkv, N, d, s, w, k = 6, 2, 150, 16, 3, 10, 9
+    q = rng.standard_normal((Hq, d))
+    K = rng.standard_normal((Hkv, N, d))
+    V = rng.standard_normal((Hkv, N, d))
+    R = rng.standard_normal((64, d)).astype(np.float32)
+    hp = oracle.prepare_hash({"kind": "lsh", "bits": 64, "dtype": "f32", "R": R})
+    codes = np.stack([oracle.encode(K[h], hp)[0] for h in range(Hkv)])
+    r = oracle.decode_step_qheads(q, K, V, codes, hp, N, s, w, k)
+    scale = 1 / math.sqrt(d)
+    win = list(range(s)) + list(range(N - w, N))
+    for h in range(Hq):
+        kv = h // (Hq // Hkv)
+        qbits = {j for j in range(64) if float(np.dot(R[j].astype(np.float64), q[h])) > 0}
+        dist = {}
+        for t in range(s, N - w):
+            kbits = {j for j in range(64) if float(np.dot(R[j].astype(np.float64), K[kv, t])) > 0}
+            dist[t] = len(qbits ^ kbits)
+        want = sorted(sorted(dist, key=lambda t: (dist[t], t))[:k])
+        assert r["idx"][h].tolist() == want
+        sel = want + win
+        logits = K[kv][sel] @ q[h] * scale
+        assert np.allclose(r["o"][h], softmax(logits) @ V[kv][sel], atol=1e-12)
+        assert abs(r["lse"][h] - logsumexp(logits)) < 1e-12
+    # G = 1: the same as the per-KV-head step
+    r1 = oracle.decode_step_qheads(q[:Hkv], K, V, codes, hp, N, s, w, k)
+    r2 = oracle.decode_step(q[:Hkv], K, V, codes, hp, N, s, w, k)
+    assert np.allclose(r1["o"], r2["o"], atol=1e-12) and np.allclose(r1["lse"], r2["lse"], atol=1e-12)
