@@ -257,7 +257,30 @@ def build_full_case(args, torch, hk, synth):
         parts = [("encode_query", enc, None), ("hamming_scan", scan, scan_bytes),
                  ("select+attend", rest, gather_bytes)]
     return parts, check, info, {"wl": wl, "K": K, "V": V, "h": h, "codes": codes, "spec": spec,
-                                "code_sets": code_sets, "Qs": Qs, "steps": steps}
+                                "code_sets": code_sets, "Qs": Qs, "steps": steps, "qsteps": qsteps}
+
+
+def qhead_overlap(torch, hk, ctx):
+    """How much the G per-query-head selections of a KV head overlap: the IoU of every
+    pair of query heads in a group (the traffic a deduplicated union would save)."""
+    wl, qs = ctx["wl"], ctx["qsteps"][0]
+    qs(ctx["Qs"][0])
+    G = wl.Hq // wl.Hkv
+    pairs = [(b, g * G + i, g * G + j) for b in range(wl.B) for g in range(wl.Hkv)
+             for i in range(G) for j in range(i + 1, G)]
+    if not pairs:
+        return None
+    bi = torch.tensor([p[0] for p in pairs], device="cuda")
+    ha = torch.tensor([p[1] for p in pairs], device="cuda")
+    hb = torch.tensor([p[2] for p in pairs], device="cuda")
+    a, b = qs.idx[bi, ha].contiguous(), qs.idx[bi, hb].contiguous()
+    ca, cb = qs.count[bi, ha].contiguous(), qs.count[bi, hb].contiguous()
+    inter = hk.topk_intersect(a, ca, b, cb)
+    torch.cuda.synchronize()
+    i, x, y = (t.cpu().numpy().astype(np.float64) for t in (inter, ca, cb))
+    iou = i / np.maximum(x + y - i, 1)
+    return {"pairs": len(pairs), "iou_mean": round(float(iou.mean()), 4),
+            "iou_max": round(float(iou.max()), 4)}
 
 
 def time_prefill(torch, hk, ctx, steps):
@@ -522,6 +545,8 @@ def main():
            "wall_ms_timed_region": round(wall_ms, 3)}
     if args.prefill and args.workload != 2:
         out["prefill"] = time_prefill(torch, hk, ctx, 10)
+    if args.qheads and args.workload != 2:
+        out["qhead_overlap"] = qhead_overlap(torch, hk, ctx)
     if args.exact and args.workload != 2:
         out["exact_topk"] = time_exact(torch, hk, ctx, args.steps)
     if args.evict and args.workload != 2:

@@ -158,9 +158,9 @@ hk_status hk_retrieve_attend(const uint32_t *codes, const uint32_t *qcodes, int 
   if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
   const hipStream_t st = as_stream(stream);
   hipError_t e = launch_hamming_scan(p.r, codes, qcodes, cap, ws, st);
-  if (e == hipSuccess) e = launch_topk_threshold(p.r, count, ws, st);
   if (e == hipSuccess)
-    e = launch_fused_attend(p, q, kc, vc, dtype, B, Hq, Hkv, cap, scale, topk, idx, o, lse, ws, st);
+    e = launch_fused_attend(p, q, kc, vc, dtype, B, Hq, Hkv, cap, scale, topk, idx, count, o, lse,
+                            ws, st);
   return from_hip(e);
 }
 
@@ -183,10 +183,8 @@ hk_status hk_select_attend(int bits, const void *q, const void *kc, const void *
   if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16)) return HK_ERR_UNSUPPORTED;
   if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
   const hipStream_t st = as_stream(stream);
-  hipError_t e = launch_topk_threshold(p.r, count, ws, st);
-  if (e == hipSuccess)
-    e = launch_fused_attend(p, q, kc, vc, dtype, B, Hq, Hkv, cap, scale, topk, idx, o, lse, ws, st);
-  return from_hip(e);
+  return from_hip(launch_fused_attend(p, q, kc, vc, dtype, B, Hq, Hkv, cap, scale, topk, idx,
+                                      count, o, lse, ws, st));
 }
 
 hk_status hk_window_indices(int64_t n_ctx, int n_sink, int n_local, int32_t *idx,

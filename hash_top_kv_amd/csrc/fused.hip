@@ -1,23 +1,24 @@
-// Fused top-k emit + exact attention over the selected tokens, for one decode step.
+// Fused top-k select + exact attention over the selected tokens, for one decode step.
 //
-// After the Hamming scan and the threshold, each chunk's workgroup compacts its selected
-// tokens (writing them to the head's ascending index list, as hk_topk_select does, and
-// to LDS), gathers their K/V rows and computes the partial attention of the G query
-// heads of its KV head over them.  Extra workgroups do the same over slices of the static
+// After the Hamming scan, each chunk's workgroup derives its head's distance threshold
+// from the chunk histograms, compacts its selected tokens (writing them to the head's
+// ascending index list, as hk_topk_select does, and to LDS), gathers their K/V rows and
+// computes the partial attention of the G query heads of its KV head over them.  Extra workgroups do the same over slices of the static
 // sink + local window.  The partials of a head -- disjoint token sets -- are then merged
 // by log-sum-exp rescaling (RetrievalAttention, atlas summary: Approach), which gives
 // attention over the selected tokens and the window together.
 //
-// Compared with emit -> sparse decode -> merge, this saves one kernel and one dependent
-// memory round trip (re-reading the index list) on the decode step's critical path.
+// Compared with threshold -> emit -> sparse decode -> merge, this saves two kernels and
+// their dependent memory round trips (the threshold's outputs, the index list) on the
+// decode step's critical path.
 #include "attend_core.h"
 #include "select_core.h"
 
 namespace hk {
 namespace {
 
-// grid (Sc + Sw, B*Hkv).  Blocks c < Sc cover chunks [c*CPB, (c+1)*CPB) of the
-// retrieval; blocks c >= Sc cover window slice c - Sc.  Block c writes the normalised
+// grid (Sc + Sw, B*Hkv), after the Hamming scan.  Blocks c < Sc cover chunks
+// [c*CPB, (c+1)*CPB) of the retrieval; blocks c >= Sc cover window slice c - Sc.  Block c writes the normalised
 // partial of part c.  A chunk block compacts its chunks' selected tokens into an LDS
 // list (and into the head's index list) and attends over the list; when a list would
 // overflow LDS it is attended and emptied first, so any selection size works.
@@ -30,8 +31,8 @@ constexpr int64_t kResidentBlocks = 768;
 
 template <int LPT, bool BF16, int G>
 __device__ __forceinline__ void emit_attend_body(
-    const uint32_t *__restrict__ stash, const int4 *__restrict__ meta,
-    const int2 *__restrict__ params, int S, int CPB, int Sc, int64_t lo, int k,
+    const uint32_t *__restrict__ stash, const uint32_t *__restrict__ hist, int bins, int64_t C,
+    int keff, int32_t *__restrict__ count, int S, int CPB, int Sc, int64_t lo, int k,
     int32_t *__restrict__ idx, const void *__restrict__ q, const void *__restrict__ kc,
     const void *__restrict__ vc, int Hq, int Hkv, int64_t cap, float scale_log2,
     int win_sinks, int64_t win_local0, int n_win, int win_rows, float *__restrict__ part_o,
@@ -59,18 +60,19 @@ __device__ __forceinline__ void emit_attend_body(
     ga.run_block(kc, vc, head_row0, len, [&](int r) { return sel[r]; });
   };
   if (c < Sc) {
-    const int2 pr = params[bh];
-    const int T = pr.x;
-    const int quota = pr.y;
     const int c0 = c * CPB;
     const int c1 = min(S, c0 + CPB);
     int len = 0;
     int32_t *out = idx + (int64_t)bh * k;
     const int nch = c1 - c0;
-    // Every chunk's stash words and counts are requested before any is compacted, and
-    // staged in LDS (indexed by chunk at run time without scratch memory).
+    // Every chunk's stash words are requested first and staged in LDS (indexed by chunk
+    // at run time without scratch memory).  While they are in flight the workgroup
+    // derives its head's threshold, tie quota and the counts before each of its chunks
+    // from the chunk histograms -- the same computation as the threshold kernel, done by
+    // every workgroup of the head, which saves a kernel and its dependent round trip.
     __shared__ uint32_t sw[kMaxCpb][LPT / 4][kScanThreads];
     __shared__ int4 smt[kMaxCpb];
+    int T, quota;
     {
       uint32_t wl[kMaxCpb][LPT / 4];
 #pragma unroll
@@ -80,7 +82,14 @@ __device__ __forceinline__ void emit_attend_body(
 #pragma unroll
         for (int i4 = 0; i4 < LPT / 4; ++i4) wl[i][i4] = sp[i4 * kScanThreads + t];
       }
-      if (t < kMaxCpb) smt[t] = meta[(int64_t)bh * S + (c0 + t < c1 ? c0 + t : c0)];
+      auto sink = [&](int cc, const int4 &m) {
+        if (cc >= c0 && cc < c1) smt[cc - c0] = m;
+      };
+      if (bins == 128)
+        head_threshold<128>(hist + (int64_t)bh * S * (128 + 16), S, C, CH, keff, T, quota, sink);
+      else
+        head_threshold<64>(hist + (int64_t)bh * S * (64 + 8), S, C, CH, keff, T, quota, sink);
+      if (c == 0 && t == 0) count[bh] = keff;
 #pragma unroll
       for (int i = 0; i < kMaxCpb; ++i)
 #pragma unroll
@@ -137,14 +146,15 @@ __device__ __forceinline__ void emit_attend_body(
 }
 
 #define HK_EMIT_ATTEND_PARAMS                                                                 \
-  const uint32_t *__restrict__ stash, const int4 *__restrict__ meta,                         \
-      const int2 *__restrict__ params, int S, int CPB, int Sc, int64_t lo, int k,            \
+  const uint32_t *__restrict__ stash, const uint32_t *__restrict__ hist, int bins, int64_t C, \
+      int keff, int32_t *__restrict__ count, int S, int CPB, int Sc, int64_t lo, int k,      \
       int32_t *__restrict__ idx, const void *__restrict__ q, const void *__restrict__ kc,    \
       const void *__restrict__ vc, int Hq, int Hkv, int64_t cap, float scale_log2,           \
       int win_sinks, int64_t win_local0, int n_win, int win_rows, float *__restrict__ part_o, \
       float *__restrict__ part_lse, int64_t rows
 #define HK_EMIT_ATTEND_ARGS                                                                   \
-  stash, meta, params, S, CPB, Sc, lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,          \
+  stash, hist, bins, C, keff, count, S, CPB, Sc, lo, k, idx, q, kc, vc, Hq, Hkv, cap,         \
+      scale_log2,                                                                             \
       win_sinks, win_local0, n_win, win_rows, part_o, part_lse, rows
 
 // bf16 (matrix cores): held to 168 VGPRs, three workgroups per CU.  fp32 (VALU) keeps
@@ -162,30 +172,30 @@ __global__ __launch_bounds__(kScanThreads) void emit_attend_f32_kernel(HK_EMIT_A
 #undef HK_EMIT_ATTEND_ARGS
 
 template <int LPT, bool BF16, int G>
-void fused_launch(const FusedPlan &p, const uint32_t *stash, const int4 *meta,
-                  const int2 *params, int k, int32_t *idx, const void *q, const void *kc,
+void fused_launch(const FusedPlan &p, const uint32_t *stash, const uint32_t *hist,
+                  int32_t *count, int k, int32_t *idx, const void *q, const void *kc,
                   const void *vc, int Hq, int Hkv, int64_t cap, float scale_log2, float *po,
                   float *pl, int64_t rows, hipStream_t st) {
   if constexpr (BF16)
     hipLaunchKernelGGL((emit_attend_bf16_kernel<LPT, G>), dim3(p.parts, p.r.BH),
-                       dim3(kScanThreads), 0, st, stash, meta, params, p.r.S, p.cpb, p.Sc,
-                       p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2, p.win_sinks,
-                       p.win_local0, p.n_win, p.win_rows, po, pl, rows);
+                       dim3(kScanThreads), 0, st, stash, hist, p.r.BINS, p.r.C, p.r.keff, count,
+                       p.r.S, p.cpb, p.Sc, p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,
+                       p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows);
   else
     hipLaunchKernelGGL((emit_attend_f32_kernel<LPT, G>), dim3(p.parts, p.r.BH),
-                       dim3(kScanThreads), 0, st, stash, meta, params, p.r.S, p.cpb, p.Sc,
-                       p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2, p.win_sinks,
-                       p.win_local0, p.n_win, p.win_rows, po, pl, rows);
+                       dim3(kScanThreads), 0, st, stash, hist, p.r.BINS, p.r.C, p.r.keff, count,
+                       p.r.S, p.cpb, p.Sc, p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,
+                       p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows);
 }
 
 template <int LPT, bool BF16>
-void fused_dispatch_g(const FusedPlan &p, const uint32_t *stash, const int4 *meta,
-                      const int2 *params, int k, int32_t *idx, const void *q, const void *kc,
+void fused_dispatch_g(const FusedPlan &p, const uint32_t *stash, const uint32_t *hist,
+                      int32_t *count, int k, int32_t *idx, const void *q, const void *kc,
                       const void *vc, int Hq, int Hkv, int64_t cap, float sl2, float *po,
                       float *pl, int64_t rows, hipStream_t st) {
 #define HK_FUSED_CASE(GG)                                                                   \
   case GG:                                                                                  \
-    fused_launch<LPT, BF16, GG>(p, stash, meta, params, k, idx, q, kc, vc, Hq, Hkv, cap,   \
+    fused_launch<LPT, BF16, GG>(p, stash, hist, count, k, idx, q, kc, vc, Hq, Hkv, cap,    \
                                 sl2, po, pl, rows, st);                                     \
     break;
   switch (p.G) {
@@ -238,23 +248,28 @@ FusedPlan plan_fused(int bits, int B, int Hq, int Hkv, int64_t n_ctx, int n_sink
 
 hipError_t launch_fused_attend(const FusedPlan &p, const void *q, const void *kc,
                                const void *vc, int dtype, int B, int Hq, int Hkv, int64_t cap,
-                               float scale, int k, int32_t *idx, float *o, float *lse, void *ws,
-                               hipStream_t st) {
+                               float scale, int k, int32_t *idx, int32_t *count, float *o,
+                               float *lse, void *ws, hipStream_t st) {
   const int64_t rows = (int64_t)B * Hq;
   if (rows == 0) return hipSuccess;
+  // Without candidate chunks no workgroup derives the threshold: the threshold kernel
+  // writes the counts (k_eff = 0) instead.
+  if (p.Sc == 0) {
+    hipError_t e = launch_topk_threshold(p.r, count, ws, st);
+    if (e != hipSuccess) return e;
+  }
   uint8_t *w8 = static_cast<uint8_t *>(ws);
   float *po = reinterpret_cast<float *>(w8 + p.off_o);
   float *pl = reinterpret_cast<float *>(w8 + p.off_lse);
   if (p.parts > 0) {
     const uint32_t *stash = reinterpret_cast<const uint32_t *>(w8 + p.r.off_stash);
-    const int4 *meta = reinterpret_cast<const int4 *>(w8 + p.r.off_meta);
-    const int2 *params = reinterpret_cast<const int2 *>(w8 + p.r.off_params);
+    const uint32_t *hist = reinterpret_cast<const uint32_t *>(w8 + p.r.off_hist);
     const float sl2 = scale * kLog2e;
     const bool bf = dtype == HK_BF16;
 #define HK_LPT(L)                                                                            \
-  if (bf) fused_dispatch_g<L, true>(p, stash, meta, params, k, idx, q, kc, vc, Hq, Hkv, cap, \
+  if (bf) fused_dispatch_g<L, true>(p, stash, hist, count, k, idx, q, kc, vc, Hq, Hkv, cap,  \
                                     sl2, po, pl, rows, st);                                  \
-  else fused_dispatch_g<L, false>(p, stash, meta, params, k, idx, q, kc, vc, Hq, Hkv, cap,   \
+  else fused_dispatch_g<L, false>(p, stash, hist, count, k, idx, q, kc, vc, Hq, Hkv, cap,    \
                                   sl2, po, pl, rows, st);
     if (p.r.lpt == 8) { HK_LPT(8) }
     else { HK_LPT(4) }

@@ -100,8 +100,8 @@ FusedPlan plan_fused(int bits, int B, int Hq, int Hkv, int64_t n_ctx, int n_sink
                      int k);
 hipError_t launch_fused_attend(const FusedPlan &p, const void *q, const void *kc,
                                const void *vc, int dtype, int B, int Hq, int Hkv, int64_t cap,
-                               float scale, int k, int32_t *idx, float *o, float *lse, void *ws,
-                               hipStream_t st);
+                               float scale, int k, int32_t *idx, int32_t *count, float *o,
+                               float *lse, void *ws, hipStream_t st);
 
 // ---------------------------------------------------------------- encoders
 hipError_t launch_encode_keys(const hk_hash &h, const void *k, int B, int Hkv, int64_t cap,

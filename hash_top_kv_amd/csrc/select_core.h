@@ -132,6 +132,173 @@ __device__ __forceinline__ void emit_chunks(Word word, Meta meta, int nch, int T
   }
 }
 
+// Threads of a workgroup that computes a head threshold.
+constexpr int kThrThreads = 256;
+
+template <int K>
+__device__ __forceinline__ void load_u32x(const uint32_t *p, uint32_t (&x)[K]) {
+#pragma unroll
+  for (int i = 0; i < K / 4; ++i) {
+    const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+    x[4 * i] = v.x;
+    x[4 * i + 1] = v.y;
+    x[4 * i + 2] = v.z;
+    x[4 * i + 3] = v.w;
+  }
+}
+
+// Sum of K values over the workgroup: per-wavefront transposed sums, then LDS.
+// Returns the total of value i in thread i < K (others: undefined).  red holds
+// kThrThreads / 64 * 16 entries.
+template <int K>
+__device__ __forceinline__ uint32_t block_sum_k(uint32_t (&x)[K], uint32_t *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t r = wave_transpose_sum<K>(x);
+  if (lane < K) red[wave * 16 + bitrev_k<K>(lane)] = r;
+  __syncthreads();
+  uint32_t t = 0;
+  if ((int)threadIdx.x < K) {
+#pragma unroll
+    for (int w = 0; w < kThrThreads / 64; ++w) t += red[w * 16 + threadIdx.x];
+  }
+  __syncthreads();
+  return t;
+}
+
+// The threshold of one head, computed by one workgroup of kThrThreads threads, one thread
+// per chunk (tiles of kThrThreads chunks).  A two-level radix select over the chunk
+// histograms hb[S][BINS + BINS/8]:
+//   1. superbin totals over all chunks -> the superbin holding T (or T = BINS when the
+//      histogrammed distances hold fewer than k_eff candidates);
+//   2. that superbin's 8 bins, totalled over the chunks -> T and the tie quota;
+//   3. per chunk, #(D < T) (its superbins below T's plus its bins of T's superbin below
+//      T) and #(D == T), then an exclusive prefix of both over chunks: sink(c, meta) is
+//      called by the thread of chunk c with meta = (below T before c, at T before c,
+//      below T in c, at T in c).
+// T = -1 when k_eff = 0.  Every thread returns T and the tie quota.  For up to
+// kThrThreads chunks per head every value is read once and kept in registers.
+template <int BINS, class Sink>
+__device__ __forceinline__ void head_threshold(const uint32_t *__restrict__ hb, int S, int64_t C,
+                                               int CH, int keff, int &T_out, int &quota_out,
+                                               Sink sink) {
+  constexpr int NSB = BINS / 8;                // 16 or 8 superbins
+  constexpr int ROW = BINS + NSB;
+  constexpr int NT = kThrThreads;
+  __shared__ uint32_t red[NT / 64 * 16];
+  __shared__ uint32_t tot[16];
+  __shared__ uint32_t scan_lds[2][NT / 64];
+  __shared__ int sh[4];                        // T, quota, superbin of T, count below it
+  const int tid = threadIdx.x;
+  auto row = [&](int c) { return hb + (int64_t)(c < S ? c : S - 1) * ROW; };
+
+  uint32_t sb0[NSB], bb0[8];                   // the first tile's values, kept
+  if (keff > 0) {
+    // 1. superbin totals
+    uint32_t acc[NSB];
+#pragma unroll
+    for (int i = 0; i < NSB; ++i) acc[i] = 0u;
+    for (int c0 = 0; c0 < S; c0 += NT) {
+      uint32_t x[NSB];
+      load_u32x<NSB>(row(c0 + tid) + BINS, x);
+      const bool ok = c0 + tid < S;
+#pragma unroll
+      for (int i = 0; i < NSB; ++i) {
+        x[i] = ok ? x[i] : 0u;
+        acc[i] += x[i];
+        if (c0 == 0) sb0[i] = x[i];
+      }
+    }
+    const uint32_t st = block_sum_k<NSB>(acc, red);
+    if (tid < NSB) tot[tid] = st;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t below = 0;
+      int s = 0;
+      while (s < NSB && below + tot[s] < (uint32_t)keff) below += tot[s++];
+      sh[2] = s;                               // NSB: T = BINS
+      sh[3] = (int)below;
+    }
+    __syncthreads();
+    const int Ts = sh[2];
+    if (Ts < NSB) {
+      // 2. the 8 bins of superbin Ts
+      uint32_t bacc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bacc[i] = 0u;
+      for (int c0 = 0; c0 < S; c0 += NT) {
+        uint32_t x[8];
+        load_u32x<8>(row(c0 + tid) + 8 * Ts, x);
+        const bool ok = c0 + tid < S;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          x[i] = ok ? x[i] : 0u;
+          bacc[i] += x[i];
+          if (c0 == 0) bb0[i] = x[i];
+        }
+      }
+      const uint32_t bt = block_sum_k<8>(bacc, red);
+      if (tid < 8) tot[tid] = bt;
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t below = (uint32_t)sh[3];
+        int b = 0;
+        while (below + tot[b] < (uint32_t)keff) below += tot[b++];   // stops at b < 8
+        sh[0] = 8 * Ts + b;
+        sh[1] = keff - (int)below;
+      }
+    } else if (tid == 0) {
+      sh[0] = BINS;
+      sh[1] = keff - sh[3];
+    }
+  } else if (tid == 0) {
+    sh[0] = -1;
+    sh[1] = 0;
+  }
+  __syncthreads();
+  const int T = sh[0];
+  const int quota = sh[1];
+  // 3. per-chunk counts and their prefix over chunks
+  uint32_t carry_lt = 0, carry_eq = 0;
+  for (int c0 = 0; c0 < S && T >= 0; c0 += NT) {
+    const int c = c0 + tid;
+    const int Ts = T >> 3;
+    uint32_t sbv[NSB], bbv[8];
+    if (c0 == 0) {
+#pragma unroll
+      for (int i = 0; i < NSB; ++i) sbv[i] = sb0[i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bbv[i] = bb0[i];
+    } else {
+      load_u32x<NSB>(row(c) + BINS, sbv);
+      if (T < BINS) load_u32x<8>(row(c) + 8 * Ts, bbv);
+    }
+    uint32_t lt = 0, eq = 0;
+    if (c < S) {
+#pragma unroll
+      for (int i = 0; i < NSB; ++i) lt += (i < Ts) ? sbv[i] : 0u;
+      if (T < BINS) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          lt += (8 * Ts + i < T) ? bbv[i] : 0u;
+          eq += (8 * Ts + i == T) ? bbv[i] : 0u;
+        }
+      } else {                                 // distance BINS is not in the histogram
+        const int64_t n = C - (int64_t)c * CH;
+        eq = (uint32_t)(n < CH ? n : CH) - lt;
+      }
+    }
+    uint32_t tl, te;
+    const uint32_t lt_ex = block_excl_scan_u32<NT>(lt, scan_lds[0], tl);
+    const uint32_t eq_ex = block_excl_scan_u32<NT>(eq, scan_lds[1], te);
+    if (c < S)
+      sink(c, make_int4((int)(carry_lt + lt_ex), (int)(carry_eq + eq_ex), (int)lt, (int)eq));
+    carry_lt += tl;
+    carry_eq += te;
+  }
+  T_out = T;
+  quota_out = quota;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wavefront: shifts within rows of 16 lanes,
 // then the row totals broadcast to the following rows (DPP row_shr, row_bcast:15/31).
 __device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
