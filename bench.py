@@ -432,6 +432,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prefill", action="store_true", help="also time the key encode of the whole cache")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step")
     ap.add_argument("--qheads", action="store_true",
                     help="time the per-query-head selection variant of the step instead")
     ap.add_argument("--exact", action="store_true",
@@ -491,6 +493,37 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_step = e0.elapsed_time(e1) / args.steps
 
+    # The same steps replayed from a HIP graph: one graph holds one step per input
+    # replica (the replicas rotate as in the eager loop), captured after the eager
+    # timing on a side stream of default priority.
+    graph = None
+    if not args.no_graph:
+        R = len(ctx.get("Qs", ctx.get("reps", [None])))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(R):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(R):
+                step(i)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // R)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        graph = {"us_per_step": round(a.elapsed_time(b) / (reps * R) * 1e3, 3),
+                 "steps": reps * R, "steps_per_graph": R}
+        check()
+
     kern = {}
     if not args.no_kernel_timing:
         # Each part of the step with an event pair around it inside the step loop (the
@@ -542,7 +575,7 @@ def main():
            "dtype": "u32+" + ("f32" if info.get("kv_dtype") == "f32" else "bf16"),
            "data": "synthetic",
            "config": info, "roofline": roofline, "kernels": kern,
-           "wall_ms_timed_region": round(wall_ms, 3)}
+           "hip_graph": graph, "wall_ms_timed_region": round(wall_ms, 3)}
     if args.prefill and args.workload != 2:
         out["prefill"] = time_prefill(torch, hk, ctx, 10)
     if args.qheads and args.workload != 2:

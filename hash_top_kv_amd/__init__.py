@@ -180,8 +180,8 @@ def encode_query(h: Hash, q: torch.Tensor, Hkv: int, qcodes: torch.Tensor | None
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A zero-filled device workspace (the calls need zeros on first use and leave their
-    counters zero)."""
+    """A device workspace of nbytes (at least 1).  The calls do not depend on its
+    contents on entry; it is zero-filled only so that padding bytes are deterministic."""
     return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
