@@ -525,16 +525,25 @@ def main():
         check()
 
     kern = {}
+    pct = None
     if not args.no_kernel_timing:
         # Each part of the step with an event pair around it inside the step loop (the
-        # pair adds its own overhead, so these figures are upper bounds).
+        # pair adds its own overhead, so these figures are upper bounds), and the whole
+        # step between its own pair, for the spread of step times.
         timers = [Timer(torch, args.steps) for _ in parts]
+        whole = Timer(torch, args.steps)
         for i in range(args.steps):
+            whole.start()
             for (name, fn, _), t in zip(parts, timers):
                 t.start()
                 fn(i)
                 t.stop()
+            whole.stop()
         torch.cuda.synchronize()
+        d = np.array([a.elapsed_time(b) for a, b in whole.ev[:whole.i]]) * 1e3
+        pct = {"p10": round(float(np.percentile(d, 10)), 3), "p50": round(float(np.median(d)), 3),
+               "p90": round(float(np.percentile(d, 90)), 3),
+               "note": "one event pair per step, with the part timers inside"}
         for (name, fn, nbytes), t in zip(parts, timers):
             ms = t.mean_ms()
             ent = {"us_in_step": round(ms * 1e3, 3)}
@@ -575,7 +584,8 @@ def main():
            "dtype": "u32+" + ("f32" if info.get("kv_dtype") == "f32" else "bf16"),
            "data": "synthetic",
            "config": info, "roofline": roofline, "kernels": kern,
-           "hip_graph": graph, "wall_ms_timed_region": round(wall_ms, 3)}
+           "step_us_spread": pct, "hip_graph": graph,
+           "wall_ms_timed_region": round(wall_ms, 3)}
     if args.prefill and args.workload != 2:
         out["prefill"] = time_prefill(torch, hk, ctx, 10)
     if args.qheads and args.workload != 2:
