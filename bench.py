@@ -527,23 +527,26 @@ def main():
     kern = {}
     pct = None
     if not args.no_kernel_timing:
-        # Each part of the step with an event pair around it inside the step loop (the
-        # pair adds its own overhead, so these figures are upper bounds), and the whole
-        # step between its own pair, for the spread of step times.
-        timers = [Timer(torch, args.steps) for _ in parts]
+        # The whole step between its own event pair, for the spread of step times; then
+        # each part of the step with an event pair around it inside the step loop (the
+        # pairs add their own overhead, so these figures are upper bounds).
         whole = Timer(torch, args.steps)
         for i in range(args.steps):
             whole.start()
-            for (name, fn, _), t in zip(parts, timers):
-                t.start()
-                fn(i)
-                t.stop()
+            step(i)
             whole.stop()
         torch.cuda.synchronize()
         d = np.array([a.elapsed_time(b) for a, b in whole.ev[:whole.i]]) * 1e3
         pct = {"p10": round(float(np.percentile(d, 10)), 3), "p50": round(float(np.median(d)), 3),
                "p90": round(float(np.percentile(d, 90)), 3),
-               "note": "one event pair per step, with the part timers inside"}
+               "note": "one event pair around each step (the pair adds its own overhead)"}
+        timers = [Timer(torch, args.steps) for _ in parts]
+        for i in range(args.steps):
+            for (name, fn, _), t in zip(parts, timers):
+                t.start()
+                fn(i)
+                t.stop()
+        torch.cuda.synchronize()
         for (name, fn, nbytes), t in zip(parts, timers):
             ms = t.mean_ms()
             ent = {"us_in_step": round(ms * 1e3, 3)}
