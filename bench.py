@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--hash i]
                     [--replicas R] [--no-cpu] [--prefill] [--exact] [--evict]
-                    [--unfused | --qheads]
+                    [--sign] [--unfused | --qheads]
 
 Default workload: retrieval at 512K tokens -- 8 KV heads x 524,288 cached 128-bit codes
 (uniform random bits plus 1% planted near neighbours of the query code), top-1024 per
@@ -176,14 +176,14 @@ def build_full_case(args, torch, hk, synth):
     whole step after the keys were encoded), or with --unfused the separate calls."""
     from hash_top_kv_amd.step import DecodeStep, QHeadStep
     wl = synth.WORKLOADS[args.workload]
-    spec = wl.hashes[args.hash]
+    spec = synth.HashSpec("sign", 128) if args.sign else wl.hashes[args.hash]
     R = args.replicas
     kv = synth.make_kv(wl)
     K = synth.to_device(kv["K"], wl.dtype)
     V = synth.to_device(kv["V"], wl.dtype)
     del kv
     hnp = synth.make_hash(wl, spec, args.hash)
-    h = hk.Hash(spec.kind, spec.bits, **synth.hash_to_device(hnp))
+    h = hk.Hash(spec.kind, spec.bits, dtype=K.dtype, **synth.hash_to_device(hnp))
     codes = torch.empty((wl.B, wl.Hkv, wl.N, spec.words), dtype=torch.int32, device="cuda")
     hk.encode_keys(h, K, codes)
     torch.cuda.synchronize()
@@ -296,8 +296,11 @@ def time_prefill(torch, hk, ctx, steps):
     torch.cuda.synchronize()
     ms = t.mean_ms()
     M = wl.B * wl.Hkv * wl.N
-    flops = 2 * M * (128 * 256 + 256 * spec.bits) if spec.kind == "mlp" else 2 * M * 128 * spec.bits
     bytes_ = M * 128 * 2 + M * spec.bits // 8
+    if spec.kind == "sign":                    # no product: bound by HBM
+        return {"kernel": "encode_keys_sign", "rows": M, "us": ms * 1e3,
+                "hbm_gbs": bytes_ / ms / 1e6, "frac_of_peak": bytes_ / ms / 1e6 / HBM_PEAK_GBS}
+    flops = 2 * M * (128 * 256 + 256 * spec.bits) if spec.kind == "mlp" else 2 * M * 128 * spec.bits
     return {"kernel": f"encode_keys_mfma ({spec.kind}-{spec.bits})", "rows": M, "us": ms * 1e3,
             "tflops": flops / ms / 1e9, "mfma_frac": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
             "hbm_gbs": bytes_ / ms / 1e6}
@@ -434,6 +437,9 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the step")
+    ap.add_argument("--sign", action="store_true",
+                    help="use sign codes of the keys themselves (128 bits) instead of the "
+                         "workload's hash")
     ap.add_argument("--qheads", action="store_true",
                     help="time the per-query-head selection variant of the step instead")
     ap.add_argument("--exact", action="store_true",

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libhk.so")
 
 HK_OK, HK_ERR_INVALID_ARGUMENT, HK_ERR_UNSUPPORTED, HK_ERR_WORKSPACE_TOO_SMALL, HK_ERR_HIP = range(5)
 HK_F32, HK_BF16 = 0, 1
-HK_HASH_LSH, HK_HASH_MLP = 0, 1
+HK_HASH_LSH, HK_HASH_MLP, HK_HASH_SIGN = 0, 1, 2
 
 
 class HkError(RuntimeError):
@@ -127,23 +127,33 @@ def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
 
 
 class Hash:
-    """Hash parameters on the device: LSH (R [bits, d]) or MLP (W1 [256, d], W2 [bits,
-    256], optional b1, b2).  All tensors share one dtype (float32 or bfloat16)."""
+    """Hash parameters on the device: LSH (R [bits, d]), MLP (W1 [256, d], W2 [bits,
+    256], optional b1, b2), or SIGN (no parameters: bit j is the sign of element j, bits
+    = d = 128; give its element type as dtype).  All tensors share one dtype (float32 or
+    bfloat16)."""
 
-    def __init__(self, kind: str, bits: int, R=None, W1=None, W2=None, b1=None, b2=None):
+    def __init__(self, kind: str, bits: int, R=None, W1=None, W2=None, b1=None, b2=None,
+                 dtype=None):
         self.kind = kind
         self.bits = int(bits)
         self.R, self.W1, self.W2, self.b1, self.b2 = R, W1, W2, b1, b2
-        ref = R if kind == "lsh" else W1
-        if ref is None:
-            raise ValueError("missing hash weights")
-        self.dtype = ref.dtype
+        if kind == "sign":
+            if dtype is None:
+                raise ValueError("a sign hash needs its element type (dtype)")
+            self.dtype = dtype
+            code = HK_HASH_SIGN
+        else:
+            ref = R if kind == "lsh" else W1
+            if ref is None:
+                raise ValueError("missing hash weights")
+            self.dtype = ref.dtype
+            code = HK_HASH_LSH if kind == "lsh" else HK_HASH_MLP
         for name in ("R", "W1", "W2", "b1", "b2"):
             t = getattr(self, name)
             if t is not None:
                 _need(t, name, dtype=self.dtype)
-        self._s = _Hash(HK_HASH_LSH if kind == "lsh" else HK_HASH_MLP, _dtype_code(ref), 128,
-                        self.bits, 0 if kind == "lsh" else 256,
+        dcode = HK_BF16 if self.dtype == torch.bfloat16 else HK_F32
+        self._s = _Hash(code, dcode, 128, self.bits, 256 if kind == "mlp" else 0,
                         _ptr(R), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2))
 
     @property

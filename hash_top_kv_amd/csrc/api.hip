@@ -27,6 +27,8 @@ hk_status check_hash(const hk_hash *h) {
     if (h->hidden != kHidden) return HK_ERR_UNSUPPORTED;
     if (!h->W1 || !h->W2) return HK_ERR_INVALID_ARGUMENT;
     if (!aligned(h->W1, 16) || !aligned(h->W2, 16)) return HK_ERR_UNSUPPORTED;
+  } else if (h->kind == HK_HASH_SIGN) {
+    if (h->bits != kHeadDim) return HK_ERR_UNSUPPORTED;
   } else {
     return HK_ERR_UNSUPPORTED;
   }

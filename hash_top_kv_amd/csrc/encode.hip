@@ -431,6 +431,64 @@ __global__ __launch_bounds__(1024) void encode_query_mfma_kernel(HashPtrs hp,
   }
 }
 
+// ------------------------------------------------------------------ sign codes
+// SIGN hash (Self-Indexing KVCache: Abstract, sign-based 1-bit keys): bit j = [x_j > 0],
+// no projection.  Keys: 16 lanes per key, lane l turns elements 8l .. 8l+7 into byte l
+// of the 16-byte code (bits 8l .. 8l+7, least significant first), so a wavefront reads
+// 4 whole rows and writes 4 whole codes.  Bound by HBM bandwidth.
+template <bool BF16>
+__global__ __launch_bounds__(256) void encode_keys_sign_kernel(const void *__restrict__ k,
+                                                               int64_t nt, int64_t cap,
+                                                               int64_t t0, int64_t total,
+                                                               uint8_t *__restrict__ codes) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t key = gid >> 4;
+  const int l = (int)(gid & 15);
+  if (key >= total) return;
+  const int64_t bh = key / nt;
+  const int64_t row = bh * cap + t0 + (key - bh * nt);
+  float x[8];
+  if constexpr (BF16) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(k) + row * kHeadDim + 8 * l);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(w[e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(k) + row * kHeadDim + 8 * l);
+    const float4 a = p[0], b = p[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+  uint32_t byte = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) byte |= (x[e] > 0.f ? 1u : 0u) << e;
+  codes[row * 16 + l] = (uint8_t)byte;
+}
+
+// Queries: one workgroup of 128 threads per (b, KV head); thread j takes element j of
+// the group-mean query (fp32, as the other query encoders), and each wavefront's ballot
+// is 64 bits of the code.
+template <bool BF16>
+__global__ __launch_bounds__(128) void encode_query_sign_kernel(const void *__restrict__ q,
+                                                                int Hq, int Hkv,
+                                                                uint32_t *__restrict__ out) {
+  const int64_t r = blockIdx.x;
+  const int j = threadIdx.x;
+  const int64_t b = r / Hkv, hg = r - b * Hkv;
+  const int G = Hq / Hkv;
+  float acc = 0.f;
+  for (int g = 0; g < G; ++g) acc += elem<BF16>(q, (size_t)((b * Hq + hg * G + g) * kHeadDim + j));
+  acc = acc / (float)G;
+  const uint64_t m = __ballot(acc > 0.f);
+  if ((j & 63) == 0) {
+    out[r * 4 + 2 * (j >> 6)] = (uint32_t)m;
+    out[r * 4 + 2 * (j >> 6) + 1] = (uint32_t)(m >> 32);
+  }
+}
+
 // ------------------------------------------------------------------ MFMA kernel
 template <bool MLP, int BITS> struct EncLayout {
   static constexpr int JT = BITS / 32;                // 32-bit output tiles
@@ -637,6 +695,15 @@ hipError_t launch_encode_keys(const hk_hash &h, const void *k, int B, int Hkv, i
   const int64_t nt = t1 - t0;
   const int64_t total = (int64_t)B * Hkv * nt;
   if (total == 0) return hipSuccess;
+  if (h.kind == HK_HASH_SIGN) {
+    const dim3 grid((unsigned)((total * 16 + 255) / 256));
+    uint8_t *cb = reinterpret_cast<uint8_t *>(codes);
+    if (h.dtype == HK_BF16)
+      hipLaunchKernelGGL(encode_keys_sign_kernel<true>, grid, dim3(256), 0, st, k, nt, cap, t0, total, cb);
+    else
+      hipLaunchKernelGGL(encode_keys_sign_kernel<false>, grid, dim3(256), 0, st, k, nt, cap, t0, total, cb);
+    return hipGetLastError();
+  }
   if (h.dtype == HK_F32) return valu_dispatch<false>(h, k, total, nt, cap, t0, codes, st);
   const HashPtrs hp{h.R, h.W1, h.b1, h.W2, h.b2};
   const bool mlp = h.kind == HK_HASH_MLP;
@@ -655,6 +722,13 @@ hipError_t launch_encode_query(const hk_hash &h, const void *q, int B, int Hq, i
                                uint32_t *qcodes, hipStream_t st) {
   const int64_t rows = (int64_t)B * Hkv;
   if (rows == 0) return hipSuccess;
+  if (h.kind == HK_HASH_SIGN) {
+    if (h.dtype == HK_BF16)
+      hipLaunchKernelGGL(encode_query_sign_kernel<true>, dim3((unsigned)rows), dim3(128), 0, st, q, Hq, Hkv, qcodes);
+    else
+      hipLaunchKernelGGL(encode_query_sign_kernel<false>, dim3((unsigned)rows), dim3(128), 0, st, q, Hq, Hkv, qcodes);
+    return hipGetLastError();
+  }
   const HashPtrs hp{h.R, h.W1, h.b1, h.W2, h.b2};
   const bool mlp = h.kind == HK_HASH_MLP, bf = h.dtype == HK_BF16;
   if (bf) {

@@ -53,7 +53,7 @@ typedef enum hk_status {
 
 typedef enum hk_dtype { HK_F32 = 0, HK_BF16 = 1 } hk_dtype;
 
-typedef enum hk_hash_kind { HK_HASH_LSH = 0, HK_HASH_MLP = 1 } hk_hash_kind;
+typedef enum hk_hash_kind { HK_HASH_LSH = 0, HK_HASH_MLP = 1, HK_HASH_SIGN = 2 } hk_hash_kind;
 
 /* Hash parameters: a host struct that points at caller-owned device tensors.
  * LSH  (HashEvict: Abstract): y = R x, R [bits][d] row-major, row j gives bit j.
@@ -61,8 +61,11 @@ typedef enum hk_hash_kind { HK_HASH_LSH = 0, HK_HASH_MLP = 1 } hk_hash_kind;
  *      W1 [hidden][d], W2 [bits][hidden] ([out][in], row-major), optional biases
  *      b1 [hidden] and b2 [bits] (NULL = zero), GELU in its exact erf form, and rho the
  *      rounding of the hidden activation to bf16 (nearest-even) when dtype is HK_BF16.
+ * SIGN (Self-Indexing KVCache: Abstract, "sign-based 1-bit" keys): y = x, the identity
+ *      projection; bits = d = 128 and no weight tensors (R, W1, W2, b1, b2 are ignored).
  * All tensors have element type `dtype`, which is also the element type of the keys and
- * queries the hash encodes.  d must be 128, bits 64 or 128, hidden 256 (MLP) or 0. */
+ * queries the hash encodes.  d must be 128, bits 64 or 128 (128 for SIGN), hidden 256
+ * (MLP) or 0. */
 typedef struct hk_hash {
   int32_t kind;    /* hk_hash_kind */
   int32_t dtype;   /* hk_dtype */

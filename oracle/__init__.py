@@ -112,7 +112,7 @@ def prepare_hash(h: dict) -> dict:
         out["W2"] = widen(h["W2"], dt)
         out["b1"] = widen(h["b1"], dt) if h.get("b1") is not None else None
         out["b2"] = widen(h["b2"], dt) if h.get("b2") is not None else None
-    else:
+    elif h["kind"] != "sign":
         raise ValueError(h["kind"])
     return out
 
@@ -123,8 +123,11 @@ def project(x, hp: dict) -> np.ndarray:
     LSH (HashEvict: Abstract, "binarized Gaussian projections"): y = R x.
     MLP (Spotlight Attention: Approach, "sign of an MLP output"): y = W2 rho(GELU(W1 x
     + b1)) + b2, with rho the bf16 rounding of the hidden layer when it is bf16.
+    SIGN (Self-Indexing KVCache: Abstract, "sign-based 1-bit" keys): y = x.
     """
     x = np.asarray(x, dtype=np.float64)
+    if hp["kind"] == "sign":
+        return x.copy()
     if hp["kind"] == "lsh":
         return x @ hp["R"].T
     a = x @ hp["W1"].T

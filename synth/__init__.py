@@ -201,8 +201,8 @@ def make_hash(wl: Workload, spec: HashSpec, index: int = 0) -> dict:
     """Random hash parameters in the workload dtype.
 
     LSH: R [bits, d] ~ N(0, 1).  MLP: W1 [hidden, d] ~ N(0, 1/d), W2 [bits, hidden]
-    ~ N(0, 1/hidden), no biases.  Values are returned in storage form (float32 or
-    bf16 bits) together with the spec.
+    ~ N(0, 1/hidden), no biases.  SIGN: none (bits = d).  Values are returned in storage
+    form (float32 or bf16 bits) together with the spec.
     """
     rng = rng_for(wl.wid, T_HASH, index)
     out = {"kind": spec.kind, "bits": spec.bits, "hidden": spec.hidden, "dtype": wl.dtype}
@@ -214,7 +214,7 @@ def make_hash(wl: Workload, spec: HashSpec, index: int = 0) -> dict:
         w2 = (rng.standard_normal((spec.bits, spec.hidden)) / math.sqrt(spec.hidden)).astype(np.float32)
         out["W1"] = _store(w1, wl.dtype)
         out["W2"] = _store(w2, wl.dtype)
-    else:
+    elif spec.kind != "sign":              # the identity: no parameters
         raise ValueError(spec.kind)
     return out
 

@@ -102,6 +102,12 @@ def test_host_validation_without_gpu(hk):
         == hk.HK_ERR_UNSUPPORTED
     assert L.hk_sparse_decode(dummy, odd, dummy, hk.HK_BF16, 1, 8, 4, 128, 10, dummy, 4, P, 4, f,
                               dummy, dummy, dummy, 1 << 30, P) == hk.HK_ERR_UNSUPPORTED
+    # sign hash: 128 bits only, no weights needed
+    hs = hk._Hash(hk.HK_HASH_SIGN, hk.HK_BF16, 128, 64, 0, P, P, P, P, P)
+    assert L.hk_encode_keys(ctypes.byref(hs), dummy, 1, 1, 10, 0, 10, dummy, P) == hk.HK_ERR_UNSUPPORTED
+    hs = hk._Hash(hk.HK_HASH_SIGN, hk.HK_BF16, 128, 128, 0, P, P, P, P, P)
+    assert L.hk_encode_keys(ctypes.byref(hs), dummy, 1, 1, 10, 5, 5, dummy, P) == hk.HK_OK
+    assert L.hk_encode_query(ctypes.byref(hs), dummy, 1, 30, 4, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
     # eviction: bad width / sizes, missing buffers, small workspace, misaligned rows
     assert L.hk_evict_select(P, P, 96, 1, 1, 10, 10, 0, 0, P, P, 0, P) == hk.HK_ERR_UNSUPPORTED
     assert L.hk_evict_select(P, P, 128, 1, 1, 10, 11, 0, 0, P, P, 0, P) == hk.HK_ERR_INVALID_ARGUMENT

@@ -441,3 +441,47 @@ def test_retrieve_attend_matches_oracle_and_unfused(case):
         l2 = l2.cpu().numpy()
         fin = np.isfinite(lse)
         assert np.array_equal(fin, np.isfinite(l2)) and np.allclose(l2[fin], lse[fin], atol=tol, rtol=0)
+
+
+# ----------------------------------------------------------------- sign codes
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sign_codes_keys_queries_and_step(dtype):
+    """SIGN hash (bit j = sign of element j): key codes bit-exact, query codes of the
+    group mean within the near-zero exemption, and a whole decode step against the
+    oracle."""
+    B, Hkv, G, N = 2, 2, 3, 5000
+    wl = synth.scaled(synth.WORKLOADS[1], B=B, Hkv=Hkv, Hq=Hkv * G, N=N, dtype=dtype,
+                      hashes=(synth.HashSpec("sign", 128),), k=100, n_sink=4, n_local=64)
+    kv = synth.make_kv(wl)
+    qn = synth.make_q(wl)
+    K, V = synth.to_device(kv["K"], dtype), synth.to_device(kv["V"], dtype)
+    h = hk.Hash("sign", 128, dtype=K.dtype)
+    hp = oracle.prepare_hash(synth.make_hash(wl, wl.hashes[0]))
+    codes = torch.full((B, Hkv, N, 4), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    hk.encode_keys(h, K, codes, 3, N)
+    Q = synth.to_device(qn, dtype)
+    qc = hk.encode_query(h, Q, Hkv)
+    torch.cuda.synchronize()
+    got = np_u32(codes)
+    for b in range(B):
+        for g in range(Hkv):
+            ref, _ = oracle.encode(oracle.widen(kv["K"][b, g, 3:], dtype), hp)
+            assert np.array_equal(got[b, g, 3:], ref)
+            assert np.all(got[b, g, :3] == 0x5A5A5A5A)
+    ref_q, yq = oracle.encode_query(oracle.widen(qn, dtype), hp, Hkv)
+    compare_codes(np_u32(qc), ref_q, yq)
+    hk.encode_keys(h, K, codes, 0, 3)
+    from hash_top_kv_amd.step import DecodeStep
+    st = DecodeStep(K, V, codes, 128, N, 4, 64, wl.k, wl.Hq, h)
+    o, lse = st(Q)
+    torch.cuda.synchronize()
+    cc = np_u32(codes)
+    tol = 2e-2 if dtype == "bf16" else 1e-5
+    for b in range(B):
+        ref = oracle.decode_step(oracle.widen(qn[b], dtype), oracle.widen(kv["K"][b], dtype),
+                                 oracle.widen(kv["V"][b], dtype), cc[b], hp, N, 4, 64, wl.k,
+                                 qcodes=np_u32(qc)[b])
+        for g in range(Hkv):
+            assert np.array_equal(st.idx[b, g, :st.keff].cpu().numpy(), ref["idx"][g])
+        assert np.max(np.abs(o[b].cpu().numpy() - ref["o"])) <= tol
+        assert np.max(np.abs(lse[b].cpu().numpy() - ref["lse"])) <= tol

@@ -223,3 +223,20 @@ def test_widen_bf16_is_exact():
     got = oracle.widen(u, "bf16")
     want = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(got, want)
+
+
+def test_sign_hash_is_the_sign_of_each_element():
+    """SIGN codes (identity projection) against bit-by-bit signs, with zero, negative
+    zero and NaN giving 0, and against LSH with R = I."""
+    rng = np.random.default_rng(91)
+    x = rng.standard_normal((50, 128))
+    x[0, :5] = [0.0, -0.0, np.nan, 1e-30, -1e-30]
+    hp = oracle.prepare_hash({"kind": "sign", "bits": 128, "dtype": "f32"})
+    codes, y = oracle.encode(x, hp)
+    for r in range(50):
+        for j in range(128):
+            want = 1 if (x[r, j] == x[r, j] and x[r, j] > 0) else 0
+            assert (int(codes[r, j // 32]) >> (j % 32)) & 1 == want
+    lsh = oracle.prepare_hash({"kind": "lsh", "bits": 128, "dtype": "f32",
+                               "R": np.eye(128, dtype=np.float32)})
+    assert np.array_equal(oracle.encode(x[1:], lsh)[0], codes[1:])
