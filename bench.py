@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--hash i]
                     [--replicas R] [--no-cpu] [--prefill] [--exact] [--evict]
-                    [--sign] [--unfused | --qheads]
+                    [--sign] [--unfused | --qheads | --varlen]
 
 Default workload: retrieval at 512K tokens -- 8 KV heads x 524,288 cached 128-bit codes
 (uniform random bits plus 1% planted near neighbours of the query code), top-1024 per
@@ -174,7 +174,7 @@ def build_retrieval_case(args, torch, hk, synth):
 def build_full_case(args, torch, hk, synth):
     """Workloads 0, 1, 3, 4: hk_encode_query + hk_hamming_scan + hk_select_attend (the
     whole step after the keys were encoded), or with --unfused the separate calls."""
-    from hash_top_kv_amd.step import DecodeStep, QHeadStep
+    from hash_top_kv_amd.step import DecodeStep, QHeadStep, VarlenDecodeStep
     wl = synth.WORKLOADS[args.workload]
     spec = synth.HashSpec("sign", 128) if args.sign else wl.hashes[args.hash]
     R = args.replicas
@@ -197,6 +197,12 @@ def build_full_case(args, torch, hk, synth):
              for cs in code_sets]
     qsteps = ([QHeadStep(K, V, cs, spec.bits, wl.N, wl.n_sink, wl.n_local, wl.k, wl.Hq, h)
                for cs in code_sets] if args.qheads else [])
+    # Variable lengths: sequence b holds N - floor(b N / 2B) tokens (from N down to about
+    # N/2), the budget stays the workload's k.
+    lengths = [wl.N - (b * wl.N) // (2 * wl.B) for b in range(wl.B)]
+    ctx_len = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    vsteps = ([VarlenDecodeStep(K, V, cs, spec.bits, ctx_len, wl.N, wl.n_sink, wl.n_local, wl.k,
+                                wl.Hq, h) for cs in code_sets] if args.varlen else [])
     Qs = [synth.to_device(synth.make_q(wl, replica=r), wl.dtype) for r in range(R)]
 
     def st(i):
@@ -216,6 +222,9 @@ def build_full_case(args, torch, hk, synth):
 
     def qst(i):
         return qsteps[i % len(qsteps)]
+
+    def var_step(i):
+        vsteps[i % len(vsteps)](Qs[i % R])
 
     def q_enc(i):
         qst(i).encode(Qs[i % R])
@@ -245,9 +254,14 @@ def build_full_case(args, torch, hk, synth):
                      if args.unfused else
                      "hk_encode_query (per query head) + hk_retrieve_topk_qheads + "
                      "hk_sparse_decode_qheads + hk_sparse_decode (window) + hk_lse_merge"
-                     if args.qheads else "hk_encode_query + hk_hamming_scan + hk_select_attend")}
+                     if args.qheads else
+                     "hk_encode_query + hk_retrieve_attend_varlen (lengths " +
+                     ",".join(map(str, lengths)) + ")"
+                     if args.varlen else "hk_encode_query + hk_hamming_scan + hk_select_attend")}
     if args.unfused:
         parts = [("decode_step", unfused, None)]
+    elif args.varlen:
+        parts = [("encode_query+retrieve_attend_varlen", var_step, None)]
     elif args.qheads:
         parts = [("encode_query", q_enc, None),
                  ("retrieve_topk_qheads", q_ret, scan_bytes),
@@ -440,6 +454,8 @@ def main():
     ap.add_argument("--sign", action="store_true",
                     help="use sign codes of the keys themselves (128 bits) instead of the "
                          "workload's hash")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time the step for sequences of different lengths (N down to N/2)")
     ap.add_argument("--qheads", action="store_true",
                     help="time the per-query-head selection variant of the step instead")
     ap.add_argument("--exact", action="store_true",

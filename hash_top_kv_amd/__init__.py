@@ -52,6 +52,8 @@ _SIGNATURES = {
     "hk_retrieve_attend_workspace": (_SZ, [_I, _I, _I, _I, _I64, _I, _I, _I]),
     "hk_evict_workspace": (_SZ, [_I, _I, _I, _I64, _I, _I]),
     "hk_exact_topk_workspace": (_SZ, [_I, _I, _I64, _I, _I, _I]),
+    "hk_retrieve_attend_varlen": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _I64,
+                                       _I, _I, _I, _F, _P, _P, _P, _P, _P, _SZ, _P]),
     "hk_retrieve_topk_qheads": (_I, [_P, _P, _I, _I, _I, _I, _I64, _I64, _I, _I, _I, _P, _P, _P,
                                      _SZ, _P]),
     "hk_sparse_decode_qheads": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _I64, _P, _I, _F,
@@ -360,6 +362,39 @@ def retrieve_attend(codes, qcodes, bits, q, k, v, n_ctx, n_sink, n_local, topk, 
                                     B, Hq, Hkv, d, cap, n_ctx, n_sink, n_local, topk, float(scale),
                                     _ptr(idx), _ptr(count), _ptr(o), _ptr(lse), _ptr(ws),
                                     ws.numel(), _stream()), "hk_retrieve_attend")
+    return o, lse, idx, count
+
+
+def retrieve_attend_varlen(codes, qcodes, bits, q, k, v, ctx_len, max_ctx, n_sink, n_local, topk,
+                           scale=None, idx=None, count=None, o=None, lse=None, ws=None):
+    """hk_retrieve_attend_varlen: as retrieve_attend, with sequence b holding ctx_len[b]
+    tokens (int32 device tensor [B], each <= max_ctx)."""
+    _need(codes, "codes", dtype=torch.int32)
+    B, Hkv, cap, W = codes.shape
+    _need(qcodes, "qcodes", dtype=torch.int32, shape=(B, Hkv, W))
+    _need(ctx_len, "ctx_len", dtype=torch.int32, shape=(B,))
+    dt = _dtype_code(q)
+    _need(q, "q")
+    _need(k, "k", dtype=q.dtype)
+    _need(v, "v", dtype=q.dtype, shape=k.shape)
+    Hq, d = q.shape[1], q.shape[2]
+    if tuple(k.shape[:3]) != (B, Hkv, cap):
+        raise ValueError("k must be [B, Hkv, cap, d] like the codes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    wsb = retrieve_attend_workspace(bits, B, Hq, Hkv, max_ctx, n_sink, n_local, topk)
+    idx, count, ws = _topk_buffers(B, Hkv, topk, codes.device, idx, count, ws, wsb)
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(o, "o", dtype=torch.float32, shape=(B, Hq, d))
+    _need(lse, "lse", dtype=torch.float32, shape=(B, Hq))
+    _check(lib().hk_retrieve_attend_varlen(_ptr(codes), _ptr(qcodes), bits, _ptr(q), _ptr(k),
+                                           _ptr(v), dt, B, Hq, Hkv, d, cap, _ptr(ctx_len), max_ctx,
+                                           n_sink, n_local, topk, float(scale), _ptr(idx),
+                                           _ptr(count), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
+                                           _stream()), "hk_retrieve_attend_varlen")
     return o, lse, idx, count
 
 

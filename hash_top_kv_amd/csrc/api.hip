@@ -352,4 +352,36 @@ hk_status hk_sparse_decode_qheads(const void *q, const void *k, const void *v, i
                                        Hq / Hkv));
 }
 
+hk_status hk_retrieve_attend_varlen(const uint32_t *codes, const uint32_t *qcodes, int bits,
+                                    const void *q, const void *kc, const void *vc, int dtype,
+                                    int B, int Hq, int Hkv, int d, int64_t cap,
+                                    const int32_t *ctx_len, int64_t max_ctx, int n_sink,
+                                    int n_local, int topk, float scale, int32_t *idx,
+                                    int32_t *count, float *o, float *lse, void *ws,
+                                    size_t ws_bytes, void *stream) {
+  hk_status s = check_retrieve(bits, B, Hkv, cap, max_ctx, n_sink, n_local, topk);
+  if (s != HK_OK) return s;
+  if (dtype != HK_F32 && dtype != HK_BF16) return HK_ERR_UNSUPPORTED;
+  if (d != kHeadDim) return HK_ERR_UNSUPPORTED;
+  if (Hkv <= 0 || Hq < Hkv || Hq % Hkv != 0) return HK_ERR_INVALID_ARGUMENT;
+  if (Hq / Hkv > kMaxGroup) return HK_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq == 0) return HK_OK;
+  if (!ctx_len) return HK_ERR_INVALID_ARGUMENT;
+  const FusedPlan p = plan_fused(bits, B, Hq, Hkv, max_ctx, n_sink, n_local, topk);
+  if (!q || !count || !o || !lse || !ws) return HK_ERR_INVALID_ARGUMENT;
+  if (p.parts > 0 && (!kc || !vc)) return HK_ERR_INVALID_ARGUMENT;
+  if (p.r.S > 0 && (!codes || !qcodes)) return HK_ERR_INVALID_ARGUMENT;
+  if (p.r.keff > 0 && !idx) return HK_ERR_INVALID_ARGUMENT;
+  if (p.r.S > 0 && !aligned(codes, code_align(bits))) return HK_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16)) return HK_ERR_UNSUPPORTED;
+  if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
+  const hipStream_t st = as_stream(stream);
+  hipError_t e = launch_hamming_scan(p.r, codes, qcodes, cap, ws, st, ctx_len, Hkv, n_local,
+                                     max_ctx);
+  if (e == hipSuccess)
+    e = launch_fused_attend(p, q, kc, vc, dtype, B, Hq, Hkv, cap, scale, topk, idx, count, o, lse,
+                            ws, st, ctx_len);
+  return from_hip(e);
+}
+
 }  // extern "C"

@@ -36,7 +36,8 @@ __device__ __forceinline__ void emit_attend_body(
     int32_t *__restrict__ idx, const void *__restrict__ q, const void *__restrict__ kc,
     const void *__restrict__ vc, int Hq, int Hkv, int64_t cap, float scale_log2,
     int win_sinks, int64_t win_local0, int n_win, int win_rows, float *__restrict__ part_o,
-    float *__restrict__ part_lse, int64_t rows) {
+    float *__restrict__ part_lse, int64_t rows, const int32_t *__restrict__ ctx_len,
+    int64_t n_local, int64_t max_ctx) {
   constexpr int CH = kScanThreads * LPT;
   static_assert(CH <= kListMax, "a chunk's selection must fit the list");
   __shared__ int32_t sel[kListMax];
@@ -47,6 +48,19 @@ __device__ __forceinline__ void emit_attend_body(
   const int t = threadIdx.x;
   const int64_t row0 = (int64_t)b * Hq + (int64_t)hkv * G;
   const size_t head_row0 = (size_t)bh * (size_t)cap;
+  // Sequences of their own lengths: the head's candidates, chunks, budget and window
+  // follow its n_b; S stays the launch's chunk stride (sized for the longest).
+  int Sb = S;
+  if (ctx_len) {
+    int64_t n = ctx_len[b];
+    n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
+    C = head_candidates(ctx_len, b, max_ctx, lo, n_local);
+    Sb = (int)((C + CH - 1) / CH);
+    keff = (int)(k < C ? k : C);
+    win_sinks = (int)(lo < n ? lo : n);
+    win_local0 = (n - n_local) > lo ? (n - n_local) : lo;
+    n_win = win_sinks + (int)(n > win_local0 ? n - win_local0 : 0);
+  }
 
   // The query fragment is loaded after the chunks are compacted: its load then issues
   // with the first K/V rows and does not hold registers through the compaction.
@@ -61,7 +75,7 @@ __device__ __forceinline__ void emit_attend_body(
   };
   if (c < Sc) {
     const int c0 = c * CPB;
-    const int c1 = min(S, c0 + CPB);
+    const int c1 = min(Sb, c0 + CPB);
     int len = 0;
     int32_t *out = idx + (int64_t)bh * k;
     const int nch = c1 - c0;
@@ -86,9 +100,9 @@ __device__ __forceinline__ void emit_attend_body(
         if (cc >= c0 && cc < c1) smt[cc - c0] = m;
       };
       if (bins == 128)
-        head_threshold<128>(hist + (int64_t)bh * S * (128 + 16), S, C, CH, keff, T, quota, sink);
+        head_threshold<128>(hist + (int64_t)bh * S * (128 + 16), Sb, C, CH, keff, T, quota, sink);
       else
-        head_threshold<64>(hist + (int64_t)bh * S * (64 + 8), S, C, CH, keff, T, quota, sink);
+        head_threshold<64>(hist + (int64_t)bh * S * (64 + 8), Sb, C, CH, keff, T, quota, sink);
       if (c == 0 && t == 0) count[bh] = keff;
 #pragma unroll
       for (int i = 0; i < kMaxCpb; ++i)
@@ -151,11 +165,12 @@ __device__ __forceinline__ void emit_attend_body(
       int32_t *__restrict__ idx, const void *__restrict__ q, const void *__restrict__ kc,    \
       const void *__restrict__ vc, int Hq, int Hkv, int64_t cap, float scale_log2,           \
       int win_sinks, int64_t win_local0, int n_win, int win_rows, float *__restrict__ part_o, \
-      float *__restrict__ part_lse, int64_t rows
+      float *__restrict__ part_lse, int64_t rows, const int32_t *__restrict__ ctx_len,       \
+      int64_t n_local, int64_t max_ctx
 #define HK_EMIT_ATTEND_ARGS                                                                   \
   stash, hist, bins, C, keff, count, S, CPB, Sc, lo, k, idx, q, kc, vc, Hq, Hkv, cap,         \
-      scale_log2,                                                                             \
-      win_sinks, win_local0, n_win, win_rows, part_o, part_lse, rows
+      scale_log2, win_sinks, win_local0, n_win, win_rows, part_o, part_lse, rows, ctx_len,    \
+      n_local, max_ctx
 
 // bf16 (matrix cores): held to 168 VGPRs, three workgroups per CU.  fp32 (VALU) keeps
 // the compiler's choice: its accumulators would spill under that limit.
@@ -175,28 +190,30 @@ template <int LPT, bool BF16, int G>
 void fused_launch(const FusedPlan &p, const uint32_t *stash, const uint32_t *hist,
                   int32_t *count, int k, int32_t *idx, const void *q, const void *kc,
                   const void *vc, int Hq, int Hkv, int64_t cap, float scale_log2, float *po,
-                  float *pl, int64_t rows, hipStream_t st) {
+                  float *pl, int64_t rows, const int32_t *ctx_len, hipStream_t st) {
   if constexpr (BF16)
     hipLaunchKernelGGL((emit_attend_bf16_kernel<LPT, G>), dim3(p.parts, p.r.BH),
                        dim3(kScanThreads), 0, st, stash, hist, p.r.BINS, p.r.C, p.r.keff, count,
                        p.r.S, p.cpb, p.Sc, p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,
-                       p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows);
+                       p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows, ctx_len,
+                       p.n_local, p.max_ctx);
   else
     hipLaunchKernelGGL((emit_attend_f32_kernel<LPT, G>), dim3(p.parts, p.r.BH),
                        dim3(kScanThreads), 0, st, stash, hist, p.r.BINS, p.r.C, p.r.keff, count,
                        p.r.S, p.cpb, p.Sc, p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,
-                       p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows);
+                       p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows, ctx_len,
+                       p.n_local, p.max_ctx);
 }
 
 template <int LPT, bool BF16>
 void fused_dispatch_g(const FusedPlan &p, const uint32_t *stash, const uint32_t *hist,
                       int32_t *count, int k, int32_t *idx, const void *q, const void *kc,
                       const void *vc, int Hq, int Hkv, int64_t cap, float sl2, float *po,
-                      float *pl, int64_t rows, hipStream_t st) {
+                      float *pl, int64_t rows, const int32_t *ctx_len, hipStream_t st) {
 #define HK_FUSED_CASE(GG)                                                                   \
   case GG:                                                                                  \
     fused_launch<LPT, BF16, GG>(p, stash, hist, count, k, idx, q, kc, vc, Hq, Hkv, cap,    \
-                                sl2, po, pl, rows, st);                                     \
+                                sl2, po, pl, rows, ctx_len, st);                            \
     break;
   switch (p.G) {
     HK_FUSED_CASE(1) HK_FUSED_CASE(2) HK_FUSED_CASE(3) HK_FUSED_CASE(4)
@@ -217,6 +234,8 @@ FusedPlan plan_fused(int bits, int B, int Hq, int Hkv, int64_t n_ctx, int n_sink
   const int64_t local0 = (n_ctx - n_local) > n_sink ? (n_ctx - n_local) : n_sink;
   p.win_sinks = (int)sinks;
   p.win_local0 = local0;
+  p.n_local = n_local;
+  p.max_ctx = n_ctx;
   p.n_win = (int)(sinks + (n_ctx > local0 ? n_ctx - local0 : 0));
   // Chunks per workgroup: at least one 16-row tile of selected rows per workgroup and no
   // more workgroups than are resident at once, while keeping at least 128 workgroups.
@@ -249,7 +268,7 @@ FusedPlan plan_fused(int bits, int B, int Hq, int Hkv, int64_t n_ctx, int n_sink
 hipError_t launch_fused_attend(const FusedPlan &p, const void *q, const void *kc,
                                const void *vc, int dtype, int B, int Hq, int Hkv, int64_t cap,
                                float scale, int k, int32_t *idx, int32_t *count, float *o,
-                               float *lse, void *ws, hipStream_t st) {
+                               float *lse, void *ws, hipStream_t st, const int32_t *ctx_len) {
   const int64_t rows = (int64_t)B * Hq;
   if (rows == 0) return hipSuccess;
   // Without candidate chunks no workgroup derives the threshold: the threshold kernel
@@ -268,9 +287,9 @@ hipError_t launch_fused_attend(const FusedPlan &p, const void *q, const void *kc
     const bool bf = dtype == HK_BF16;
 #define HK_LPT(L)                                                                            \
   if (bf) fused_dispatch_g<L, true>(p, stash, hist, count, k, idx, q, kc, vc, Hq, Hkv, cap,  \
-                                    sl2, po, pl, rows, st);                                  \
+                                    sl2, po, pl, rows, ctx_len, st);                         \
   else fused_dispatch_g<L, false>(p, stash, hist, count, k, idx, q, kc, vc, Hq, Hkv, cap,    \
-                                  sl2, po, pl, rows, st);
+                                  sl2, po, pl, rows, ctx_len, st);
     if (p.r.lpt == 8) { HK_LPT(8) }
     else { HK_LPT(4) }
 #undef HK_LPT

@@ -15,6 +15,16 @@ constexpr int kMaxGroup = 8;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Candidates [lo, n - n_local) of sequence b whose context length is ctx_len[b],
+// clamped to [0, max_ctx].
+__device__ __forceinline__ int64_t head_candidates(const int32_t *ctx_len, int b, int64_t max_ctx,
+                                                   int64_t lo, int64_t n_local) {
+  int64_t n = ctx_len[b];
+  n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
+  const int64_t hi = n - n_local;
+  return hi > lo ? hi - lo : 0;
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -52,8 +62,9 @@ struct RetrievePlan {
 RetrievePlan plan_retrieve(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, int n_local,
                            int k);
 hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
-                               const uint32_t *qcodes, int64_t cap, void *ws,
-                               hipStream_t st);
+                               const uint32_t *qcodes, int64_t cap, void *ws, hipStream_t st,
+                               const int32_t *ctx_len = nullptr, int Hkv = 1,
+                               int64_t n_local = 0, int64_t max_ctx = 0);
 // Per-query-head retrieval: p planned with B*Hq heads; each code is read once and
 // compared with the G query codes of its KV head.
 hipError_t launch_hamming_scan_qheads(const RetrievePlan &p, int G, const uint32_t *codes,
@@ -93,7 +104,7 @@ hipError_t launch_lse_merge_parts(const float *o_parts, const float *lse_parts, 
 struct FusedPlan {
   RetrievePlan r;
   int win_sinks = 0, n_win = 0, win_rows = 64, Sw = 0, parts = 0, G = 1, cpb = 1, Sc = 0;
-  int64_t win_local0 = 0;
+  int64_t win_local0 = 0, n_local = 0, max_ctx = 0;
   size_t off_o = 0, off_lse = 0, total = 0;
 };
 FusedPlan plan_fused(int bits, int B, int Hq, int Hkv, int64_t n_ctx, int n_sink, int n_local,
@@ -101,7 +112,8 @@ FusedPlan plan_fused(int bits, int B, int Hq, int Hkv, int64_t n_ctx, int n_sink
 hipError_t launch_fused_attend(const FusedPlan &p, const void *q, const void *kc,
                                const void *vc, int dtype, int B, int Hq, int Hkv, int64_t cap,
                                float scale, int k, int32_t *idx, int32_t *count, float *o,
-                               float *lse, void *ws, hipStream_t st);
+                               float *lse, void *ws, hipStream_t st,
+                               const int32_t *ctx_len = nullptr);
 
 // ---------------------------------------------------------------- encoders
 hipError_t launch_encode_keys(const hk_hash &h, const void *k, int B, int Hkv, int64_t cap,

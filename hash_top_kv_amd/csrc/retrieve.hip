@@ -26,10 +26,15 @@ namespace {
 // histogram of the chunk goes to hist[bh][c]: bins 0 .. 32W-1, then 4W "superbins", each
 // the count of 8 consecutive distances (the count at distance 32W follows from the
 // chunk size).
+// ctx_len (device, [B]; NULL = every sequence has the full context) gives each sequence
+// its own context length n_b <= max_ctx: head bh (of sequence bh / Hkv) then has
+// C_b = max(0, n_b - n_local - lo) candidates, and workgroups past its last chunk end
+// at once (the threshold reads only the head's own chunks).
 template <int W, int LPT>
 __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
     const uint32_t *__restrict__ codes, const uint32_t *__restrict__ qcodes, int64_t cap,
-    int64_t lo, int64_t C, int S, uint32_t *__restrict__ stash, uint32_t *__restrict__ hist_out) {
+    int64_t lo, int64_t C, int S, uint32_t *__restrict__ stash, uint32_t *__restrict__ hist_out,
+    const int32_t *__restrict__ ctx_len, int Hkv, int64_t n_local, int64_t max_ctx) {
   constexpr int BINS = 32 * W;
   constexpr int NBP = BINS + 4;
   constexpr int CH = kScanThreads * LPT;
@@ -42,6 +47,10 @@ __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
   const int bh = blockIdx.y;
   const int t = threadIdx.x;
   const int wave = t >> 6;
+  if (ctx_len) {
+    C = head_candidates(ctx_len, bh / Hkv, max_ctx, lo, n_local);
+    if ((int64_t)c * CH >= C) return;
+  }
 
   // The histograms are cleared and the query code read before the codes are requested:
   // a barrier after the code loads would make every thread wait for all of them, while
@@ -246,9 +255,11 @@ void scan_group_launch(const RetrievePlan &p, int G, const uint32_t *codes,
 
 template <int W, int LPT>
 void scan_launch(const RetrievePlan &p, const uint32_t *codes, const uint32_t *qcodes,
-                 int64_t cap, uint32_t *stash, uint32_t *hist, hipStream_t st) {
+                 int64_t cap, uint32_t *stash, uint32_t *hist, const int32_t *ctx_len, int Hkv,
+                 int64_t n_local, int64_t max_ctx, hipStream_t st) {
   hipLaunchKernelGGL((hamming_scan_kernel<W, LPT>), dim3(p.S, p.BH), dim3(kScanThreads), 0,
-                     st, codes, qcodes, cap, p.lo, p.C, p.S, stash, hist);
+                     st, codes, qcodes, cap, p.lo, p.C, p.S, stash, hist, ctx_len, Hkv, n_local,
+                     max_ctx);
 }
 
 }  // namespace
@@ -286,18 +297,22 @@ RetrievePlan plan_retrieve(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, 
 
 hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
                                const uint32_t *qcodes, int64_t cap, void *ws,
-                               hipStream_t st) {
+                               hipStream_t st, const int32_t *ctx_len, int Hkv,
+                               int64_t n_local, int64_t max_ctx) {
   if (p.BH == 0 || p.S == 0) return hipSuccess;
   uint8_t *w8 = static_cast<uint8_t *>(ws);
   uint32_t *stash = reinterpret_cast<uint32_t *>(w8 + p.off_stash);
   uint32_t *hist = reinterpret_cast<uint32_t *>(w8 + p.off_hist);
+#define HK_SCAN(WW, LL) \
+  scan_launch<WW, LL>(p, codes, qcodes, cap, stash, hist, ctx_len, Hkv, n_local, max_ctx, st)
   if (p.W == 4) {
-    if (p.lpt == 8) scan_launch<4, 8>(p, codes, qcodes, cap, stash, hist, st);
-    else scan_launch<4, 4>(p, codes, qcodes, cap, stash, hist, st);
+    if (p.lpt == 8) HK_SCAN(4, 8);
+    else HK_SCAN(4, 4);
   } else {
-    if (p.lpt == 8) scan_launch<2, 8>(p, codes, qcodes, cap, stash, hist, st);
-    else scan_launch<2, 4>(p, codes, qcodes, cap, stash, hist, st);
+    if (p.lpt == 8) HK_SCAN(2, 8);
+    else HK_SCAN(2, 4);
   }
+#undef HK_SCAN
   return hipGetLastError();
 }
 

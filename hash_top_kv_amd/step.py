@@ -20,7 +20,8 @@ import math
 import torch
 
 from . import (Hash, encode_query, evict_replace, evict_select, evict_workspace, hamming_scan,
-               lse_merge, retrieve_attend_workspace, retrieve_topk_qheads, retrieve_topk_workspace,
+               lse_merge, retrieve_attend_varlen, retrieve_attend_workspace, retrieve_topk_qheads,
+               retrieve_topk_workspace,
                select_attend, sparse_decode, sparse_decode_qheads, sparse_decode_workspace,
                window_indices, workspace, _check, _ptr, _stream, lib)
 
@@ -199,3 +200,34 @@ class QHeadStep:
             qcodes = self.encode(q)
         self.retrieve(qcodes)
         return self.attend(q)
+
+
+class VarlenDecodeStep:
+    """The decode step for a batch of sequences of their own lengths (ctx_len [B] int32 on
+    the device, each <= max_ctx): hk_encode_query, then hk_retrieve_attend_varlen
+    (scan, select and attend with each sequence's own candidates, budget and window)."""
+
+    def __init__(self, K, V, codes, bits, ctx_len, max_ctx, n_sink, n_local, k, Hq,
+                 hash: Hash | None = None):
+        self.K, self.V, self.codes, self.bits, self.hash = K, V, codes, bits, hash
+        B, Hkv, cap, d = K.shape
+        self.B, self.Hkv, self.cap, self.d, self.Hq = B, Hkv, cap, d, Hq
+        self.ctx_len, self.max_ctx = ctx_len, max_ctx
+        self.n_sink, self.n_local, self.k = n_sink, n_local, k
+        dev = K.device
+        self.idx = torch.zeros((B, Hkv, max(k, 1)), dtype=torch.int32, device=dev)
+        self.count = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+        self.ws = workspace(retrieve_attend_workspace(bits, B, Hq, Hkv, max_ctx, n_sink, n_local,
+                                                      k), dev)
+        self.o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        self.qcodes = torch.empty((B, Hkv, bits // 32), dtype=torch.int32, device=dev)
+        self.scale = 1.0 / math.sqrt(d)
+
+    def __call__(self, q, qcodes=None):
+        if qcodes is None:
+            qcodes = encode_query(self.hash, q, self.Hkv, self.qcodes)
+        retrieve_attend_varlen(self.codes, qcodes, self.bits, q, self.K, self.V, self.ctx_len,
+                               self.max_ctx, self.n_sink, self.n_local, self.k, scale=self.scale,
+                               idx=self.idx, count=self.count, o=self.o, lse=self.lse, ws=self.ws)
+        return self.o, self.lse

@@ -307,6 +307,22 @@ hk_status hk_sparse_decode_qheads(const void *q, const void *k, const void *v, i
                                   float scale, float *o, float *lse, void *ws, size_t ws_bytes,
                                   void *stream);
 
+/* hk_retrieve_attend for a batch of sequences of their own lengths: sequence b holds
+ * ctx_len[b] cached tokens (clamped to [0, max_ctx]); its candidates, budget
+ * k_eff = min(topk, candidates), window and count follow its own length, exactly as a
+ * call of hk_retrieve_attend with n_ctx = ctx_len[b] on that sequence alone.
+ *   ctx_len  device int32 [B].
+ *   max_ctx  host: an upper bound of the lengths (<= cap), which sizes the launch and the
+ *            workspace: hk_retrieve_attend_workspace(bits, B, Hq, Hkv, max_ctx, ...).
+ * Other arguments and errors as hk_retrieve_attend; ctx_len NULL -> INVALID_ARGUMENT. */
+hk_status hk_retrieve_attend_varlen(const uint32_t *codes, const uint32_t *qcodes, int bits,
+                                    const void *q, const void *kc, const void *vc, int dtype,
+                                    int B, int Hq, int Hkv, int d, int64_t cap,
+                                    const int32_t *ctx_len, int64_t max_ctx, int n_sink,
+                                    int n_local, int topk, float scale, int32_t *idx,
+                                    int32_t *count, float *o, float *lse, void *ws,
+                                    size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

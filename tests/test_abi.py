@@ -139,6 +139,13 @@ def test_host_validation_without_gpu(hk):
     assert L.hk_topk_intersect(dummy, dummy, 4, dummy, dummy, 4, -1, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
     assert L.hk_topk_intersect(P, dummy, 4, dummy, dummy, 4, 3, dummy, P) == hk.HK_ERR_INVALID_ARGUMENT
     assert L.hk_topk_intersect(P, P, 4, P, P, 4, 0, P, P) == hk.HK_OK
+    # variable lengths: the lengths array is required
+    assert L.hk_retrieve_attend_varlen(dummy, dummy, 128, dummy, dummy, dummy, hk.HK_BF16, 1, 8, 4,
+                                       128, 10, P, 10, 0, 0, 3, f, dummy, dummy, dummy, dummy,
+                                       dummy, 1 << 30, P) == hk.HK_ERR_INVALID_ARGUMENT
+    assert L.hk_retrieve_attend_varlen(dummy, dummy, 128, dummy, dummy, dummy, hk.HK_BF16, 1, 8, 4,
+                                       128, 10, dummy, 11, 0, 0, 3, f, dummy, dummy, dummy, dummy,
+                                       dummy, 1 << 30, P) == hk.HK_ERR_INVALID_ARGUMENT
     # per-query-head retrieval and attention
     assert L.hk_retrieve_topk_qheads(P, P, 128, 1, 6, 4, 10, 10, 0, 0, 3, P, P, P, 0, P) \
         == hk.HK_ERR_INVALID_ARGUMENT

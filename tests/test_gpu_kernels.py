@@ -485,3 +485,58 @@ def test_sign_codes_keys_queries_and_step(dtype):
             assert np.array_equal(st.idx[b, g, :st.keff].cpu().numpy(), ref["idx"][g])
         assert np.max(np.abs(o[b].cpu().numpy() - ref["o"])) <= tol
         assert np.max(np.abs(lse[b].cpu().numpy() - ref["lse"])) <= tol
+
+
+# ----------------------------------------------------------------- variable lengths
+VARLEN_CASES = [
+    # bits, dtype, Hq, Hkv, cap, lengths, s, w, k
+    (128, "bf16", 8, 2, 9000, (9000, 4711, 70, 0, 2049, 8999), 4, 64, 180),
+    (64, "bf16", 7, 1, 30000, (30000, 12345, 68, 1), 4, 512, 600),
+    (128, "f32", 4, 4, 5000, (5000, 3000), 4, 64, 100),
+    (128, "bf16", 4, 2, 3000, (3000, 3000, 3000), 0, 0, 60),     # equal lengths, no window
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: "-".join(map(str, c[:5])) + f"-B{len(c[5])}")
+def test_retrieve_attend_varlen_matches_oracle_per_sequence(case):
+    """Each sequence of a variable-length batch gives what the oracle gives for that
+    sequence alone with its own n_ctx (selection bit-exact, attention within the bound),
+    including sequences with no candidates and an empty one."""
+    bits, dtype, Hq, Hkv, cap, lengths, s, w, k = case
+    say(f"retrieve_attend_varlen {case}")
+    B, W = len(lengths), bits // 32
+    rng = np.random.default_rng(cap + B)
+    codes = rng.integers(0, 2 ** 32, size=(B, Hkv, cap, W), dtype=np.uint32)
+    qc = rng.integers(0, 2 ** 32, size=(B, Hkv, W), dtype=np.uint32)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    K = torch.from_numpy(rng.standard_normal((B, Hkv, cap, 128)).astype(np.float32) * 1.5).to(tdt).cuda()
+    V = torch.from_numpy(rng.standard_normal((B, Hkv, cap, 128)).astype(np.float32)).to(tdt).cuda()
+    Q = torch.from_numpy(rng.standard_normal((B, Hq, 128)).astype(np.float32) * 1.5).to(tdt).cuda()
+    ctx = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    o, lse, idx, cnt = hk.retrieve_attend_varlen(codes_tensor(codes), codes_tensor(qc), bits, Q, K, V,
+                                                 ctx, max(lengths), s, w, k)
+    torch.cuda.synchronize()
+    o, lse, idx, cnt = o.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    Kd, Vd, Qd = (x.cpu().to(torch.float64).numpy() for x in (K, V, Q))
+    G = Hq // Hkv
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    scale = 1 / math.sqrt(128)
+    for b, n in enumerate(lengths):
+        win = oracle.window_indices(n, s, w)
+        for h in range(Hkv):
+            sel = oracle.select_topk(codes[b, h], qc[b, h], n, s, w, k)
+            assert cnt[b, h] == sel.size and np.array_equal(idx[b, h, :sel.size], sel), (b, h)
+            for g in range(G):
+                hq = h * G + g
+                o1, l1 = oracle.attend(Qd[b, hq], Kd[b, h][sel], Vd[b, h][sel], scale)
+                o2, l2 = oracle.attend(Qd[b, hq], Kd[b, h][win], Vd[b, h][win], scale)
+                ro, rl = oracle.lse_merge(np.stack([o1, o2]), np.array([l1, l2]))
+                assert np.max(np.abs(o[b, hq] - ro)) <= tol, (b, hq)
+                assert (rl == -np.inf and lse[b, hq] == -np.inf) or abs(lse[b, hq] - rl) <= tol
+    if len(set(lengths)) == 1:
+        # equal lengths: the same as the uniform call, bit for bit
+        o2, l2, i2, c2 = hk.retrieve_attend(codes_tensor(codes), codes_tensor(qc), bits, Q, K, V,
+                                            lengths[0], s, w, k)
+        torch.cuda.synchronize()
+        assert np.array_equal(o2.cpu().numpy(), o) and np.array_equal(l2.cpu().numpy(), lse)
+        assert np.array_equal(c2.cpu().numpy(), cnt)
