@@ -74,8 +74,11 @@ __device__ __forceinline__ void emit_attend_body(
     ga.run_block(kc, vc, head_row0, len, [&](int r) { return sel[r]; });
   };
   if (c < Sc) {
-    const int c0 = c * CPB;
-    const int c1 = min(Sb, c0 + CPB);
+    // A shorter sequence spreads its Sb chunks over all Sc chunk workgroups of its head
+    // (Sb <= S <= Sc * CPB, so at most CPB each), not over the first Sb / CPB of them.
+    const int cpb = ctx_len ? (Sb + Sc - 1) / Sc : CPB;
+    const int c0 = c * cpb;
+    const int c1 = min(Sb, c0 + cpb);
     int len = 0;
     int32_t *out = idx + (int64_t)bh * k;
     const int nch = c1 - c0;

@@ -494,6 +494,8 @@ VARLEN_CASES = [
     (64, "bf16", 7, 1, 30000, (30000, 12345, 68, 1), 4, 512, 600),
     (128, "f32", 4, 4, 5000, (5000, 3000), 4, 64, 100),
     (128, "bf16", 4, 2, 3000, (3000, 3000, 3000), 0, 0, 60),     # equal lengths, no window
+    # enough chunks for several per workgroup, so shorter sequences spread fewer chunks
+    (128, "bf16", 8, 2, 50000, (50000, 31000, 12000, 47000, 5000, 2000), 4, 64, 100),
 ]
 
 
