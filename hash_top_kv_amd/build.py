@@ -34,9 +34,12 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
+# Kernel arguments preloaded into SGPRs at launch (up to 16 dwords), so a kernel's first
+# memory requests need no scalar load of its arguments first.
 def common_flags() -> list[str]:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-kernarg-preload-count=16",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             "-Wall", "-Wno-unused-function", "-Wno-unused-result"]
 

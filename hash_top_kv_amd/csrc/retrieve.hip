@@ -52,15 +52,6 @@ __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
     if ((int64_t)c * CH >= C) return;
   }
 
-  // The histograms are cleared and the query code read before the codes are requested:
-  // a barrier after the code loads would make every thread wait for all of them, while
-  // here each token is processed as soon as its own load has landed.
-  for (int i = t; i < (kScanThreads / 64) * NBP; i += kScanThreads) (&hist[0][0])[i] = 0u;
-  uint32_t q[W];
-#pragma unroll
-  for (int w = 0; w < W; ++w) q[w] = qcodes[(int64_t)bh * W + w];
-  __syncthreads();
-
   const int64_t p0 = (int64_t)c * CH;
   const int64_t pw = p0 + (int64_t)wave * (64 * LPT) + (t & 63);   // item i: pw + 64*i
   const V *base = reinterpret_cast<const V *>(codes + ((int64_t)bh * cap + lo) * W);
@@ -78,6 +69,15 @@ __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
       v[i] = (p < C) ? __builtin_nontemporal_load(base + p) : CV::zero();
     }
   }
+
+  // The histograms are cleared and the query code read while the codes are in flight
+  // (the barrier waits for the LDS stores, not for the loads), and each token is then
+  // processed as soon as its own load has landed.
+  for (int i = t; i < (kScanThreads / 64) * NBP; i += kScanThreads) (&hist[0][0])[i] = 0u;
+  uint32_t q[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) q[w] = qcodes[(int64_t)bh * W + w];
+  __syncthreads();
 
   uint32_t *st = stash + ((int64_t)bh * S + c) * stash_words_per_chunk<LPT>();
 #pragma unroll
