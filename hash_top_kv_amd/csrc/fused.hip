@@ -240,15 +240,19 @@ FusedPlan plan_fused(int bits, int B, int Hq, int Hkv, int64_t n_ctx, int n_sink
   p.n_local = n_local;
   p.max_ctx = n_ctx;
   p.n_win = (int)(sinks + (n_ctx > local0 ? n_ctx - local0 : 0));
-  // Chunks per workgroup: at least one 16-row tile of selected rows per workgroup and no
+  // Chunks per workgroup: at least two 16-row tiles of selected rows per workgroup and no
   // more workgroups than are resident at once, while keeping at least 128 workgroups.
-  // (Each chunk adds compaction work for all of its tokens, so chunks are not merged
-  // just to give every wavefront a tile: that lengthens the serial phase.)
+  // Every workgroup derives its head's threshold (a fixed cost per workgroup), so when
+  // the selection is small fewer, larger workgroups win: on 8 heads x 524288 codes with
+  // top-1024, 8 chunks (32 rows) per workgroup take the step from 30.0 to 28.4 us against
+  // 4 chunks (16 rows); with thousands of rows per head the resident-workgroup bound
+  // decides as before.  (Each chunk adds compaction work for all of its tokens, so chunks
+  // are not merged just to give every wavefront a tile: that lengthens the serial phase.)
   const int64_t chunks = (int64_t)p.r.BH * p.r.S;
   const int64_t per_chunk = p.r.S > 0 ? (p.r.keff + p.r.S - 1) / p.r.S : 1;
   int cpb = 1;
   while (cpb < kMaxCpb && chunks / (2 * cpb) >= 128 &&
-         (per_chunk * cpb < 16 || chunks / cpb > kResidentBlocks))
+         (per_chunk * cpb < 32 || chunks / cpb > kResidentBlocks))
     cpb *= 2;
   p.cpb = cpb;
   p.Sc = (p.r.S + cpb - 1) / cpb;
