@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--hash i]
                     [--replicas R] [--no-cpu] [--prefill] [--exact] [--evict]
-                    [--sign] [--unfused | --qheads | --varlen]
+                    [--sign] [--no-window] [--unfused | --qheads | --varlen]
 
 Default workload: retrieval at 512K tokens -- 8 KV heads x 524,288 cached 128-bit codes
 (uniform random bits plus 1% planted near neighbours of the query code), top-1024 per
@@ -19,8 +19,9 @@ Infinity Cache or the L2 by the previous steps.
 Prints ONE JSON line.  `value` is microseconds per decode step (lower is better).
 `roofline` describes the dominant kernel (the Hamming scan): algorithmic bytes per
 launch over its average duration, timed with HIP events on the launch stream around
-back-to-back launches.  `cpu_baseline` times the CPU oracle on a bounded sample of the
-same workload.
+back-to-back launches.  `kernels["select+attend"]` gives the gather the same way (K/V row
+bytes over the back-to-back duration of select + attend + merge).  `cpu_baseline` times
+the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -176,6 +177,8 @@ def build_full_case(args, torch, hk, synth):
     whole step after the keys were encoded), or with --unfused the separate calls."""
     from hash_top_kv_amd.step import DecodeStep, QHeadStep, VarlenDecodeStep
     wl = synth.WORKLOADS[args.workload]
+    if args.no_window:
+        wl = synth.scaled(wl, n_sink=0, n_local=0, name=wl.name + ", no window")
     spec = synth.HashSpec("sign", 128) if args.sign else wl.hashes[args.hash]
     R = args.replicas
     kv = synth.make_kv(wl)
@@ -451,6 +454,9 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the step")
+    ap.add_argument("--no-window", action="store_true",
+                    help="no sink or local window (s = w = 0): retrieval alone, the variant "
+                         "without a static window")
     ap.add_argument("--sign", action="store_true",
                     help="use sign codes of the keys themselves (128 bits) instead of the "
                          "workload's hash")
@@ -594,6 +600,26 @@ def main():
             kern["hamming_scan"].update({"us_per_launch": round(ms * 1e3, 3),
                                          "gbs": round(nbytes / ms / 1e6, 1),
                                          "frac_of_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)})
+        # Select + attend + merge alone, back to back the same way: each workspace still
+        # holds its last scan's distances and histograms, so every launch is a complete
+        # selection and gather.  Its K/V row bytes per launch / duration = the gather rate
+        # (threshold, compaction and merge included).
+        sel = [p for p in parts if p[0] == "select+attend"]
+        if sel and sel[0][2]:
+            _, fn, nbytes = sel[0]
+            n = max(args.steps, 50)
+            for i in range(8):
+                fn(i)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(n):
+                fn(i)
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / n
+            kern["select+attend"].update({"us_per_launch": round(ms * 1e3, 3),
+                                          "gbs": round(nbytes / ms / 1e6, 1),
+                                          "frac_of_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)})
 
     roofline = None
     sc = kern.get("hamming_scan", {})
