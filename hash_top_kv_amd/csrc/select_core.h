@@ -147,22 +147,16 @@ __device__ __forceinline__ void load_u32x(const uint32_t *p, uint32_t (&x)[K]) {
   }
 }
 
-// Sum of K values over the workgroup: per-wavefront transposed sums, then LDS.
-// Returns the total of value i in thread i < K (others: undefined).  red holds
-// kThrThreads / 64 * 16 entries.
-template <int K>
-__device__ __forceinline__ uint32_t block_sum_k(uint32_t (&x)[K], uint32_t *red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t r = wave_transpose_sum<K>(x);
-  if (lane < K) red[wave * 16 + bitrev_k<K>(lane)] = r;
-  __syncthreads();
-  uint32_t t = 0;
-  if ((int)threadIdx.x < K) {
-#pragma unroll
-    for (int w = 0; w < kThrThreads / 64; ++w) t += red[w * 16 + threadIdx.x];
-  }
-  __syncthreads();
-  return t;
+// Inclusive prefix sum over the 64 lanes of a wavefront: shifts within rows of 16 lanes,
+// then the row totals broadcast to the following rows (DPP row_shr, row_bcast:15/31).
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
 }
 
 // The threshold of one head, computed by one workgroup of kThrThreads threads, one thread
@@ -177,6 +171,11 @@ __device__ __forceinline__ uint32_t block_sum_k(uint32_t (&x)[K], uint32_t *red)
 //      below T in c, at T in c).
 // T = -1 when k_eff = 0.  Every thread returns T and the tie quota.  For up to
 // kThrThreads chunks per head every value is read once and kept in registers.
+//
+// Each level is one exchange through LDS: the wavefronts' partial totals go to LDS, and
+// after one barrier every wavefront adds them up itself and finds the bin that reaches
+// k_eff with an inclusive scan over its lanes and a ballot (the same answer in every
+// wavefront), so no thread walks the totals serially and no result is broadcast.
 template <int BINS, class Sink>
 __device__ __forceinline__ void head_threshold(const uint32_t *__restrict__ hb, int S, int64_t C,
                                                int CH, int keff, int &T_out, int &quota_out,
@@ -184,14 +183,16 @@ __device__ __forceinline__ void head_threshold(const uint32_t *__restrict__ hb, 
   constexpr int NSB = BINS / 8;                // 16 or 8 superbins
   constexpr int ROW = BINS + NSB;
   constexpr int NT = kThrThreads;
-  __shared__ uint32_t red[NT / 64 * 16];
-  __shared__ uint32_t tot[16];
-  __shared__ uint32_t scan_lds[2][NT / 64];
-  __shared__ int sh[4];                        // T, quota, superbin of T, count below it
+  constexpr int NW = NT / 64;
+  __shared__ uint32_t red1[NW][16];            // per-wavefront superbin totals
+  __shared__ uint32_t red2[NW][8];             // per-wavefront bin totals of T's superbin
+  __shared__ uint2 part[2][NW];                // per-wavefront (below, at) totals, per tile
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   auto row = [&](int c) { return hb + (int64_t)(c < S ? c : S - 1) * ROW; };
 
   uint32_t sb0[NSB], bb0[8];                   // the first tile's values, kept
+  int T = -1, quota = 0;
   if (keff > 0) {
     // 1. superbin totals
     uint32_t acc[NSB];
@@ -208,18 +209,18 @@ __device__ __forceinline__ void head_threshold(const uint32_t *__restrict__ hb, 
         if (c0 == 0) sb0[i] = x[i];
       }
     }
-    const uint32_t st = block_sum_k<NSB>(acc, red);
-    if (tid < NSB) tot[tid] = st;
+    const uint32_t r1 = wave_transpose_sum<NSB>(acc);
+    if (lane < NSB) red1[wave][bitrev_k<NSB>(lane)] = r1;
     __syncthreads();
-    if (tid == 0) {
-      uint32_t below = 0;
-      int s = 0;
-      while (s < NSB && below + tot[s] < (uint32_t)keff) below += tot[s++];
-      sh[2] = s;                               // NSB: T = BINS
-      sh[3] = (int)below;
+    uint32_t tot = 0;
+    if (lane < NSB) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += red1[w][lane];
     }
-    __syncthreads();
-    const int Ts = sh[2];
+    const uint32_t inc = wave_incl_scan_dpp(tot);                 // lanes >= NSB add 0
+    const uint64_t reach = __ballot(lane < NSB && inc >= (uint32_t)keff);
+    const int Ts = reach ? (int)__builtin_ctzll(reach) : NSB;
+    const uint32_t below = Ts == 0 ? 0u : (uint32_t)__shfl((int)inc, Ts - 1, 64);
     if (Ts < NSB) {
       // 2. the 8 bins of superbin Ts
       uint32_t bacc[8];
@@ -236,27 +237,26 @@ __device__ __forceinline__ void head_threshold(const uint32_t *__restrict__ hb, 
           if (c0 == 0) bb0[i] = x[i];
         }
       }
-      const uint32_t bt = block_sum_k<8>(bacc, red);
-      if (tid < 8) tot[tid] = bt;
+      const uint32_t r2 = wave_transpose_sum<8>(bacc);
+      if (lane < 8) red2[wave][bitrev_k<8>(lane)] = r2;
       __syncthreads();
-      if (tid == 0) {
-        uint32_t below = (uint32_t)sh[3];
-        int b = 0;
-        while (below + tot[b] < (uint32_t)keff) below += tot[b++];   // stops at b < 8
-        sh[0] = 8 * Ts + b;
-        sh[1] = keff - (int)below;
+      uint32_t bt = 0;
+      if (lane < 8) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) bt += red2[w][lane];
       }
-    } else if (tid == 0) {
-      sh[0] = BINS;
-      sh[1] = keff - sh[3];
+      const uint32_t binc = wave_incl_scan_dpp(bt) + below;
+      // the superbin holds the k_eff-th distance, so one of its 8 bins reaches k_eff
+      const uint64_t reach2 = __ballot(lane < 8 && binc >= (uint32_t)keff);
+      const int b = (int)__builtin_ctzll(reach2);
+      const uint32_t bbelow = b == 0 ? below : (uint32_t)__shfl((int)binc, b - 1, 64);
+      T = 8 * Ts + b;
+      quota = keff - (int)bbelow;
+    } else {
+      T = BINS;
+      quota = keff - (int)below;
     }
-  } else if (tid == 0) {
-    sh[0] = -1;
-    sh[1] = 0;
   }
-  __syncthreads();
-  const int T = sh[0];
-  const int quota = sh[1];
   // 3. per-chunk counts and their prefix over chunks
   uint32_t carry_lt = 0, carry_eq = 0;
   for (int c0 = 0; c0 < S && T >= 0; c0 += NT) {
@@ -287,28 +287,29 @@ __device__ __forceinline__ void head_threshold(const uint32_t *__restrict__ hb, 
         eq = (uint32_t)(n < CH ? n : CH) - lt;
       }
     }
-    uint32_t tl, te;
-    const uint32_t lt_ex = block_excl_scan_u32<NT>(lt, scan_lds[0], tl);
-    const uint32_t eq_ex = block_excl_scan_u32<NT>(eq, scan_lds[1], te);
+    // Exclusive prefix over the tile's chunks: scans within each wavefront, then the
+    // wavefront totals through LDS (double-buffered across tiles, one barrier per tile).
+    const uint32_t lt_inc = wave_incl_scan_dpp(lt), eq_inc = wave_incl_scan_dpp(eq);
+    uint2 *pt = part[(c0 / NT) & 1];
+    if (lane == 63) pt[wave] = make_uint2(lt_inc, eq_inc);
+    __syncthreads();
+    uint32_t off_lt = 0, off_eq = 0, tl = 0, te = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint2 x = pt[w];
+      off_lt += (w < wave) ? x.x : 0u;
+      off_eq += (w < wave) ? x.y : 0u;
+      tl += x.x;
+      te += x.y;
+    }
     if (c < S)
-      sink(c, make_int4((int)(carry_lt + lt_ex), (int)(carry_eq + eq_ex), (int)lt, (int)eq));
+      sink(c, make_int4((int)(carry_lt + off_lt + lt_inc - lt),
+                        (int)(carry_eq + off_eq + eq_inc - eq), (int)lt, (int)eq));
     carry_lt += tl;
     carry_eq += te;
   }
   T_out = T;
   quota_out = quota;
-}
-
-// Inclusive prefix sum over the 64 lanes of a wavefront: shifts within rows of 16 lanes,
-// then the row totals broadcast to the following rows (DPP row_shr, row_bcast:15/31).
-__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);   // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);   // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);   // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);   // row_shr:8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return v;
 }
 
 // Writes the selected tokens of nch consecutive chunks (nch uniform, at most MAXC) into
