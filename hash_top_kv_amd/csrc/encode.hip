@@ -41,18 +41,29 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // z >= 0, absolute error at most 1.5e-7.  One reciprocal and one base-2 exponential;
 // exp(-a^2 / 2) / 2 = 2^(-a^2 log2(e) / 2 - 1).  For |a| > 13 the exponential underflows
 // to zero and GELU(a) is max(a, 0) to fp32 precision.
+// With x = |a| and k = p / sqrt 2, t = 1 / (1 + k x) gives x t = (1 - t) / k, so
+// x t P(t) = (1 - t) P'(t) with P' = P / k (coefficients divided by k once, here): one
+// fused multiply-add instead of two products.  1 - t is exact (t lies in (0, 1]); the
+// rounding of t then moves the result by at most about 2e-7.  max(a, 0) is an integer
+// max of the bits (a negative float, -0 included, is a negative integer): one operation
+// with no NaN canonicalisation (the inputs are finite).
+constexpr double kErfP = 0.3275911 * 0.70710678118654752;   // p / sqrt 2
 __device__ __forceinline__ float gelu(float a) {
-  constexpr float kP = 0.3275911f * 0.70710678118654752f;   // p / sqrt 2
+  constexpr float kP = (float)kErfP;
   constexpr float kHalfLog2e = -0.72134752044448170f;       // -log2(e) / 2
+  constexpr float c1 = (float)(0.254829592 / kErfP), c2 = (float)(-0.284496736 / kErfP);
+  constexpr float c3 = (float)(1.421413741 / kErfP), c4 = (float)(-1.453152027 / kErfP);
+  constexpr float c5 = (float)(1.061405429 / kErfP);
   const float x = fabsf(a);
   const float t = __builtin_amdgcn_rcpf(fmaf(kP, x, 1.0f));
-  float p = 1.061405429f;
-  p = fmaf(p, t, -1.453152027f);
-  p = fmaf(p, t, 1.421413741f);
-  p = fmaf(p, t, -0.284496736f);
-  p = fmaf(p, t, 0.254829592f);
+  float p = c5;
+  p = fmaf(p, t, c4);
+  p = fmaf(p, t, c3);
+  p = fmaf(p, t, c2);
+  p = fmaf(p, t, c1);
+  const float u = fmaf(-t, p, p);                           // x t P(t)
   const float g = __builtin_amdgcn_exp2f(fmaf(x * kHalfLog2e, x, -1.0f));
-  return fmaf(-x, (p * t) * g, fmaxf(a, 0.f));
+  return fmaf(-u, g, __int_as_float(max(__float_as_int(a), 0)));   // max(a, 0)
 }
 
 // Round to the nearest bf16 (ties to even); finite inputs.
