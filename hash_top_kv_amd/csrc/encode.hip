@@ -648,13 +648,16 @@ __global__ __launch_bounds__((EncLayout<MLP, BITS>::WAVES * 64)) void encode_key
     uint32_t words[JT];
 #pragma unroll
     for (int j = 0; j < JT; ++j) {
+      // acc_row(r, lg) = acc_row(r, 0) + 4 lg: constant shifts per register, then one
+      // shift by the lane group.
       uint32_t w = 0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float y = yacc[j][r];
         if constexpr (BIAS) y += bias[L::NB1 + 32 * j + acc_row(r, lg)];
-        w |= (y > 0.f ? 1u : 0u) << acc_row(r, lg);
+        w |= (y > 0.f ? 1u : 0u) << acc_row(r, 0);
       }
+      w <<= 4 * lg;
       words[j] = w | __shfl_xor(w, 32);
     }
     if (ok) {
