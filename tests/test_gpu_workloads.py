@@ -98,7 +98,7 @@ def _check_head_step(gpu_idx, gpu_o, gpu_lse, qg, Kf, Vf, key_codes, qcode_ref, 
 def _encode_and_check(wl, spec, hidx, sample):
     d = _inputs(wl.wid)
     hnp = synth.make_hash(wl, spec, hidx)
-    h = hk.Hash(spec.kind, spec.bits, **synth.hash_to_device(hnp))
+    h = hk.Hash(spec.kind, spec.bits, dtype=d["K"].dtype, **synth.hash_to_device(hnp))
     codes = torch.zeros((wl.B, wl.Hkv, wl.N, spec.words), dtype=torch.int32, device="cuda")
     hk.encode_keys(h, d["K"], codes)
     torch.cuda.synchronize()
@@ -113,9 +113,9 @@ def _encode_and_check(wl, spec, hidx, sample):
     return h, hnp, hp, codes, ref_codes
 
 
-def _run_workload(wid, hidx=0):
+def _run_workload(wid, hidx=0, spec=None):
     wl = synth.WORKLOADS[wid]
-    spec = wl.hashes[hidx]
+    spec = spec or wl.hashes[hidx]
     sample = _sample_heads(wl)
     d = _inputs(wid)
     h, hnp, hp, codes, ref_codes = _encode_and_check(wl, spec, hidx, sample)
@@ -160,12 +160,58 @@ def test_workload3_batch16_131072_mlp128():
     _run_workload(3)
 
 
+def test_workload3_sign_codes():
+    """Sign codes (bit j = sign of element j) at full size: keys and query codes bit for
+    bit, the step on sampled heads."""
+    _run_workload(3, spec=synth.HashSpec("sign", 128))
+
+
+def test_workload3_per_sequence_lengths():
+    """The batch-16 workload with the benchmark's per-sequence lengths (131072 down to
+    69632): each sampled sequence against the oracle's step at its own length."""
+    wl = synth.WORKLOADS[3]
+    spec = wl.hashes[0]
+    sample = _sample_heads(wl)
+    d = _inputs(3)
+    h, hnp, hp, codes, ref_codes = _encode_and_check(wl, spec, 0, sample)
+    for (b, g), ref in ref_codes.items():
+        codes[b, g] = codes_tensor(ref)
+    lengths = [wl.N - (b * wl.N) // (2 * wl.B) for b in range(wl.B)]
+    ctx_len = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    from hash_top_kv_amd.step import VarlenDecodeStep
+    step = VarlenDecodeStep(d["K"], d["V"], codes, spec.bits, ctx_len, wl.N, wl.n_sink,
+                            wl.n_local, wl.k, wl.Hq, h)
+    o, lse = step(d["Q"])
+    torch.cuda.synchronize()
+    qref, qy = oracle.encode_query(oracle.widen(d["q"], wl.dtype), hp, wl.Hkv)
+    compare_codes(np_u32(step.qcodes), qref, qy)
+    gidx, gcnt = step.idx.cpu().numpy(), step.count.cpu().numpy()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    G = wl.G
+    for b, g in sample:
+        n = lengths[b]
+        wb = synth.scaled(wl, N=n)
+        keff = max(0, min(wl.k, n - wl.n_sink - wl.n_local))
+        assert gcnt[b, g] == keff, (b, g)
+        Kf = oracle.widen(d["kv"]["K"][b, g], wl.dtype)
+        Vf = oracle.widen(d["kv"]["V"][b, g], wl.dtype)
+        qg = oracle.widen(d["q"][b, g * G:(g + 1) * G], wl.dtype)
+        e = _check_head_step(gidx[b, g, :keff], o[b, g * G:(g + 1) * G], lse[b, g * G:(g + 1) * G],
+                             qg, Kf, Vf, ref_codes[(b, g)][:n], qref[b, g], qy[b, g], wb, 2e-2)
+        say(f"  sequence {b} (n = {n}), head {g}: max|do| {e[0]:.2e} max|dlse| {e[1]:.2e}")
+
+
 def test_workload4_qwen_lsh64():
     _run_workload(4, 0)
 
 
 def test_workload4_qwen_mlp128():
     _run_workload(4, 1)
+
+
+def test_workload4_sign_codes():
+    """Sign codes at full size on the GQA 7:1 workload."""
+    _run_workload(4, spec=synth.HashSpec("sign", 128))
 
 
 @pytest.mark.parametrize("hidx", [0, 1])
@@ -186,6 +232,33 @@ def test_workload4_prefill_encode_sampled_rows(hidx):
     got = np_u32(codes).reshape(-1, spec.words)[rows]
     n = compare_codes(got, ref, y)
     say(f"  {spec.kind}-{spec.bits}: 30000 sampled rows, exempt bits differing: {n}")
+
+
+def test_workload2_fused_step_512k_planted():
+    """The 512K retrieval step as the benchmark runs it: hk_hamming_scan, then
+    hk_select_attend on the same workspace."""
+    wl = synth.WORKLOADS[2]
+    d = _inputs(2)
+    g = synth.make_given_codes(wl)
+    codes, qc = codes_tensor(g["codes"]), codes_tensor(g["qcodes"])
+    B, Hkv, k = wl.B, wl.Hkv, wl.k
+    ws = hk.workspace(hk.retrieve_attend_workspace(128, B, wl.Hq, Hkv, wl.N, 0, 0, k))
+    idx = torch.empty((B, Hkv, k), dtype=torch.int32, device="cuda")
+    count = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
+    o = torch.empty((B, wl.Hq, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, wl.Hq), dtype=torch.float32, device="cuda")
+    hk.hamming_scan(codes, qc, 128, wl.N, 0, 0, k, ws)
+    hk.select_attend(128, d["Q"], d["K"], d["V"], wl.N, 0, 0, k, idx, count, o, lse, ws)
+    torch.cuda.synchronize()
+    idx, count, o, lse = (t.cpu().numpy() for t in (idx, count, o, lse))
+    for h in range(Hkv):
+        pos, dl = g["planted_pos"][0, h], g["planted_delta"][0, h]
+        closed = np.sort(pos[np.lexsort((pos, dl))[:k]])
+        assert count[0, h] == k and np.array_equal(idx[0, h], closed), h
+        Kf = oracle.widen(d["kv"]["K"][0, h][closed], wl.dtype)
+        Vf = oracle.widen(d["kv"]["V"][0, h][closed], wl.dtype)
+        ro, rl = oracle.attend(oracle.widen(d["q"][0, h], wl.dtype), Kf, Vf, 1 / math.sqrt(128))
+        assert np.max(np.abs(o[0, h] - ro)) <= 2e-2 and abs(lse[0, h] - rl) <= 2e-2
 
 
 def test_workload2_retrieval_512k_planted():
