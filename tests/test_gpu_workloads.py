@@ -214,6 +214,69 @@ def test_workload4_sign_codes():
     _run_workload(4, spec=synth.HashSpec("sign", 128))
 
 
+def test_workload4_per_query_head_step():
+    """Per-query-head selection at full size (28 query heads over 4 KV heads x 262144
+    LSH-64 codes, top-5243 each), as the benchmark's --qheads step runs it: every query
+    head of one sequence against the oracle, indices bit for bit given identical codes."""
+    wl = synth.WORKLOADS[4]
+    spec = wl.hashes[0]
+    d = _inputs(4)
+    hnp = synth.make_hash(wl, spec, 0)
+    h = hk.Hash(spec.kind, spec.bits, **synth.hash_to_device(hnp))
+    codes = torch.empty((wl.B, wl.Hkv, wl.N, spec.words), dtype=torch.int32, device="cuda")
+    hk.encode_keys(h, d["K"], codes)
+    from hash_top_kv_amd.step import QHeadStep
+    step = QHeadStep(d["K"], d["V"], codes, spec.bits, wl.N, wl.n_sink, wl.n_local, wl.k,
+                     wl.Hq, h)
+    o, lse = step(d["Q"])
+    torch.cuda.synchronize()
+    b = wl.B - 1
+    qc = np_u32(step.qcodes)
+    hp = oracle.prepare_hash(hnp)
+    ref_q, yq = oracle.encode(oracle.widen(d["q"][b], wl.dtype), hp)
+    compare_codes(qc[b], ref_q, yq)
+    ref = oracle.decode_step_qheads(oracle.widen(d["q"][b], wl.dtype),
+                                    oracle.widen(d["kv"]["K"][b], wl.dtype),
+                                    oracle.widen(d["kv"]["V"][b], wl.dtype), np_u32(codes[b]), hp,
+                                    wl.N, wl.n_sink, wl.n_local, wl.k, qcodes=qc[b])
+    idx, count = step.idx.cpu().numpy(), step.count.cpu().numpy()
+    for hq in range(wl.Hq):
+        assert count[b, hq] == ref["idx"][hq].size
+        assert np.array_equal(idx[b, hq, :count[b, hq]], ref["idx"][hq]), hq
+    err_o = float(np.max(np.abs(o[b].cpu().numpy() - ref["o"])))
+    err_l = float(np.max(np.abs(lse[b].cpu().numpy() - ref["lse"])))
+    assert err_o <= 2e-2 and err_l <= 2e-2, (err_o, err_l)
+    say(f"  sequence {b}: {wl.Hq} query heads, max|do| {err_o:.2e} max|dlse| {err_l:.2e}")
+
+
+def test_workload4_exact_topk():
+    """The exact top-k by logit at full size (4 x 4 x 262144 keys, top-5243), sampled
+    heads: the count exact, every token clearly above the k-th logit selected and none
+    clearly below (fp32 against fp64 logits)."""
+    wl = synth.WORKLOADS[4]
+    d = _inputs(4)
+    idx, count = hk.exact_topk(d["Q"], d["K"], wl.N, wl.n_sink, wl.n_local, wl.k)
+    torch.cuda.synchronize()
+    idx, count = idx.cpu().numpy(), count.cpu().numpy()
+    cand = oracle.candidate_range(wl.N, wl.n_sink, wl.n_local)
+    keff = min(wl.k, cand.size)
+    G = wl.G
+    for b, g in _sample_heads(wl):
+        assert count[b, g] == keff
+        got = idx[b, g, :keff]
+        assert np.all(np.diff(got) > 0) and got[0] >= wl.n_sink and got[-1] < wl.N - wl.n_local
+        Kw = oracle.widen(d["kv"]["K"][b, g], wl.dtype)
+        qg = oracle.widen(d["q"][b, g * G:(g + 1) * G], wl.dtype)
+        want = oracle.exact_topk_group(qg, Kw, wl.N, wl.n_sink, wl.n_local, wl.k)
+        score = Kw[cand] @ qg.sum(axis=0)
+        band = 1e-5 * (np.abs(Kw[cand]) @ np.abs(qg).sum(axis=0))
+        kth = np.sort(score)[::-1][keff - 1]
+        sel = np.zeros(wl.N, bool)
+        sel[got] = True
+        assert sel[cand[score > kth + band]].all() and not sel[cand[score < kth - band]].any()
+        say(f"  head {(b, g)}: {len(np.setxor1d(got, want)) // 2} swaps inside the rounding band")
+
+
 @pytest.mark.parametrize("hidx", [0, 1])
 def test_workload4_prefill_encode_sampled_rows(hidx):
     """The key encode of all 4 x 4 x 262144 keys (the prefill), sampled rows."""
