@@ -29,7 +29,7 @@ constexpr int kMaxCpb = 8;                 // chunks per workgroup, bounded by r
 // compaction, first gather, combine) over more rows.
 constexpr int64_t kResidentBlocks = 768;
 
-template <int LPT, bool BF16, int G>
+template <int LPT, bool BF16, int G, int MAXC>
 __device__ __forceinline__ void emit_attend_body(
     const uint32_t *__restrict__ stash, const uint32_t *__restrict__ hist, int bins, int64_t C,
     int keff, int32_t *__restrict__ count, int S, int CPB, int Sc, int64_t lo, int k,
@@ -87,13 +87,13 @@ __device__ __forceinline__ void emit_attend_body(
     // derives its head's threshold, tie quota and the counts before each of its chunks
     // from the chunk histograms -- the same computation as the threshold kernel, done by
     // every workgroup of the head, which saves a kernel and its dependent round trip.
-    __shared__ uint32_t sw[kMaxCpb][LPT / 4][kScanThreads];
-    __shared__ int4 smt[kMaxCpb];
+    __shared__ uint32_t sw[MAXC][LPT / 4][kScanThreads];
+    __shared__ int4 smt[MAXC];
     int T, quota;
     {
-      uint32_t wl[kMaxCpb][LPT / 4];
+      uint32_t wl[MAXC][LPT / 4];
 #pragma unroll
-      for (int i = 0; i < kMaxCpb; ++i) {
+      for (int i = 0; i < MAXC; ++i) {
         const int ch = c0 + i < c1 ? c0 + i : c0;
         const uint32_t *sp = stash + ((int64_t)bh * S + ch) * stash_words_per_chunk<LPT>();
 #pragma unroll
@@ -108,14 +108,14 @@ __device__ __forceinline__ void emit_attend_body(
         head_threshold<64>(hist + (int64_t)bh * S * (64 + 8), Sb, C, CH, keff, T, quota, sink);
       if (c == 0 && t == 0) count[bh] = keff;
 #pragma unroll
-      for (int i = 0; i < kMaxCpb; ++i)
+      for (int i = 0; i < MAXC; ++i)
 #pragma unroll
         for (int i4 = 0; i4 < LPT / 4; ++i4) sw[i][i4][t] = wl[i][i4];
     }
     __syncthreads();
     int total = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxCpb; ++i)
+    for (int i = 0; i < MAXC; ++i)
       total += (i < nch && T >= 0) ? chunk_selected(smt[i], quota) : 0;
     if (total > 0 && total <= kListMax) {
       // All chunks compacted together: the block's selected tokens occupy positions
@@ -123,7 +123,7 @@ __device__ __forceinline__ void emit_attend_body(
       // index list afterwards, in coalesced stores.
       const int4 m0 = smt[0];
       const int first = m0.x + min(m0.y, quota);
-      emit_chunks_lanes<LPT, kMaxCpb>(sw, smt, nch, T, quota, lo + (int64_t)c0 * CH, first, sel);
+      emit_chunks_lanes<LPT, MAXC>(sw, smt, nch, T, quota, lo + (int64_t)c0 * CH, first, sel);
       for (int r = t; r < total; r += kScanThreads) out[first + r] = sel[r];
       attend_list(total);
     } else if (total > kListMax) {
@@ -176,36 +176,51 @@ __device__ __forceinline__ void emit_attend_body(
       n_local, max_ctx
 
 // bf16 (matrix cores): held to 168 VGPRs, three workgroups per CU.  fp32 (VALU) keeps
-// the compiler's choice: its accumulators would spill under that limit.
-template <int LPT, int G>
+// the compiler's choice: its accumulators would spill under that limit.  MAXC (8, or 4
+// when the plan puts at most 4 chunks in a workgroup) sizes the staged stash and the
+// compaction, which handle all MAXC slots at once.
+template <int LPT, int G, int MAXC>
 __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(3))) void
 emit_attend_bf16_kernel(HK_EMIT_ATTEND_PARAMS) {
-  emit_attend_body<LPT, true, G>(HK_EMIT_ATTEND_ARGS);
+  emit_attend_body<LPT, true, G, MAXC>(HK_EMIT_ATTEND_ARGS);
 }
-template <int LPT, int G>
+template <int LPT, int G, int MAXC>
 __global__ __launch_bounds__(kScanThreads) void emit_attend_f32_kernel(HK_EMIT_ATTEND_PARAMS) {
-  emit_attend_body<LPT, false, G>(HK_EMIT_ATTEND_ARGS);
+  emit_attend_body<LPT, false, G, MAXC>(HK_EMIT_ATTEND_ARGS);
 }
 #undef HK_EMIT_ATTEND_PARAMS
 #undef HK_EMIT_ATTEND_ARGS
+
+template <int LPT, bool BF16, int G, int MAXC>
+void fused_launch_c(const FusedPlan &p, const uint32_t *stash, const uint32_t *hist,
+                  int32_t *count, int k, int32_t *idx, const void *q, const void *kc,
+                  const void *vc, int Hq, int Hkv, int64_t cap, float scale_log2, float *po,
+                  float *pl, int64_t rows, const int32_t *ctx_len, hipStream_t st) {
+  if constexpr (BF16)
+    hipLaunchKernelGGL((emit_attend_bf16_kernel<LPT, G, MAXC>), dim3(p.parts, p.r.BH),
+                       dim3(kScanThreads), 0, st, stash, hist, p.r.BINS, p.r.C, p.r.keff, count,
+                       p.r.S, p.cpb, p.Sc, p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,
+                       p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows, ctx_len,
+                       p.n_local, p.max_ctx);
+  else
+    hipLaunchKernelGGL((emit_attend_f32_kernel<LPT, G, MAXC>), dim3(p.parts, p.r.BH),
+                       dim3(kScanThreads), 0, st, stash, hist, p.r.BINS, p.r.C, p.r.keff, count,
+                       p.r.S, p.cpb, p.Sc, p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,
+                       p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows, ctx_len,
+                       p.n_local, p.max_ctx);
+}
 
 template <int LPT, bool BF16, int G>
 void fused_launch(const FusedPlan &p, const uint32_t *stash, const uint32_t *hist,
                   int32_t *count, int k, int32_t *idx, const void *q, const void *kc,
                   const void *vc, int Hq, int Hkv, int64_t cap, float scale_log2, float *po,
                   float *pl, int64_t rows, const int32_t *ctx_len, hipStream_t st) {
-  if constexpr (BF16)
-    hipLaunchKernelGGL((emit_attend_bf16_kernel<LPT, G>), dim3(p.parts, p.r.BH),
-                       dim3(kScanThreads), 0, st, stash, hist, p.r.BINS, p.r.C, p.r.keff, count,
-                       p.r.S, p.cpb, p.Sc, p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,
-                       p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows, ctx_len,
-                       p.n_local, p.max_ctx);
+  if (p.cpb <= 4)
+    fused_launch_c<LPT, BF16, G, 4>(p, stash, hist, count, k, idx, q, kc, vc, Hq, Hkv, cap,
+                                    scale_log2, po, pl, rows, ctx_len, st);
   else
-    hipLaunchKernelGGL((emit_attend_f32_kernel<LPT, G>), dim3(p.parts, p.r.BH),
-                       dim3(kScanThreads), 0, st, stash, hist, p.r.BINS, p.r.C, p.r.keff, count,
-                       p.r.S, p.cpb, p.Sc, p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,
-                       p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows, ctx_len,
-                       p.n_local, p.max_ctx);
+    fused_launch_c<LPT, BF16, G, kMaxCpb>(p, stash, hist, count, k, idx, q, kc, vc, Hq, Hkv,
+                                          cap, scale_log2, po, pl, rows, ctx_len, st);
 }
 
 template <int LPT, bool BF16>
