@@ -29,7 +29,7 @@ constexpr int kMaxCpb = 8;                 // chunks per workgroup, bounded by r
 // compaction, first gather, combine) over more rows.
 constexpr int64_t kResidentBlocks = 768;
 
-template <int LPT, bool BF16, int G, int MAXC>
+template <int LPT, bool BF16, int G, int MAXC, int REPS>
 __device__ __forceinline__ void emit_attend_body(
     const uint32_t *__restrict__ stash, const uint32_t *__restrict__ hist, int bins, int64_t C,
     int keff, int32_t *__restrict__ count, int S, int CPB, int Sc, int64_t lo, int k,
@@ -74,80 +74,108 @@ __device__ __forceinline__ void emit_attend_body(
     ga.run_block(kc, vc, head_row0, len, [&](int r) { return sel[r]; });
   };
   if (c < Sc) {
-    // A shorter sequence spreads its Sb chunks over all Sc chunk workgroups of its head
-    // (Sb <= S <= Sc * CPB, so at most CPB each), not over the first Sb / CPB of them.
-    const int cpb = ctx_len ? (Sb + Sc - 1) / Sc : CPB;
-    const int c0 = c * cpb;
-    const int c1 = min(Sb, c0 + cpb);
-    int len = 0;
+    // Chunk workgroup c covers chunk groups c and, when REPS = 2, c + Sc of its head, one
+    // after the other: the head's threshold is derived once for both, and the two
+    // groups' tokens go into one online softmax (one partial per workgroup).  A group is
+    // CPB chunks; a shorter sequence spreads its Sb chunks over all Sc * REPS groups of
+    // its head (Sb <= S <= Sc * REPS * CPB, so at most CPB each).
+    const int ngroups = Sc * REPS;
+    const int cpb = ctx_len ? (Sb + ngroups - 1) / ngroups : CPB;
+    // chunks [g0(r), g1(r)) of group r; uniform over the workgroup
+    auto g0 = [&](int r) { return (c + r * Sc) * cpb; };
+    auto g1 = [&](int r) { return min(Sb, g0(r) + cpb); };
     int32_t *out = idx + (int64_t)bh * k;
-    const int nch = c1 - c0;
-    // Every chunk's stash words are requested first and staged in LDS (indexed by chunk
-    // at run time without scratch memory).  While they are in flight the workgroup
-    // derives its head's threshold, tie quota and the counts before each of its chunks
-    // from the chunk histograms -- the same computation as the threshold kernel, done by
-    // every workgroup of the head, which saves a kernel and its dependent round trip.
+    // A group's stash words are staged in LDS (indexed by chunk at run time without
+    // scratch memory).  The first group's are requested before the threshold is derived,
+    // and arrive while it is.
     __shared__ uint32_t sw[MAXC][LPT / 4][kScanThreads];
-    __shared__ int4 smt[MAXC];
-    int T, quota;
-    {
-      uint32_t wl[MAXC][LPT / 4];
+    __shared__ int4 smt[REPS][MAXC];
+    auto load_stash = [&](int r, uint32_t(&wl)[MAXC][LPT / 4]) {
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
-        const int ch = c0 + i < c1 ? c0 + i : c0;
+        int ch = g0(r) + i < g1(r) ? g0(r) + i : g0(r);
+        ch = ch < S ? ch : S - 1;                // an empty group past the last chunk
         const uint32_t *sp = stash + ((int64_t)bh * S + ch) * stash_words_per_chunk<LPT>();
 #pragma unroll
         for (int i4 = 0; i4 < LPT / 4; ++i4) wl[i][i4] = sp[i4 * kScanThreads + t];
       }
+    };
+    auto stage_stash = [&](const uint32_t(&wl)[MAXC][LPT / 4]) {
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i)
+#pragma unroll
+        for (int i4 = 0; i4 < LPT / 4; ++i4) sw[i][i4][t] = wl[i][i4];
+    };
+    // The head's threshold, tie quota and the counts before each chunk of the groups,
+    // from the chunk histograms -- the computation of the threshold kernel, done by
+    // every workgroup of the head, which saves a kernel and its dependent round trip.
+    int T, quota;
+    {
+      uint32_t wl[MAXC][LPT / 4];
+      load_stash(0, wl);
       auto sink = [&](int cc, const int4 &m) {
-        if (cc >= c0 && cc < c1) smt[cc - c0] = m;
+#pragma unroll
+        for (int r = 0; r < REPS; ++r)
+          if (cc >= g0(r) && cc < g1(r)) smt[r][cc - g0(r)] = m;
       };
       if (bins == 128)
         head_threshold<128>(hist + (int64_t)bh * S * (128 + 16), Sb, C, CH, keff, T, quota, sink);
       else
         head_threshold<64>(hist + (int64_t)bh * S * (64 + 8), Sb, C, CH, keff, T, quota, sink);
       if (c == 0 && t == 0) count[bh] = keff;
-#pragma unroll
-      for (int i = 0; i < MAXC; ++i)
-#pragma unroll
-        for (int i4 = 0; i4 < LPT / 4; ++i4) sw[i][i4][t] = wl[i][i4];
+      stage_stash(wl);
     }
     __syncthreads();
-    int total = 0;
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i)
-      total += (i < nch && T >= 0) ? chunk_selected(smt[i], quota) : 0;
-    if (total > 0 && total <= kListMax) {
-      // All chunks compacted together: the block's selected tokens occupy positions
-      // [first, first + total) of the head's list.  The list goes to LDS first and to the
-      // index list afterwards, in coalesced stores.
-      const int4 m0 = smt[0];
-      const int first = m0.x + min(m0.y, quota);
-      emit_chunks_lanes<LPT, MAXC>(sw, smt, nch, T, quota, lo + (int64_t)c0 * CH, first, sel);
-      for (int r = t; r < total; r += kScanThreads) out[first + r] = sel[r];
-      attend_list(total);
-    } else if (total > kListMax) {
-      // Too many for the list: chunk by chunk, attending whenever the list would overflow.
-      for (int i = 0; i < nch; ++i) {
-        const int4 mt = smt[i];
-        const int nsel = chunk_selected(mt, quota);
-        if (nsel == 0) continue;
-        if (len + nsel > kListMax) {
-          attend_list(len);
-          __syncthreads();                   // the list is reused
-          len = 0;
-        }
-        const int base = len - (mt.x + min(mt.y, quota));   // list slot = base + position
-        emit_chunks<LPT, 1>([&](int, int kk) { return sw[i][kk][t]; }, [&](int) { return mt; },
-                            1, T, quota, lo + (int64_t)(c0 + i) * CH,
-                            [&](int pos, int32_t tok) {
-                              out[pos] = tok;
-                              sel[base + pos] = tok;
-                            });
+    for (int r = 0; r < REPS; ++r) {
+      if (r > 0) {
+        // Every wavefront is done with the previous group's list and stash.
         __syncthreads();
-        len += nsel;
+        uint32_t wl[MAXC][LPT / 4];
+        load_stash(r, wl);
+        stage_stash(wl);
+        __syncthreads();
       }
-      if (len > 0) attend_list(len);
+      const int c0 = g0(r);
+      const int nch = g1(r) - c0;
+      const int4 *mt_r = smt[r];
+      int total = 0;
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i)
+        total += (i < nch && T >= 0) ? chunk_selected(mt_r[i], quota) : 0;
+      if (total > 0 && total <= kListMax) {
+        // All chunks compacted together: the group's selected tokens occupy positions
+        // [first, first + total) of the head's list.  The list goes to LDS first and to
+        // the index list afterwards, in coalesced stores.
+        const int4 m0 = mt_r[0];
+        const int first = m0.x + min(m0.y, quota);
+        emit_chunks_lanes<LPT, MAXC>(sw, mt_r, nch, T, quota, lo + (int64_t)c0 * CH, first, sel);
+        for (int rr = t; rr < total; rr += kScanThreads) out[first + rr] = sel[rr];
+        attend_list(total);
+      } else if (total > kListMax) {
+        // Too many for the list: chunk by chunk, attending whenever the list would overflow.
+        int len = 0;
+        for (int i = 0; i < nch; ++i) {
+          const int4 mt = mt_r[i];
+          const int nsel = chunk_selected(mt, quota);
+          if (nsel == 0) continue;
+          if (len + nsel > kListMax) {
+            attend_list(len);
+            __syncthreads();                   // the list is reused
+            len = 0;
+          }
+          const int base = len - (mt.x + min(mt.y, quota));   // list slot = base + position
+          emit_chunks<LPT, 1>([&](int, int kk) { return sw[i][kk][t]; }, [&](int) { return mt; },
+                              1, T, quota, lo + (int64_t)(c0 + i) * CH,
+                              [&](int pos, int32_t tok) {
+                                out[pos] = tok;
+                                sel[base + pos] = tok;
+                              });
+          __syncthreads();
+          len += nsel;
+        }
+        if (len > 0) attend_list(len);
+      }
     }
     if (!ga_ready) ga.init(q, row0, scale_log2);
   } else {
@@ -178,32 +206,34 @@ __device__ __forceinline__ void emit_attend_body(
 // bf16 (matrix cores): held to 168 VGPRs, three workgroups per CU.  fp32 (VALU) keeps
 // the compiler's choice: its accumulators would spill under that limit.  MAXC (8, or 4
 // when the plan puts at most 4 chunks in a workgroup) sizes the staged stash and the
-// compaction, which handle all MAXC slots at once.
-template <int LPT, int G, int MAXC>
+// compaction, which handle all MAXC slots at once.  REPS (1 or 2) chunk groups per
+// chunk workgroup: 2 when one group of 8 chunks per workgroup would need more workgroups
+// than are resident at once.
+template <int LPT, int G, int MAXC, int REPS>
 __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(3))) void
 emit_attend_bf16_kernel(HK_EMIT_ATTEND_PARAMS) {
-  emit_attend_body<LPT, true, G, MAXC>(HK_EMIT_ATTEND_ARGS);
+  emit_attend_body<LPT, true, G, MAXC, REPS>(HK_EMIT_ATTEND_ARGS);
 }
-template <int LPT, int G, int MAXC>
+template <int LPT, int G, int MAXC, int REPS>
 __global__ __launch_bounds__(kScanThreads) void emit_attend_f32_kernel(HK_EMIT_ATTEND_PARAMS) {
-  emit_attend_body<LPT, false, G, MAXC>(HK_EMIT_ATTEND_ARGS);
+  emit_attend_body<LPT, false, G, MAXC, REPS>(HK_EMIT_ATTEND_ARGS);
 }
 #undef HK_EMIT_ATTEND_PARAMS
 #undef HK_EMIT_ATTEND_ARGS
 
-template <int LPT, bool BF16, int G, int MAXC>
+template <int LPT, bool BF16, int G, int MAXC, int REPS>
 void fused_launch_c(const FusedPlan &p, const uint32_t *stash, const uint32_t *hist,
                   int32_t *count, int k, int32_t *idx, const void *q, const void *kc,
                   const void *vc, int Hq, int Hkv, int64_t cap, float scale_log2, float *po,
                   float *pl, int64_t rows, const int32_t *ctx_len, hipStream_t st) {
   if constexpr (BF16)
-    hipLaunchKernelGGL((emit_attend_bf16_kernel<LPT, G, MAXC>), dim3(p.parts, p.r.BH),
+    hipLaunchKernelGGL((emit_attend_bf16_kernel<LPT, G, MAXC, REPS>), dim3(p.parts, p.r.BH),
                        dim3(kScanThreads), 0, st, stash, hist, p.r.BINS, p.r.C, p.r.keff, count,
                        p.r.S, p.cpb, p.Sc, p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,
                        p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows, ctx_len,
                        p.n_local, p.max_ctx);
   else
-    hipLaunchKernelGGL((emit_attend_f32_kernel<LPT, G, MAXC>), dim3(p.parts, p.r.BH),
+    hipLaunchKernelGGL((emit_attend_f32_kernel<LPT, G, MAXC, REPS>), dim3(p.parts, p.r.BH),
                        dim3(kScanThreads), 0, st, stash, hist, p.r.BINS, p.r.C, p.r.keff, count,
                        p.r.S, p.cpb, p.Sc, p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,
                        p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows, ctx_len,
@@ -216,11 +246,14 @@ void fused_launch(const FusedPlan &p, const uint32_t *stash, const uint32_t *his
                   const void *vc, int Hq, int Hkv, int64_t cap, float scale_log2, float *po,
                   float *pl, int64_t rows, const int32_t *ctx_len, hipStream_t st) {
   if (p.cpb <= 4)
-    fused_launch_c<LPT, BF16, G, 4>(p, stash, hist, count, k, idx, q, kc, vc, Hq, Hkv, cap,
-                                    scale_log2, po, pl, rows, ctx_len, st);
+    fused_launch_c<LPT, BF16, G, 4, 1>(p, stash, hist, count, k, idx, q, kc, vc, Hq, Hkv, cap,
+                                       scale_log2, po, pl, rows, ctx_len, st);
+  else if (p.reps == 2)
+    fused_launch_c<LPT, BF16, G, kMaxCpb, 2>(p, stash, hist, count, k, idx, q, kc, vc, Hq, Hkv,
+                                             cap, scale_log2, po, pl, rows, ctx_len, st);
   else
-    fused_launch_c<LPT, BF16, G, kMaxCpb>(p, stash, hist, count, k, idx, q, kc, vc, Hq, Hkv,
-                                          cap, scale_log2, po, pl, rows, ctx_len, st);
+    fused_launch_c<LPT, BF16, G, kMaxCpb, 1>(p, stash, hist, count, k, idx, q, kc, vc, Hq, Hkv,
+                                             cap, scale_log2, po, pl, rows, ctx_len, st);
 }
 
 template <int LPT, bool BF16>
@@ -271,11 +304,20 @@ FusedPlan plan_fused(int bits, int B, int Hq, int Hkv, int64_t n_ctx, int n_sink
     cpb *= 2;
   p.cpb = cpb;
   p.Sc = (p.r.S + cpb - 1) / cpb;
+  p.reps = 1;
   // Window slices of about as many rows as a chunk workgroup attends (at least 64), of
   // equal size.
   const int64_t target = per_chunk * cpb > 64 ? per_chunk * cpb : 64;
   p.Sw = (int)((p.n_win + target - 1) / target);
   p.win_rows = p.Sw > 0 ? (int)((p.n_win + p.Sw - 1) / p.Sw) : 64;
+  // Two groups of 8 chunks per chunk workgroup when one would need more workgroups than
+  // are resident at once: the head's threshold is derived once for both groups, and the
+  // serial phase is not paid again by a second round of workgroups (16 x 131072 tokens,
+  // 8 KV heads: 768 workgroups in one round instead of 1280, select+attend 65 -> 58 us).
+  if (p.cpb == kMaxCpb && p.Sc >= 2 && (int64_t)p.r.BH * (p.Sc + p.Sw) > kResidentBlocks) {
+    p.reps = 2;
+    p.Sc = (p.Sc + 1) / 2;
+  }
   p.parts = p.Sc + p.Sw;
   size_t off = p.r.total;
   const size_t rows = (size_t)B * Hq;

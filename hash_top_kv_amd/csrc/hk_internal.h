@@ -104,6 +104,7 @@ hipError_t launch_lse_merge_parts(const float *o_parts, const float *lse_parts, 
 struct FusedPlan {
   RetrievePlan r;
   int win_sinks = 0, n_win = 0, win_rows = 64, Sw = 0, parts = 0, G = 1, cpb = 1, Sc = 0;
+  int reps = 1;                  // chunk groups per chunk workgroup (1 or 2)
   int64_t win_local0 = 0, n_local = 0, max_ctx = 0;
   size_t off_o = 0, off_lse = 0, total = 0;
 };
