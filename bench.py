@@ -30,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -49,11 +50,22 @@ KERNEL_SOURCES = ["include/hk.h", "hash_top_kv_amd/csrc/hk_internal.h",
                   "hash_top_kv_amd/csrc/api.hip"]
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments or layout: edits to comments keep the digest."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(files=KERNEL_SOURCES) -> str:
+    """Digest of what the kernels are built from: the sources (comments aside) and the
+    build script with its compiler flags."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
+    with open(os.path.join(ROOT, "hash_top_kv_amd", "build.py"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 

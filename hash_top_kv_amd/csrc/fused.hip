@@ -1,12 +1,13 @@
 // Fused top-k select + exact attention over the selected tokens, for one decode step.
 //
-// After the Hamming scan, each chunk's workgroup derives its head's distance threshold
+// After the Hamming scan, each chunk workgroup derives its head's distance threshold
 // from the chunk histograms, compacts its selected tokens (writing them to the head's
 // ascending index list, as hk_topk_select does, and to LDS), gathers their K/V rows and
-// computes the partial attention of the G query heads of its KV head over them.  Extra workgroups do the same over slices of the static
-// sink + local window.  The partials of a head -- disjoint token sets -- are then merged
-// by log-sum-exp rescaling (RetrievalAttention, atlas summary: Approach), which gives
-// attention over the selected tokens and the window together.
+// computes the partial attention of the G query heads of its KV head over them.  Window
+// workgroups do the same over slices of the static sink + local window.  The partials of
+// a head -- disjoint token sets -- are then merged by log-sum-exp rescaling
+// (RetrievalAttention, atlas summary: Approach), which gives attention over the selected
+// tokens and the window together.
 //
 // Compared with threshold -> emit -> sparse decode -> merge, this saves two kernels and
 // their dependent memory round trips (the threshold's outputs, the index list) on the
@@ -17,11 +18,12 @@
 namespace hk {
 namespace {
 
-// grid (Sc + Sw, B*Hkv), after the Hamming scan.  Blocks c < Sc cover chunks
-// [c*CPB, (c+1)*CPB) of the retrieval; blocks c >= Sc cover window slice c - Sc.  Block c writes the normalised
-// partial of part c.  A chunk block compacts its chunks' selected tokens into an LDS
-// list (and into the head's index list) and attends over the list; when a list would
-// overflow LDS it is attended and emptied first, so any selection size works.
+// grid (Sc + Sw, B*Hkv), after the Hamming scan.  Block c < Sc covers chunk group c (and
+// c + Sc when REPS = 2) of the head, a group being chunks [g*CPB, (g+1)*CPB); blocks
+// c >= Sc cover window slice c - Sc.  Block c writes the normalised partial of part c.
+// A chunk block compacts its chunks' selected tokens into an LDS list (and into the
+// head's index list) and attends over the list; when a list would overflow LDS it is
+// attended and emptied first, so any selection size works.
 constexpr int kListMax = 4096;
 constexpr int kMaxCpb = 8;                 // chunks per workgroup, bounded by registers
 // Workgroups resident at once at this kernel's register use (3 per CU).  Beyond that,
