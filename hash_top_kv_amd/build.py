@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhk.so")
-SOURCES = ["api.hip", "retrieve.hip", "attend.hip", "fused.hip", "encode.hip", "evict.hip", "exact.hip"]
+SOURCES = ["api.hip", "retrieve.hip", "attend.hip", "fused.hip", "encode.hip", "evict.hip", "exact.hip",
+           "probe.hip"]
 ARCH = "gfx950"
 # The attention kernels keep their matrix-core accumulators in ordinary VGPRs: the
 # online-softmax rescale multiplies them in place, which with accumulation registers

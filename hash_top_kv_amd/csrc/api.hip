@@ -384,4 +384,15 @@ hk_status hk_retrieve_attend_varlen(const uint32_t *codes, const uint32_t *qcode
   return from_hip(e);
 }
 
+size_t hk_read_probe_sink_words(size_t bytes) { return (size_t)read_probe_blocks(bytes); }
+
+hk_status hk_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+  if (bytes % 16 != 0) return HK_ERR_INVALID_ARGUMENT;
+  if (bytes == 0) return HK_OK;
+  if (!src || !sink) return HK_ERR_INVALID_ARGUMENT;
+  if (!aligned(src, 16)) return HK_ERR_UNSUPPORTED;
+  if (read_probe_blocks(bytes) > 0x7FFFFFFF) return HK_ERR_UNSUPPORTED;
+  return from_hip(launch_read_probe(src, bytes, sink, as_stream(stream)));
+}
+
 }  // extern "C"

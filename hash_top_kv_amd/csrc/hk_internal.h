@@ -101,6 +101,11 @@ hipError_t launch_lse_merge_parts(const float *o_parts, const float *lse_parts, 
 // hk_retrieve_attend: the retrieval workspace (RetrievePlan) followed by one normalised
 // partial per group of `cpb` chunks of each head and per window slice: o [parts][B*Hq][d],
 // lse [parts][B*Hq], parts = Sc + Sw.
+// A plain streaming read of bytes (multiple of 16) from src; sink receives
+// read_probe_blocks(bytes) words.
+int64_t read_probe_blocks(size_t bytes);
+hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, hipStream_t st);
+
 struct FusedPlan {
   RetrievePlan r;
   int win_sinks = 0, n_win = 0, win_rows = 64, Sw = 0, parts = 0, G = 1, cpb = 1, Sc = 0;

@@ -323,6 +323,17 @@ hk_status hk_retrieve_attend_varlen(const uint32_t *codes, const uint32_t *qcode
                                     int32_t *count, float *o, float *lse, void *ws,
                                     size_t ws_bytes, void *stream);
 
+/* Measurement aid, not a step of the decode path: a plain streaming read of `bytes`
+ * (a multiple of 16) from device memory src (16-byte aligned) with 16-byte non-temporal
+ * loads, one pass of 32 KB per workgroup (the Hamming scan's access pattern): the rate
+ * that the kernels' bandwidth figures are compared with beside the spec peak.
+ *   sink  device uint32 array of hk_read_probe_sink_words(bytes) entries (written: the
+ *         XOR of the words each workgroup read, so the loads are kept).
+ * Errors: bytes not a multiple of 16, or NULL src / sink with bytes > 0 ->
+ * INVALID_ARGUMENT; src not 16-byte aligned -> UNSUPPORTED; bytes = 0 enqueues nothing. */
+size_t hk_read_probe_sink_words(size_t bytes);
+hk_status hk_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

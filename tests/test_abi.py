@@ -163,6 +163,18 @@ def test_host_validation_without_gpu(hk):
     assert L.hk_window_indices(-1, 4, 64, P, ctypes.byref(n), P) == hk.HK_ERR_INVALID_ARGUMENT
 
 
+def test_read_probe_host_checks(hk):
+    """The read probe rejects sizes that are not whole 16-byte vectors and missing
+    pointers on the host; zero bytes enqueue nothing."""
+    L = hk.lib()
+    assert L.hk_read_probe_sink_words(1 << 30) == (1 << 30) // 32768
+    assert L.hk_read_probe_sink_words(16) == 1
+    assert L.hk_read_probe(None, 24, None, None) == 1          # not a multiple of 16
+    assert L.hk_read_probe(None, 32, None, None) == 1          # NULL src / sink
+    assert L.hk_read_probe(None, 0, None, None) == 0           # nothing to read
+    assert L.hk_read_probe(ctypes.c_void_p(0x1008), 32, ctypes.c_void_p(0x2000), None) == 2
+
+
 def test_workspace_sizes_grow_with_the_problem(hk):
     a = hk.retrieve_topk_workspace(128, 1, 8, 100000, 4, 64, 100)
     b = hk.retrieve_topk_workspace(128, 1, 8, 200000, 4, 64, 100)

@@ -542,3 +542,19 @@ def test_retrieve_attend_varlen_matches_oracle_per_sequence(case):
         torch.cuda.synchronize()
         assert np.array_equal(o2.cpu().numpy(), o) and np.array_equal(l2.cpu().numpy(), lse)
         assert np.array_equal(c2.cpu().numpy(), cnt)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 3 * (1 << 20) + 16 * 7, 64 << 20])
+def test_read_probe_reads_every_byte(nbytes):
+    """The measurement probe reads the whole buffer: the XOR of its per-workgroup words is
+    the XOR of every 32-bit word of the buffer."""
+    say(f"read_probe {nbytes} bytes")
+    rng = np.random.default_rng(nbytes % 1000)
+    data = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
+    x = torch.from_numpy(data.view(np.int32)).cuda()
+    sink = hk.read_probe(x)
+    torch.cuda.synchronize()
+    words = int(hk.lib().hk_read_probe_sink_words(nbytes))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)[:words])
+    assert got == np.bitwise_xor.reduce(data)
+
