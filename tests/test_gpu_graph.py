@@ -22,9 +22,9 @@ def _lib():
     hk = hash_top_kv_amd
 
 
-@pytest.mark.parametrize("variant", ["fused", "unfused", "qheads"])
+@pytest.mark.parametrize("variant", ["fused", "unfused", "qheads", "varlen"])
 def test_graph_replays_equal_eager(variant):
-    from hash_top_kv_amd.step import DecodeStep, QHeadStep
+    from hash_top_kv_amd.step import DecodeStep, QHeadStep, VarlenDecodeStep
     say(f"graph replay, {variant} step")
     wl = synth.scaled(synth.WORKLOADS[1], B=2, Hq=8, Hkv=2, N=20000, k=400)
     spec = wl.hashes[0]
@@ -36,6 +36,10 @@ def test_graph_replays_equal_eager(variant):
     Qs = [synth.to_device(synth.make_q(wl, replica=r), wl.dtype) for r in range(3)]
     if variant == "qheads":
         mk = lambda: QHeadStep(K, V, codes, spec.bits, wl.N, wl.n_sink, wl.n_local, wl.k, wl.Hq, h)
+    elif variant == "varlen":
+        ctx_len = torch.tensor([wl.N, wl.N // 3], dtype=torch.int32, device="cuda")
+        mk = lambda: VarlenDecodeStep(K, V, codes, spec.bits, ctx_len, wl.N, wl.n_sink,
+                                      wl.n_local, wl.k, wl.Hq, h)
     else:
         mk = lambda: DecodeStep(K, V, codes, spec.bits, wl.N, wl.n_sink, wl.n_local, wl.k, wl.Hq, h)
     steps = [mk(), mk(), mk()]
