@@ -34,6 +34,7 @@ namespace {
 // distance bytes (16 x 8 heads x 131072 tokens) the scan takes 47.5 us against 49.2 with
 // ordinary stores, with 4.2 MB (8 x 524288) 13.0 against 12.4 -- so the launch picks
 // non-temporal stores when the distance bytes exceed a quarter of the 32 MB of L2.
+constexpr int64_t kStashNtBytes = 8 << 20;
 template <int W, int LPT, bool NT_STASH>
 __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
     const uint32_t *__restrict__ codes, const uint32_t *__restrict__ qcodes, int64_t cap,
@@ -172,7 +173,7 @@ __global__ void window_indices_kernel(int32_t n_sinks, int64_t local0, int32_t n
 // (per-query-head selection): each code is read once and compared with every query code
 // of the group; query head g of the group gets its own distance stash and histograms,
 // laid out as if it were a head of its own (head index bh*G + g).
-template <int W, int LPT, int G>
+template <int W, int LPT, int G, bool NT_STASH>
 __global__ __launch_bounds__(kScanThreads) void hamming_scan_group_kernel(
     const uint32_t *__restrict__ codes, const uint32_t *__restrict__ qcodes, int64_t cap,
     int64_t lo, int64_t C, int S, uint32_t *__restrict__ stash, uint32_t *__restrict__ hist_out) {
@@ -222,7 +223,10 @@ __global__ __launch_bounds__(kScanThreads) void hamming_scan_group_kernel(
         }
         packed |= d << (8 * j);
       }
-      st[i4 * kScanThreads + t] = packed;
+      if constexpr (NT_STASH)
+        __builtin_nontemporal_store(packed, st + i4 * kScanThreads + t);
+      else
+        st[i4 * kScanThreads + t] = packed;
     }
   }
   __syncthreads();
@@ -251,10 +255,16 @@ void scan_group_launch(const RetrievePlan &p, int G, const uint32_t *codes,
                        const uint32_t *qcodes, int64_t cap, uint32_t *stash, uint32_t *hist,
                        hipStream_t st) {
   const dim3 grid(p.S, p.BH / G), blk(kScanThreads);
+  // p.BH counts query heads here: the distance bytes of all of them
+  const bool nt = (int64_t)p.BH * p.S * p.ch > kStashNtBytes;
 #define HK_GS(GG)                                                                            \
   case GG:                                                                                   \
-    hipLaunchKernelGGL((hamming_scan_group_kernel<W, LPT, GG>), grid, blk, 0, st, codes,     \
-                       qcodes, cap, p.lo, p.C, p.S, stash, hist);                            \
+    if (nt)                                                                                  \
+      hipLaunchKernelGGL((hamming_scan_group_kernel<W, LPT, GG, true>), grid, blk, 0, st,    \
+                         codes, qcodes, cap, p.lo, p.C, p.S, stash, hist);                   \
+    else                                                                                     \
+      hipLaunchKernelGGL((hamming_scan_group_kernel<W, LPT, GG, false>), grid, blk, 0, st,   \
+                         codes, qcodes, cap, p.lo, p.C, p.S, stash, hist);                   \
     break;
   switch (G) { HK_GS(2) HK_GS(3) HK_GS(4) HK_GS(5) HK_GS(6) HK_GS(7) HK_GS(8) default: break; }
 #undef HK_GS
@@ -264,7 +274,6 @@ template <int W, int LPT>
 void scan_launch(const RetrievePlan &p, const uint32_t *codes, const uint32_t *qcodes,
                  int64_t cap, uint32_t *stash, uint32_t *hist, const int32_t *ctx_len, int Hkv,
                  int64_t n_local, int64_t max_ctx, hipStream_t st) {
-  constexpr int64_t kStashNtBytes = 8 << 20;
   if ((int64_t)p.BH * p.S * p.ch > kStashNtBytes)
     hipLaunchKernelGGL((hamming_scan_kernel<W, LPT, true>), dim3(p.S, p.BH), dim3(kScanThreads),
                        0, st, codes, qcodes, cap, p.lo, p.C, p.S, stash, hist, ctx_len, Hkv,
