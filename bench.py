@@ -508,8 +508,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the step shards by (batch, KV head) with no exchange; see the design notes)",
+        print("bench.py measures one GPU: the library has no multi-GPU path (the step would "
+              "shard by (batch, KV head), with no exchange inside a step)",
               file=sys.stderr)
         sys.exit(2)
 
