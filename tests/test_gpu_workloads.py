@@ -113,8 +113,8 @@ def _encode_and_check(wl, spec, hidx, sample):
     return h, hnp, hp, codes, ref_codes
 
 
-def _run_workload(wid, hidx=0, spec=None):
-    wl = synth.WORKLOADS[wid]
+def _run_workload(wid, hidx=0, spec=None, k=None):
+    wl = synth.WORKLOADS[wid] if k is None else synth.scaled(synth.WORKLOADS[wid], k=k)
     spec = spec or wl.hashes[hidx]
     sample = _sample_heads(wl)
     d = _inputs(wid)
@@ -158,6 +158,12 @@ def test_workload1_llama3_8b_mlp128():
 
 def test_workload3_batch16_131072_mlp128():
     _run_workload(3)
+
+
+def test_workload3_large_budget():
+    """The batch-16 workload with k = 40000: two chunk groups per workgroup, each group
+    selecting about 5000 tokens, more than the workgroup's list holds at once."""
+    _run_workload(3, k=40000)
 
 
 def test_workload3_sign_codes():
