@@ -558,3 +558,40 @@ def test_read_probe_reads_every_byte(nbytes):
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)[:words])
     assert got == np.bitwise_xor.reduce(data)
 
+
+def test_retrieve_attend_fp32_two_chunk_groups():
+    """fp32 K/V at the batch-16 x 131072 shape (8 KV heads, 32 query heads, sink 4 + local
+    512, top-2%), where the fused step runs two chunk groups per workgroup: sampled heads
+    against the oracle (top-k bit for bit, attention within the fp32 bound).  Inputs are
+    drawn on the device."""
+    B, Hkv, G, N, s, w, k = 16, 8, 4, 131072, 4, 512, 2621
+    Hq = Hkv * G
+    say("retrieve_attend fp32, 16 x 8 x 131072, two chunk groups per workgroup")
+    gen = torch.Generator(device="cuda").manual_seed(123)
+    K = torch.randn((B, Hkv, N, 128), generator=gen, device="cuda")
+    V = torch.randn((B, Hkv, N, 128), generator=gen, device="cuda")
+    q = torch.randn((B, Hq, 128), generator=gen, device="cuda")
+    codes = torch.randint(-2 ** 31, 2 ** 31 - 1, (B, Hkv, N, 4), generator=gen, device="cuda",
+                          dtype=torch.int32)
+    qc = torch.randint(-2 ** 31, 2 ** 31 - 1, (B, Hkv, 4), generator=gen, device="cuda",
+                       dtype=torch.int32)
+    o, lse, idx, count = hk.retrieve_attend(codes, qc, 128, q, K, V, N, s, w, k)
+    torch.cuda.synchronize()
+    o, lse, idx, count = (t.cpu().numpy() for t in (o, lse, idx, count))
+    scale = 1 / np.sqrt(128)
+    win = oracle.window_indices(N, s, w)
+    for b, g in [(0, 0), (15, 7), (9, 3)]:
+        cc = np_u32(codes[b, g])
+        want = oracle.select_topk(cc, np_u32(qc[b, g]), N, s, w, k)
+        assert count[b, g] == want.size and np.array_equal(idx[b, g, :want.size], want), (b, g)
+        Kf = K[b, g].double().cpu().numpy()
+        Vf = V[b, g].double().cpu().numpy()
+        for h in range(G):
+            qh = q[b, g * G + h].double().cpu().numpy()
+            o1, l1 = oracle.attend(qh, Kf[want], Vf[want], scale)
+            o2, l2 = oracle.attend(qh, Kf[win], Vf[win], scale)
+            ro, rl = oracle.lse_merge(np.stack([o1, o2]), np.array([l1, l2]))
+            assert np.max(np.abs(o[b, g * G + h] - ro)) <= 1e-5 and abs(lse[b, g * G + h] - rl) <= 1e-5
+    del K, V
+    torch.cuda.empty_cache()
+
