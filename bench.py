@@ -89,6 +89,31 @@ def stream_read_rate(torch, hk, mib=1024, reps=20):
             "how": "hk_read_probe: 1 GiB, 16-byte non-temporal loads, 20 launches back to back"}
 
 
+def same_size_read_rate(torch, hk, nbytes, reps=200):
+    """hk_read_probe over exactly nbytes (the scan's algorithmic bytes), launched back to
+    back over buffers rotated through 1 GiB so that no launch finds its data in a cache:
+    what a pure read of that size reaches, launch ramp and drain included."""
+    n = nbytes - nbytes % 16
+    if n <= 0:
+        return None
+    R = min(64, max(1, -(-(1 << 30) // n)))
+    bufs = [torch.ones(n // 4, dtype=torch.int32, device="cuda") for _ in range(R)]
+    sink = hk.read_probe(bufs[0])
+    for i in range(2 * R):
+        hk.read_probe(bufs[i % R], sink)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        hk.read_probe(bufs[i % R], sink)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return {"bytes": n, "us_per_launch": round(ms * 1e3, 3), "gbs": round(n / ms / 1e6, 1),
+            "how": f"hk_read_probe: {n} bytes, {R} rotating buffers, {reps} launches back to back"}
+
+
 def read_traffic(name: str):
     """HBM bytes per launch of a kernel from a committed counter summary, if the kernel
     sources have not changed since it was taken (else None)."""
@@ -664,6 +689,10 @@ def main():
                     "alg_bytes_per_launch": sc["alg_bytes"], "us_per_launch": sc["us_per_launch"]}
         if stream:
             roofline["frac_of_measured_read"] = round(a / stream["gbs"], 4)
+            same = same_size_read_rate(torch, hk, sc["alg_bytes"])
+            if same:
+                stream["same_size_as_scan"] = same
+                roofline["frac_of_same_size_read"] = round(a / same["gbs"], 4)
     out = {"metric": METRIC, "value": round(ms_step * 1e3, 3), "unit": "us/step", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
            "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
