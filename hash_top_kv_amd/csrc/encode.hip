@@ -325,6 +325,28 @@ __global__ __launch_bounds__(1024) void encode_query_mfma_kernel(HashPtrs hp,
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int n = lane & 15, g = lane >> 4;
   const bool has1 = wave < NT1, has2 = MLP && wave < NT2;
+  // Group means: thread t -> row t/64, dims 2*(t%64), +1.  The query rows are requested
+  // before the weights, so that the two round trips to memory overlap; all G <= 8 loads
+  // are in flight before any is summed.
+  const int rr = t >> 6, e0 = 2 * (t & 63);
+  const int G = Hq / Hkv;
+  uint32_t qv[kMaxGroup];
+  {
+    const int64_t r = r0 + rr;
+    const int64_t b = r / Hkv, hg = r - b * Hkv;
+#pragma unroll
+    for (int j = 0; j < kMaxGroup; ++j)
+      qv[j] = (r < rows && j < G)
+                  ? *reinterpret_cast<const uint32_t *>(q + (size_t)((b * Hq + hg * G + j) * D + e0))
+                  : 0u;
+  }
+  // The MLP's biases for this lane's columns, requested with the rest.
+  float bias1 = 0.f, bias2 = 0.f;
+  if constexpr (MLP) {
+    const int col = 16 * wave + n;
+    if (has1 && hp.b1) bias1 = elem<true>(hp.b1, col);
+    if (has2 && hp.b2) bias2 = elem<true>(hp.b2, col);
+  }
   {
     constexpr int C1 = N1 * D / 8, C2 = MLP ? BITS * NH / 8 : 0;   // 16-byte vectors
     constexpr int L1 = (C1 + 1023) / 1024, L2 = (C2 + 1023) / 1024;
@@ -358,23 +380,13 @@ __global__ __launch_bounds__(1024) void encode_query_mfma_kernel(HashPtrs hp,
     }
   }
   if (t < kQTile * W) words[t / W][t % W] = 0u;
-  // Group means: thread t -> row t/64, dims 2*(t%64), +1.  All G <= 8 loads are issued
-  // before any is summed.
   {
-    const int rr = t >> 6, e0 = 2 * (t & 63);
-    const int64_t r = r0 + rr;
     float acc0 = 0.f, acc1 = 0.f;
-    if (r < rows) {
-      const int64_t b = r / Hkv, hg = r - b * Hkv;
-      const int G = Hq / Hkv;
-      uint32_t v[kMaxGroup];
-#pragma unroll
-      for (int j = 0; j < kMaxGroup; ++j)
-        v[j] = j < G ? *reinterpret_cast<const uint32_t *>(q + (size_t)((b * Hq + hg * G + j) * D + e0)) : 0u;
+    if (r0 + rr < rows) {
 #pragma unroll
       for (int j = 0; j < kMaxGroup; ++j) {
-        acc0 += __uint_as_float(v[j] << 16);
-        acc1 += __uint_as_float(v[j] & 0xFFFF0000u);
+        acc0 += __uint_as_float(qv[j] << 16);
+        acc1 += __uint_as_float(qv[j] & 0xFFFF0000u);
       }
       acc0 = acc0 / (float)G;
       acc1 = acc1 / (float)G;
@@ -400,9 +412,8 @@ __global__ __launch_bounds__(1024) void encode_query_mfma_kernel(HashPtrs hp,
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p2, bw, acc, 0, 0, 0);
     }
     if constexpr (MLP) {
-      const float bias = hp.b1 ? elem<true>(hp.b1, col) : 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) hs[4 * g + j][col] = (uint16_t)bf16_bits(gelu(acc[j] + bias));
+      for (int j = 0; j < 4; ++j) hs[4 * g + j][col] = (uint16_t)bf16_bits(gelu(acc[j] + bias1));
     } else {
       y = acc;
     }
@@ -423,11 +434,9 @@ __global__ __launch_bounds__(1024) void encode_query_mfma_kernel(HashPtrs hp,
   // lanes 16g .. 16g+15, those bits of row 4g + j.
   constexpr int NT = MLP ? NT2 : NT1;
   if (wave < NT) {
-    const int col = 16 * wave + n;
-    const float bias = (MLP && hp.b2) ? elem<true>(hp.b2, col) : 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint64_t m = __ballot(y[j] + bias > 0.f);
+      const uint64_t m = __ballot(y[j] + bias2 > 0.f);
       if (lane < 4) {
         const int row = 4 * lane + j;
         const uint32_t bits16 = (uint32_t)(m >> (16 * lane)) & 0xFFFFu;
