@@ -42,7 +42,8 @@ __device__ __forceinline__ void emit_attend_body(
     int64_t n_local, int64_t max_ctx) {
   constexpr int CH = kScanThreads * LPT;
   static_assert(CH <= kListMax, "a chunk's selection must fit the list");
-  __shared__ int32_t sel[kListMax];
+  static_assert(kHistLdsWords <= kListMax, "the chunk histograms are staged in the list");
+  __shared__ __attribute__((aligned(16))) int32_t sel[kListMax];
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / Hkv;
@@ -111,8 +112,26 @@ __device__ __forceinline__ void emit_attend_body(
     // The head's threshold, tie quota and the counts before each chunk of the groups,
     // from the chunk histograms -- the computation of the threshold kernel, done by
     // every workgroup of the head, which saves a kernel and its dependent round trip.
+    // When the head's bin counts fit in LDS (Sb * bins <= kHistLdsWords: up to 32 chunks
+    // of 128-bit codes), they are requested together with the stash and the threshold
+    // is derived from LDS, one round trip to memory instead of two.
     int T, quota;
     {
+      const int roww = bins + bins / 8;
+      const uint32_t *hh = hist + (int64_t)bh * S * roww;
+      const bool hist_lds = keff > 0 && Sb * bins <= kHistLdsWords;   // uniform
+      constexpr int HV = kHistLdsWords / 4 / kScanThreads;
+      const int qpr = bins / 4;                // 16-byte vectors per chunk row
+      uint4 hv[HV];
+      if (hist_lds) {
+#pragma unroll
+        for (int i = 0; i < HV; ++i) {
+          const int v = t + kScanThreads * i;
+          const int cc = v / qpr;
+          hv[i] = cc < Sb ? *reinterpret_cast<const uint4 *>(hh + (int64_t)cc * roww + 4 * (v - cc * qpr))
+                          : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
       uint32_t wl[MAXC][LPT / 4];
       load_stash(0, wl);
       auto sink = [&](int cc, const int4 &m) {
@@ -120,10 +139,23 @@ __device__ __forceinline__ void emit_attend_body(
         for (int r = 0; r < REPS; ++r)
           if (cc >= g0(r) && cc < g1(r)) smt[r][cc - g0(r)] = m;
       };
-      if (bins == 128)
-        head_threshold<128>(hist + (int64_t)bh * S * (128 + 16), Sb, C, CH, keff, T, quota, sink);
-      else
-        head_threshold<64>(hist + (int64_t)bh * S * (64 + 8), Sb, C, CH, keff, T, quota, sink);
+      if (hist_lds) {
+        uint32_t *hl = reinterpret_cast<uint32_t *>(sel);
+#pragma unroll
+        for (int i = 0; i < HV; ++i) {
+          const int v = t + kScanThreads * i;
+          if (v < Sb * qpr) reinterpret_cast<uint4 *>(hl)[v] = hv[i];
+        }
+        __syncthreads();
+        if (bins == 128)
+          head_threshold_lds<128>(hl, Sb, C, CH, keff, T, quota, sink);
+        else
+          head_threshold_lds<64>(hl, Sb, C, CH, keff, T, quota, sink);
+      } else if (bins == 128) {
+        head_threshold<128>(hh, Sb, C, CH, keff, T, quota, sink);
+      } else {
+        head_threshold<64>(hh, Sb, C, CH, keff, T, quota, sink);
+      }
       if (c == 0 && t == 0) count[bh] = keff;
       stage_stash(wl);
     }

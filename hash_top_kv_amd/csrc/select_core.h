@@ -312,6 +312,105 @@ __device__ __forceinline__ void head_threshold(const uint32_t *__restrict__ hb, 
   quota_out = quota;
 }
 
+// Words of chunk histograms a workgroup can hold in LDS (the selection list's space,
+// which is unused while the threshold is derived).
+constexpr int kHistLdsWords = 4096;
+
+// head_threshold for a head whose chunk histograms fit in LDS: hl[S][BINS] holds the bin
+// counts of its S chunks (S * BINS <= kHistLdsWords), copied there by the caller in one
+// round trip together with its other loads, so that no step waits on memory.  Gives the
+// same T, tie quota and sink calls as head_threshold (kThrThreads threads):
+//   1. bin totals over the chunks (wavefront w adds chunks w, w + 4, ...), exchanged
+//      through LDS; every wavefront then scans the totals and takes the first bin whose
+//      inclusive count reaches k_eff (T = BINS when none does);
+//   2. per chunk, #(D < T) and #(D == T) from TPC threads that each add BPT bins, and the
+//      exclusive prefix of both over the chunks.
+template <int BINS, class Sink>
+__device__ __forceinline__ void head_threshold_lds(const uint32_t *hl, int S, int64_t C, int CH,
+                                                   int keff, int &T_out, int &quota_out,
+                                                   Sink sink) {
+  constexpr int NT = kThrThreads, NW = NT / 64;
+  constexpr int NJ = BINS / 64;                // 64-bin blocks: one per lane each
+  constexpr int SMAX = kHistLdsWords / BINS;   // 32 or 64 chunks
+  constexpr int TPC = NT / SMAX;               // threads per chunk: 8 or 4
+  constexpr int BPT = BINS / TPC;              // bins per thread: 16
+  static_assert(NT % SMAX == 0 && BINS % TPC == 0 && (BPT & (BPT - 1)) == 0, "layout");
+  __shared__ uint32_t red[NW][BINS];
+  __shared__ uint2 part[NW];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  int T = -1, quota = 0;
+  if (keff > 0) {
+    uint32_t p[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) p[j] = 0u;
+    for (int c = wave; c < S; c += NW)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) p[j] += hl[c * BINS + 64 * j + lane];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) red[wave][64 * j + lane] = p[j];
+    __syncthreads();
+    uint32_t run = 0, below = 0;               // run: count of the bins before block j
+    int found = -1;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      uint32_t tot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += red[w][64 * j + lane];
+      const uint32_t inc = wave_incl_scan_dpp(tot) + run;
+      const uint64_t reach = __ballot(inc >= (uint32_t)keff);
+      if (found < 0 && reach) {
+        const int b = (int)__builtin_ctzll(reach);
+        found = 64 * j + b;
+        below = b == 0 ? run : (uint32_t)__shfl((int)inc, b - 1, 64);
+      }
+      run = (uint32_t)__shfl((int)inc, 63, 64);
+    }
+    T = found < 0 ? BINS : found;
+    quota = keff - (int)(found < 0 ? run : below);
+  }
+  if (T >= 0) {
+    const int c = tid / TPC, pp = tid - c * TPC;
+    uint32_t lt = 0, eq = 0;
+    if (c < S) {
+      const uint32_t *hc = hl + c * BINS + pp * BPT;
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) {
+        const int ii = (i + c) & (BPT - 1);    // rotated by chunk: fewer LDS bank conflicts
+        const int b = pp * BPT + ii;
+        const uint32_t v = hc[ii];
+        lt += b < T ? v : 0u;
+        eq += b == T ? v : 0u;
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < TPC; o <<= 1) {
+      lt += (uint32_t)__shfl_xor((int)lt, o, 64);
+      eq += (uint32_t)__shfl_xor((int)eq, o, 64);
+    }
+    if (T == BINS && c < S) {                  // distance BINS is not in the histogram
+      const int64_t n = C - (int64_t)c * CH;
+      eq = (uint32_t)(n < CH ? n : CH) - lt;
+    }
+    const bool lead = pp == 0 && c < S;
+    const uint32_t lt_inc = wave_incl_scan_dpp(lead ? lt : 0u);
+    const uint32_t eq_inc = wave_incl_scan_dpp(lead ? eq : 0u);
+    if (lane == 63) part[wave] = make_uint2(lt_inc, eq_inc);
+    __syncthreads();
+    uint32_t off_lt = 0, off_eq = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint2 x = part[w];
+      off_lt += (w < wave) ? x.x : 0u;
+      off_eq += (w < wave) ? x.y : 0u;
+    }
+    if (lead)
+      sink(c, make_int4((int)(off_lt + lt_inc - lt), (int)(off_eq + eq_inc - eq), (int)lt, (int)eq));
+  }
+  T_out = T;
+  quota_out = quota;
+}
+
 // Writes the selected tokens of nch consecutive chunks (nch uniform, at most MAXC) into
 // list[position - first], where first is the head-list position of the first chunk's
 // first selected token.  The chunks' distance stashes are in LDS (sw[chunk][word][thread]
