@@ -386,6 +386,17 @@ FUSED_CASES = [
     (128, "bf16", 1, 4, 2, 1000, 4, 64, 0, 0),      # k = 0: the window only
     (128, "bf16", 1, 2, 2, 0, 4, 64, 10, 0),        # empty context
     (128, "f32", 2, 16, 2, 70000, 4, 512, 1400, 0), # several window slices, G = 8
+    # heads whose bin counts just fit in LDS (64 chunks x 64 bins, 32 x 128) and one
+    # chunk more, which read them from memory
+    (64, "bf16", 1, 2, 2, 65536 + 68, 4, 64, 1300, 3),
+    (64, "bf16", 1, 2, 2, 65536 + 69, 4, 64, 1300, 0),
+    (128, "bf16", 1, 4, 2, 32768 + 68, 4, 64, 655, 4),
+    (128, "bf16", 1, 4, 2, 32768 + 69, 4, 64, 655, 0),
+    # pool < 0: a share of -pool/10 of the tokens at distance `bits` (the complement of
+    # the query code, not counted in the histograms), so that T = bits
+    (128, "bf16", 1, 4, 2, 5000, 4, 64, 100, -10),
+    (64, "bf16", 2, 2, 2, 9000, 4, 64, 5000, -6),
+    (128, "bf16", 1, 4, 2, 70000 + 68, 4, 64, 40000, -6),
 ]
 
 
@@ -396,12 +407,15 @@ def test_retrieve_attend_matches_oracle_and_unfused(case):
     W = bits // 32
     rng = np.random.default_rng(N + k + 7)
     cap = N + 5
-    if pool:
+    if pool > 0:
         table = rng.integers(0, 2 ** 32, size=(pool, W), dtype=np.uint32)
         codes = table[rng.integers(0, pool, size=(B, Hkv, cap))]
     else:
         codes = rng.integers(0, 2 ** 32, size=(B, Hkv, cap, W), dtype=np.uint32)
     qc = rng.integers(0, 2 ** 32, size=(B, Hkv, W), dtype=np.uint32)
+    if pool < 0:
+        far = rng.random((B, Hkv, cap)) < -pool / 10
+        codes = np.where(far[..., None], ~qc[:, :, None, :], codes)
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     K = torch.from_numpy(rng.standard_normal((B, Hkv, cap, 128)).astype(np.float32) * 1.5).to(tdt).cuda()
     V = torch.from_numpy(rng.standard_normal((B, Hkv, cap, 128)).astype(np.float32)).to(tdt).cuda()
