@@ -47,7 +47,7 @@ KERNEL_SOURCES = ["include/hk.h", "hash_top_kv_amd/csrc/hk_internal.h",
                   "hash_top_kv_amd/csrc/retrieve.hip", "hash_top_kv_amd/csrc/attend.hip",
                   "hash_top_kv_amd/csrc/fused.hip", "hash_top_kv_amd/csrc/encode.hip",
                   "hash_top_kv_amd/csrc/evict.hip", "hash_top_kv_amd/csrc/exact.hip",
-                  "hash_top_kv_amd/csrc/api.hip"]
+                  "hash_top_kv_amd/csrc/probe.hip", "hash_top_kv_amd/csrc/api.hip"]
 
 
 def _code_only(text: str) -> str:

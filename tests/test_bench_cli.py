@@ -1,0 +1,63 @@
+"""bench.py's command-line contract and the bookkeeping it reports, on the host: one GPU
+only, a loud failure without a GPU, and the profile digest that decides whether stored
+HBM counter figures still describe the kernels."""
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=300, cwd=ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = _run("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in (r.stdout + r.stderr)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="a GPU is present")
+def test_no_gpu_fails_loudly():
+    r = _run("--steps", "1", "--warmup", "0")
+    assert r.returncode != 0
+    assert "GPU" in (r.stdout + r.stderr)
+    assert not r.stdout.strip().startswith("{")        # no result line
+
+
+def test_digest_ignores_comments_and_layout_only():
+    a = "int f(int x) { return x + 1; }"
+    b = "// the successor\nint f(int x) {\n  return x + 1;  /* plus one */\n}\n"
+    c = "int f(int x) { return x + 2; }"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
+
+
+def test_digest_covers_every_kernel_source():
+    d = bench.source_digest()
+    assert len(d) == 16
+    csrc = os.path.join(ROOT, "hash_top_kv_amd", "csrc")
+    built = {f for f in os.listdir(csrc) if f.endswith((".hip", ".h"))}
+    listed = {os.path.basename(f) for f in bench.KERNEL_SOURCES}
+    assert built <= listed, built - listed
+
+
+def test_counter_summary_is_used_only_for_the_current_sources(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "cur_counters.txt").write_text("source_digest: ffffffffffffffff\n"
+                                           "hbm_bytes_per_launch: 123\n")
+    (prof / "old_counters.txt").write_text("source_digest: 0000000000000000\n"
+                                           "hbm_bytes_per_launch: 123\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_digest", lambda: "ffffffffffffffff")
+    assert bench.read_traffic("cur") == 123.0
+    assert bench.read_traffic("old") is None
+    assert bench.read_traffic("missing") is None
