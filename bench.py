@@ -114,6 +114,59 @@ def same_size_read_rate(torch, hk, nbytes, reps=200):
             "how": f"hk_read_probe: {n} bytes, {R} rotating buffers, {reps} launches back to back"}
 
 
+def graph_us(torch, fns, reps):
+    """Average time of one call of fns[i] when all of fns are captured, in order, in one
+    HIP graph and the graph is replayed reps times (no host launch cost)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for fn in fns:
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in fns:
+            fn()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * len(fns)) * 1e3
+
+
+def same_rows_gather(torch, hk, ctx, sel_fn, n_lists=8, reps=20):
+    """hk_gather_probe over exactly the K/V rows that select+attend gathers (the row lists
+    of n_lists consecutive steps, in the rotation of the step's own timing), at the best
+    of a few workgroup sizes: a pure read of those rows, with nothing of the selection or
+    the attention.  Both it and select+attend are timed as HIP-graph replays, so that the
+    host's launch cost is in neither."""
+    lists = [ctx["gather_rows"](i) for i in range(n_lists)]
+    K, V = ctx["K"], ctx["V"]
+    n = lists[0].numel()
+    if n == 0:
+        return None, None
+    best = None
+    for rpb in (256, 512, 1024, 2048):
+        sink = hk.gather_probe(K, V, lists[0], rpb)
+        us = graph_us(torch, [lambda i=i, rpb=rpb, sink=sink: hk.gather_probe(
+            K, V, lists[i % n_lists], rpb, sink) for i in range(2 * n_lists)], reps)
+        if best is None or us < best[0]:
+            best = (us, rpb)
+    sel_us = graph_us(torch, [lambda i=i: sel_fn(i) for i in range(n_lists)], 2 * reps)
+    nbytes = n * 512
+    return ({"rows_256B": n, "bytes": nbytes, "us_per_launch": round(best[0], 3),
+             "gbs": round(nbytes / best[0] / 1e3, 1), "rows_per_workgroup": best[1],
+             "how": f"hk_gather_probe: the K and V rows of {n_lists} steps' selections and "
+                    "windows, HIP-graph replay, best of 256/512/1024/2048 rows per workgroup"},
+            sel_us)
+
+
 def read_traffic(name: str):
     """HBM bytes per launch of a kernel from a committed counter summary, if the kernel
     sources have not changed since it was taken (else None)."""
@@ -218,6 +271,13 @@ def build_retrieval_case(args, torch, hk, synth):
             want = np.sort(pos[0, h][order[:k]])
             assert np.array_equal(got[0, h], want), f"head {h}: top-k differs from the planted set"
 
+    def gather_rows(i):
+        """The K/V rows step i gathers, as rows of the [B*Hkv*N] table (no window)."""
+        scan(i)
+        rest(i)
+        base = torch.arange(B * Hkv, device="cuda", dtype=torch.int64).view(B, Hkv, 1) * N
+        return (idx[..., :k].to(torch.int64) + base).flatten().to(torch.int32)
+
     scan_bytes = B * Hkv * N * 16
     gather_bytes = B * Hkv * k * 2 * 128 * 2 + B * wl.Hq * 128 * 2
     info = {"workload": wl.name, "B": B, "Hq": wl.Hq, "Hkv": Hkv, "N": N, "k": k,
@@ -226,7 +286,8 @@ def build_retrieval_case(args, torch, hk, synth):
             "step": ("hk_hamming_scan + hk_topk_select + hk_sparse_decode" if args.unfused
                      else "hk_hamming_scan + hk_select_attend (= hk_retrieve_attend)")}
     parts = [("hamming_scan", scan, scan_bytes), ("select+attend", rest, gather_bytes)]
-    return parts, check, info, {"wl": wl, "reps": reps, "kv": kv}
+    return parts, check, info, {"wl": wl, "reps": reps, "kv": kv, "K": K, "V": V,
+                                "gather_rows": None if args.unfused else gather_rows}
 
 
 def build_full_case(args, torch, hk, synth):
@@ -304,6 +365,20 @@ def build_full_case(args, torch, hk, synth):
             torch.cuda.synchronize()
             assert bool((qst(0).count == qst(0).keff).all())
 
+    def gather_rows(i):
+        """The K/V rows step i gathers (each head's selection, then its window), as
+        256-byte rows of the [B*Hkv*N] table (two per token for fp32)."""
+        enc(i)
+        scan(i)
+        rest(i)
+        s = st(i)
+        base = torch.arange(wl.B * wl.Hkv, device="cuda", dtype=torch.int64).view(wl.B, wl.Hkv, 1) * wl.N
+        win = s.win.to(torch.int64).view(1, 1, -1).expand(wl.B, wl.Hkv, -1)
+        tok = torch.cat([s.idx[..., :s.keff].to(torch.int64), win], dim=2) + base
+        if wl.dtype == "f32":
+            tok = torch.stack([2 * tok, 2 * tok + 1], dim=-1)
+        return tok.flatten().to(torch.int32)
+
     esz = 4 if wl.dtype == "f32" else 2
     s0 = steps[0]
     gather_bytes = wl.B * wl.Hkv * (s0.keff + s0.n_win) * 2 * 128 * esz
@@ -330,8 +405,10 @@ def build_full_case(args, torch, hk, synth):
     else:
         parts = [("encode_query", enc, None), ("hamming_scan", scan, scan_bytes),
                  ("select+attend", rest, gather_bytes)]
+    plain = not (args.unfused or args.varlen or args.qheads)
     return parts, check, info, {"wl": wl, "K": K, "V": V, "h": h, "codes": codes, "spec": spec,
-                                "code_sets": code_sets, "Qs": Qs, "steps": steps, "qsteps": qsteps}
+                                "code_sets": code_sets, "Qs": Qs, "steps": steps, "qsteps": qsteps,
+                                "gather_rows": gather_rows if plain else None}
 
 
 def qhead_overlap(torch, hk, ctx):
@@ -677,6 +754,13 @@ def main():
             kern["select+attend"].update({"us_per_launch": round(ms * 1e3, 3),
                                           "gbs": round(nbytes / ms / 1e6, 1),
                                           "frac_of_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)})
+            if ctx.get("gather_rows"):
+                same, sel_us = same_rows_gather(torch, hk, ctx, fn)
+                if same:
+                    kern["select+attend"]["us_per_launch_graph"] = round(sel_us, 3)
+                    kern["select+attend"]["same_rows_gather"] = same
+                    kern["select+attend"]["frac_of_same_rows_gather"] = round(
+                        same["us_per_launch"] / sel_us, 4)
 
     roofline = None
     sc = kern.get("hamming_scan", {})

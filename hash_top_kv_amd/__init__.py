@@ -40,6 +40,8 @@ _SIGNATURES = {
     "hk_strerror": (ctypes.c_char_p, [_I]),
     "hk_read_probe_sink_words": (_SZ, [_SZ]),
     "hk_read_probe": (_I, [_P, _SZ, _P, _P]),
+    "hk_gather_probe_sink_words": (_SZ, [_I64, _I]),
+    "hk_gather_probe": (_I, [_P, _P, _I64, _P, _I64, _I, _P, _P]),
     "hk_encode_keys": (_I, [ctypes.POINTER(_Hash), _P, _I, _I, _I64, _I64, _I64, _P, _P]),
     "hk_encode_query": (_I, [ctypes.POINTER(_Hash), _P, _I, _I, _I, _P, _P]),
     "hk_retrieve_topk_workspace": (_SZ, [_I, _I, _I, _I64, _I, _I, _I]),
@@ -555,3 +557,26 @@ def read_probe(src: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Ten
         raise HkError(1, "read_probe: sink too small")
     _check(lib().hk_read_probe(_ptr(src), nbytes, _ptr(sink), _stream()), "hk_read_probe")
     return sink
+
+
+def gather_probe(k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, rows_per_block: int = 512,
+                 sink: torch.Tensor | None = None) -> torch.Tensor:
+    """hk_gather_probe: a plain gather of the 256-byte K and V rows idx (a measurement aid).
+    k, v: contiguous device tensors viewed as [table_rows][256 bytes]; idx: int32."""
+    for t, nm in ((k, "k"), (v, "v"), (idx, "idx")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise HkError(1, f"gather_probe: {nm} must be a contiguous device tensor")
+    _need(idx, "idx", dtype=torch.int32)
+    rows = k.numel() * k.element_size() // 256
+    if v.numel() * v.element_size() // 256 != rows:
+        raise HkError(1, "gather_probe: k and v differ in size")
+    n = idx.numel()
+    words = int(lib().hk_gather_probe_sink_words(n, rows_per_block))
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=k.device)
+    elif sink.numel() < words:
+        raise HkError(1, "gather_probe: sink too small")
+    _check(lib().hk_gather_probe(_ptr(k), _ptr(v), rows, _ptr(idx), n, rows_per_block,
+                                 _ptr(sink), _stream()), "hk_gather_probe")
+    return sink
+

@@ -395,4 +395,20 @@ hk_status hk_read_probe(const void *src, size_t bytes, uint32_t *sink, void *str
   return from_hip(launch_read_probe(src, bytes, sink, as_stream(stream)));
 }
 
+size_t hk_gather_probe_sink_words(int64_t n_idx, int rows_per_block) {
+  if (n_idx <= 0 || !gather_probe_rows_ok(rows_per_block)) return 0;
+  return (size_t)gather_probe_blocks(n_idx, rows_per_block);
+}
+
+hk_status hk_gather_probe(const void *k, const void *v, int64_t table_rows, const int32_t *idx,
+                          int64_t n_idx, int rows_per_block, uint32_t *sink, void *stream) {
+  if (n_idx < 0 || !gather_probe_rows_ok(rows_per_block)) return HK_ERR_INVALID_ARGUMENT;
+  if (n_idx == 0) return HK_OK;
+  if (!k || !v || !idx || !sink || table_rows < 1) return HK_ERR_INVALID_ARGUMENT;
+  if (!aligned(k, 16) || !aligned(v, 16)) return HK_ERR_UNSUPPORTED;
+  if (gather_probe_blocks(n_idx, rows_per_block) > 0x7FFFFFFF) return HK_ERR_UNSUPPORTED;
+  return from_hip(launch_gather_probe(k, v, table_rows, idx, n_idx, rows_per_block, sink,
+                                      as_stream(stream)));
+}
+
 }  // extern "C"

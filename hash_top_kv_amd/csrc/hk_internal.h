@@ -103,6 +103,11 @@ hipError_t launch_lse_merge_parts(const float *o_parts, const float *lse_parts, 
 // lse [parts][B*Hq], parts = Sc + Sw.
 // A plain streaming read of bytes (multiple of 16) from src; sink receives
 // read_probe_blocks(bytes) words.
+int64_t gather_probe_blocks(int64_t n_idx, int rows_per_block);
+bool gather_probe_rows_ok(int rows_per_block);
+hipError_t launch_gather_probe(const void *k, const void *v, int64_t table_rows,
+                               const int32_t *idx, int64_t n_idx, int rows_per_block,
+                               uint32_t *sink, hipStream_t st);
 int64_t read_probe_blocks(size_t bytes);
 hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, hipStream_t st);
 

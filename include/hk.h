@@ -334,6 +334,23 @@ hk_status hk_retrieve_attend_varlen(const uint32_t *codes, const uint32_t *qcode
 size_t hk_read_probe_sink_words(size_t bytes);
 hk_status hk_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
+/* Measurement aid, not a step of the decode path: a plain gather of K/V rows in the
+ * access pattern of the attention (the rows a partial-attention step reads; RetrievalAttention,
+ * Summary), so that the attention kernels' gather rates can be set against the rate of
+ * a pure read of the same rows.  For each of the n_idx entries of idx, reads the
+ * 256-byte row idx[i] of k and of v ([table_rows][256 bytes], 16-byte aligned; a bf16
+ * d = 128 K/V cache viewed as one table); entries outside [0, table_rows) read row 0.
+ * Workgroup b takes entries [b*rows_per_block, (b+1)*rows_per_block).
+ *   sink  device uint32 array of hk_gather_probe_sink_words(n_idx, rows_per_block)
+ *         entries (written: the XOR of the words each workgroup read).
+ * Errors: n_idx < 0, rows_per_block not a multiple of 16 in [16, 4096], or NULL k / v /
+ * idx / sink or table_rows < 1 with n_idx > 0 -> INVALID_ARGUMENT; k or v not 16-byte
+ * aligned -> UNSUPPORTED; n_idx = 0 enqueues nothing.  The sink size is 0 for invalid
+ * arguments. */
+size_t hk_gather_probe_sink_words(int64_t n_idx, int rows_per_block);
+hk_status hk_gather_probe(const void *k, const void *v, int64_t table_rows, const int32_t *idx,
+                          int64_t n_idx, int rows_per_block, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -175,6 +175,24 @@ def test_read_probe_host_checks(hk):
     assert L.hk_read_probe(ctypes.c_void_p(0x1008), 32, ctypes.c_void_p(0x2000), None) == 2
 
 
+def test_gather_probe_host_checks(hk):
+    """The gather probe rejects bad workgroup sizes, negative counts and missing pointers
+    on the host; an empty list enqueues nothing."""
+    L = hk.lib()
+    P = ctypes.c_void_p(0x1000)
+    assert L.hk_gather_probe_sink_words(1000, 512) == 2
+    assert L.hk_gather_probe_sink_words(1024, 512) == 2
+    assert L.hk_gather_probe_sink_words(1000, 500) == 0            # not a multiple of 16
+    assert L.hk_gather_probe_sink_words(1000, 8192) == 0           # above 4096
+    assert L.hk_gather_probe(P, P, 10, P, 5, 500, P, None) == 1    # rows per workgroup
+    assert L.hk_gather_probe(P, P, 10, P, -1, 512, P, None) == 1   # negative count
+    assert L.hk_gather_probe(P, P, 0, P, 5, 512, P, None) == 1     # empty table
+    assert L.hk_gather_probe(None, P, 10, P, 5, 512, P, None) == 1
+    assert L.hk_gather_probe(P, P, 10, None, 5, 512, P, None) == 1
+    assert L.hk_gather_probe(P, P, 10, P, 0, 512, None, None) == 0  # nothing to read
+    assert L.hk_gather_probe(ctypes.c_void_p(0x1008), P, 10, P, 5, 512, P, None) == 2
+
+
 def test_workspace_sizes_grow_with_the_problem(hk):
     a = hk.retrieve_topk_workspace(128, 1, 8, 100000, 4, 64, 100)
     b = hk.retrieve_topk_workspace(128, 1, 8, 200000, 4, 64, 100)

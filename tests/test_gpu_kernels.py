@@ -573,6 +573,30 @@ def test_read_probe_reads_every_byte(nbytes):
     assert got == np.bitwise_xor.reduce(data)
 
 
+@pytest.mark.parametrize("rpb", [16, 512, 4096])
+def test_gather_probe_reads_every_row(rpb):
+    """The gather probe reads the K and V row of every list entry, duplicates and
+    out-of-range entries (row 0) included: the XOR of its sink equals the XOR of those
+    rows' words."""
+    say(f"gather_probe rows_per_block={rpb}")
+    rng = np.random.default_rng(rpb)
+    rows = 5000
+    Kw = rng.integers(0, 2 ** 32, size=(rows, 64), dtype=np.uint32)
+    Vw = rng.integers(0, 2 ** 32, size=(rows, 64), dtype=np.uint32)
+    idx = rng.integers(0, rows, size=9001).astype(np.int32)
+    idx[::97] = idx[3]                                     # duplicates
+    idx[5], idx[77], idx[-1] = -3, rows, 2 ** 31 - 1       # outside the table: row 0
+    k = torch.from_numpy(Kw.view(np.int32)).cuda()
+    v = torch.from_numpy(Vw.view(np.int32)).cuda()
+    sink = hk.gather_probe(k, v, torch.from_numpy(idx).cuda(), rpb)
+    torch.cuda.synchronize()
+    words = int(hk.lib().hk_gather_probe_sink_words(idx.size, rpb))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)[:words])
+    eff = np.where((idx >= 0) & (idx < rows), idx, 0)
+    want = np.bitwise_xor.reduce(Kw[eff].ravel()) ^ np.bitwise_xor.reduce(Vw[eff].ravel())
+    assert got == want
+
+
 def test_retrieve_attend_fp32_two_chunk_groups():
     """fp32 K/V at the batch-16 x 131072 shape (8 KV heads, 32 query heads, sink 4 + local
     512, top-2%), where the fused step runs two chunk groups per workgroup: sampled heads
