@@ -47,7 +47,8 @@ KERNEL_SOURCES = ["include/hk.h", "hash_top_kv_amd/csrc/hk_internal.h",
                   "hash_top_kv_amd/csrc/retrieve.hip", "hash_top_kv_amd/csrc/attend.hip",
                   "hash_top_kv_amd/csrc/fused.hip", "hash_top_kv_amd/csrc/encode.hip",
                   "hash_top_kv_amd/csrc/evict.hip", "hash_top_kv_amd/csrc/exact.hip",
-                  "hash_top_kv_amd/csrc/probe.hip", "hash_top_kv_amd/csrc/api.hip"]
+                  "hash_top_kv_amd/csrc/probe.hip", "hash_top_kv_amd/csrc/api.hip",
+                  "include/hk_probe.h"]
 
 
 def _code_only(text: str) -> str:
@@ -69,17 +70,17 @@ def source_digest(files=KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def stream_read_rate(torch, hk, mib=1024, reps=20):
+def stream_read_rate(torch, hkp, mib=1024, reps=20):
     """Measured read rate beside the 8 TB/s spec peak: hk_read_probe (16-byte
     non-temporal loads, 2048 workgroups) over a 1 GiB buffer, launched back to back."""
     x = torch.ones((mib << 20) // 4, dtype=torch.int32, device="cuda")
-    sink = hk.read_probe(x)
+    sink = hkp.read_probe(x)
     for _ in range(3):
-        hk.read_probe(x, sink)
+        hkp.read_probe(x, sink)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
-        hk.read_probe(x, sink)
+        hkp.read_probe(x, sink)
     b.record()
     torch.cuda.synchronize()
     gbs = x.numel() * 4 * reps / (a.elapsed_time(b) * 1e6)
@@ -89,7 +90,7 @@ def stream_read_rate(torch, hk, mib=1024, reps=20):
             "how": "hk_read_probe: 1 GiB, 16-byte non-temporal loads, 20 launches back to back"}
 
 
-def same_size_read_rate(torch, hk, nbytes, reps=200):
+def same_size_read_rate(torch, hkp, nbytes, reps=200):
     """hk_read_probe over exactly nbytes (the scan's algorithmic bytes), launched back to
     back over buffers rotated through 1 GiB so that no launch finds its data in a cache:
     what a pure read of that size reaches, launch ramp and drain included."""
@@ -98,13 +99,13 @@ def same_size_read_rate(torch, hk, nbytes, reps=200):
         return None
     R = min(64, max(1, -(-(1 << 30) // n)))
     bufs = [torch.ones(n // 4, dtype=torch.int32, device="cuda") for _ in range(R)]
-    sink = hk.read_probe(bufs[0])
+    sink = hkp.read_probe(bufs[0])
     for i in range(2 * R):
-        hk.read_probe(bufs[i % R], sink)
+        hkp.read_probe(bufs[i % R], sink)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(reps):
-        hk.read_probe(bufs[i % R], sink)
+        hkp.read_probe(bufs[i % R], sink)
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
@@ -140,7 +141,7 @@ def graph_us(torch, fns, reps):
     return a.elapsed_time(b) / (reps * len(fns)) * 1e3
 
 
-def same_rows_gather(torch, hk, ctx, sel_fn, n_lists=8, reps=20):
+def same_rows_gather(torch, hkp, ctx, sel_fn, n_lists=8, reps=20):
     """hk_gather_probe over exactly the K/V rows that select+attend gathers (the row lists
     of n_lists consecutive steps, in the rotation of the step's own timing), at the best
     of a few workgroup sizes: a pure read of those rows, with nothing of the selection or
@@ -153,8 +154,8 @@ def same_rows_gather(torch, hk, ctx, sel_fn, n_lists=8, reps=20):
         return None, None
     best = None
     for rpb in (256, 512, 1024, 2048):
-        sink = hk.gather_probe(K, V, lists[0], rpb)
-        us = graph_us(torch, [lambda i=i, rpb=rpb, sink=sink: hk.gather_probe(
+        sink = hkp.gather_probe(K, V, lists[0], rpb)
+        us = graph_us(torch, [lambda i=i, rpb=rpb, sink=sink: hkp.gather_probe(
             K, V, lists[i % n_lists], rpb, sink) for i in range(2 * n_lists)], reps)
         if best is None or us < best[0]:
             best = (us, rpb)
@@ -617,6 +618,7 @@ def main():
 
     import torch
     import hash_top_kv_amd as hk
+    from hash_top_kv_amd import probe as hkp
     import synth
 
     if not torch.cuda.is_available():
@@ -755,7 +757,7 @@ def main():
                                           "gbs": round(nbytes / ms / 1e6, 1),
                                           "frac_of_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)})
             if ctx.get("gather_rows"):
-                same, sel_us = same_rows_gather(torch, hk, ctx, fn)
+                same, sel_us = same_rows_gather(torch, hkp, ctx, fn)
                 if same:
                     kern["select+attend"]["us_per_launch_graph"] = round(sel_us, 3)
                     kern["select+attend"]["same_rows_gather"] = same
@@ -764,7 +766,7 @@ def main():
 
     roofline = None
     sc = kern.get("hamming_scan", {})
-    stream = None if args.no_kernel_timing else stream_read_rate(torch, hk)
+    stream = None if args.no_kernel_timing else stream_read_rate(torch, hkp)
     if "gbs" in sc:
         a = sc["gbs"]
         roofline = {"kernel": "hamming_scan", "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS,
@@ -773,7 +775,7 @@ def main():
                     "alg_bytes_per_launch": sc["alg_bytes"], "us_per_launch": sc["us_per_launch"]}
         if stream:
             roofline["frac_of_measured_read"] = round(a / stream["gbs"], 4)
-            same = same_size_read_rate(torch, hk, sc["alg_bytes"])
+            same = same_size_read_rate(torch, hkp, sc["alg_bytes"])
             if same:
                 stream["same_size_as_scan"] = same
                 roofline["frac_of_same_size_read"] = round(a / same["gbs"], 4)

@@ -1,10 +1,11 @@
-"""Build libhk.so (HIP for gfx950) in-tree with hipcc.
+"""Build libhk.so and libhk_probe.so (HIP for gfx950) in-tree with hipcc.
 
     python hash_top_kv_amd/build.py        # or __graft_entry__.build()
 
-Each translation unit compiles to hash_top_kv_amd/_build/*.o in parallel, then one
-shared library is linked next to this file.  Packed-fp32 instructions are disabled for
-all device code.
+Each translation unit compiles to hash_top_kv_amd/_build/*.o in parallel.  libhk.so (the
+decode path, include/hk.h) and libhk_probe.so (the measurement aids of
+include/hk_probe.h) are linked next to this file.  Packed-fp32 instructions are disabled
+for all device code.
 """
 from __future__ import annotations
 
@@ -18,8 +19,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhk.so")
-SOURCES = ["api.hip", "retrieve.hip", "attend.hip", "fused.hip", "encode.hip", "evict.hip", "exact.hip",
-           "probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libhk_probe.so")
+LIB_SOURCES = ["api.hip", "retrieve.hip", "attend.hip", "fused.hip", "encode.hip", "evict.hip",
+               "exact.hip"]
+PROBE_SOURCES = ["probe.hip"]
+SOURCES = LIB_SOURCES + PROBE_SOURCES
 ARCH = "gfx950"
 # The attention kernels keep their matrix-core accumulators in ordinary VGPRs: the
 # online-softmax rescale multiplies them in place, which with accumulation registers
@@ -58,18 +62,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link failed for {os.path.basename(out)}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    # the largest translation units first, so the parallel build ends sooner
+    order = sorted(SOURCES, key=lambda f: -os.path.getsize(os.path.join(CSRC, f)))
+    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(order, ex.map(_compile, order)))
+    _link([objs[f] for f in LIB_SOURCES], LIB)
+    _link([objs[f] for f in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

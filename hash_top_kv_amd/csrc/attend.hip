@@ -70,11 +70,14 @@ __global__ __launch_bounds__(256) void lse_merge_small_kernel(
 #pragma unroll
   for (int j = 0; j < PW; ++j) {
     const int p = wave + 4 * j;
-    const int pp = p < P ? p : 0;
-    x[j] = p < P ? lse_parts[(int64_t)pp * rows + row] : -INFINITY;
-    const float *op = o_parts + ((int64_t)pp * rows + row) * D;
-    va[j] = op[lane];
-    vb[j] = op[lane + 64];
+    x[j] = -INFINITY;
+    va[j] = vb[j] = 0.f;
+    if (p < P) {                               // parts past P are never read
+      x[j] = lse_parts[(int64_t)p * rows + row];
+      const float *op = o_parts + ((int64_t)p * rows + row) * D;
+      va[j] = op[lane];
+      vb[j] = op[lane + 64];
+    }
   }
   float M = -INFINITY;
 #pragma unroll
@@ -203,6 +206,14 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
   if (t == 0) lse[row] = M == -INFINITY ? -INFINITY : M + logf(S);
 }
 
+// Attention over empty sets: o = 0, lse = -inf for every row (reads nothing).
+__global__ __launch_bounds__(256) void empty_rows_kernel(int64_t rows, int d, float *__restrict__ o,
+                                                         float *__restrict__ lse) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < rows * d) o[i] = 0.f;
+  if (i < rows) lse[i] = -INFINITY;
+}
+
 template <bool BF16, int G>
 void decode_launch(const DecodePlan &pl, const void *q, const void *k, const void *v, int B,
                    int Hq, int Hkv, int64_t cap, const int32_t *idx, int64_t idx_stride,
@@ -285,12 +296,20 @@ hipError_t launch_sparse_decode(const DecodePlan &pl, const void *q, const void 
 
 hipError_t launch_lse_merge_parts(const float *o_parts, const float *lse_parts, int P,
                                   int64_t rows, int d, float *o, float *lse, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (P == 0) {
+    // No partial exists (and no partial space was reserved): every row is the empty set.
+    hipLaunchKernelGGL(empty_rows_kernel, dim3((unsigned)((rows * d + 255) / 256)), dim3(256), 0,
+                       st, rows, d, o, lse);
+    return hipGetLastError();
+  }
   return launch_lse_merge(o_parts, lse_parts, P, rows, d, o, lse, st);
 }
 
 hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int P,
                             int64_t rows, int d, float *o, float *lse, hipStream_t st) {
   if (rows == 0) return hipSuccess;
+  if (P < 1) return hipErrorInvalidValue;      // the merge kernels read part 0 .. P-1
   if (P <= kMergeSmallParts && d == kHeadDim) {
     hipLaunchKernelGGL(lse_merge_small_kernel, dim3((unsigned)rows), dim3(256), 0, st,
                        o_parts, lse_parts, P, rows, o, lse);

@@ -93,7 +93,8 @@ hipError_t launch_sparse_decode(const DecodePlan &p, const void *q, const void *
                                 float *lse, void *ws, hipStream_t st, int kv_group = 1);
 hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int P,
                             int64_t rows, int d, float *o, float *lse, hipStream_t st);
-// Same kernel, also for P == 0 (every row empty: o = 0, lse = -inf).
+// As launch_lse_merge for P >= 1.  P == 0 (no partial written, none reserved) writes
+// o = 0, lse = -inf to every row without reading o_parts or lse_parts.
 hipError_t launch_lse_merge_parts(const float *o_parts, const float *lse_parts, int P,
                                   int64_t rows, int d, float *o, float *lse, hipStream_t st);
 
@@ -101,16 +102,6 @@ hipError_t launch_lse_merge_parts(const float *o_parts, const float *lse_parts, 
 // hk_retrieve_attend: the retrieval workspace (RetrievePlan) followed by one normalised
 // partial per group of `cpb` chunks of each head and per window slice: o [parts][B*Hq][d],
 // lse [parts][B*Hq], parts = Sc + Sw.
-// A plain streaming read of bytes (multiple of 16) from src; sink receives
-// read_probe_blocks(bytes) words.
-int64_t gather_probe_blocks(int64_t n_idx, int rows_per_block);
-bool gather_probe_rows_ok(int rows_per_block);
-hipError_t launch_gather_probe(const void *k, const void *v, int64_t table_rows,
-                               const int32_t *idx, int64_t n_idx, int rows_per_block,
-                               uint32_t *sink, hipStream_t st);
-int64_t read_probe_blocks(size_t bytes);
-hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, hipStream_t st);
-
 struct FusedPlan {
   RetrievePlan r;
   int win_sinks = 0, n_win = 0, win_rows = 64, Sw = 0, parts = 0, G = 1, cpb = 1, Sc = 0;
@@ -143,7 +134,7 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
   return v;
 }
 
-// Sums each of K per-lane values (K = 8 or 16) over the 64 lanes of a wavefront, by a
+// Sums each of K per-lane values (K = 8, 16 or 32) over the 64 lanes of a wavefront, by a
 // butterfly that halves the values held per lane at every exchange, then adds across the
 // remaining lane bits.  Returns, in lane l, the total of value bitrev(l mod K), where
 // bitrev reverses log2(K) bits.
@@ -175,15 +166,16 @@ __device__ __forceinline__ int bitrev_k(int l) {
 }
 template <int K>
 __device__ __forceinline__ uint32_t wave_transpose_sum(uint32_t (&x)[K]) {
-  static_assert(K == 8 || K == 16, "8 or 16 values");
+  static_assert(K == 8 || K == 16 || K == 32, "8, 16 or 32 values");
   const int lane = threadIdx.x & 63;
   transpose_sum_step<K, 1>(x, lane);
   transpose_sum_step<K, 2>(x, lane);
   transpose_sum_step<K, 4>(x, lane);
-  if constexpr (K == 16) transpose_sum_step<K, 8>(x, lane);
+  if constexpr (K >= 16) transpose_sum_step<K, 8>(x, lane);
+  if constexpr (K == 32) transpose_sum_step<K, 16>(x, lane);
   uint32_t r = x[0];
   if constexpr (K == 8) r += swizzle_xor<8>(r);
-  r += swizzle_xor<16>(r);
+  if constexpr (K <= 16) r += swizzle_xor<16>(r);
   r += (uint32_t)__shfl_xor((int)r, 32, 64);
   return r;
 }

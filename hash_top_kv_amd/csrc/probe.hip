@@ -1,7 +1,9 @@
 // A plain streaming read and a plain random-row gather, for the measured rates that the
 // kernels' bandwidth figures are compared with (beside the spec peak).  Not steps of the
-// decode path.
+// decode path: this translation unit is the library libhk_probe.so of its own, with the C
+// entry points of hk_probe.h.
 #include "hk_internal.h"
+#include "hk_probe.h"
 
 namespace hk {
 namespace {
@@ -85,8 +87,6 @@ __global__ __launch_bounds__(kProbeThreads) void gather_probe_kernel(
   if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
-}  // namespace
-
 int64_t gather_probe_blocks(int64_t n_idx, int rows_per_block) {
   return rows_per_block > 0 ? (n_idx + rows_per_block - 1) / rows_per_block : 0;
 }
@@ -118,4 +118,44 @@ hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, hipS
   return hipGetLastError();
 }
 
+}  // namespace
 }  // namespace hk
+
+using namespace hk;
+
+namespace {
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline hk_status from_hip(hipError_t e) { return e == hipSuccess ? HK_OK : HK_ERR_HIP; }
+inline hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+}  // namespace
+
+extern "C" {
+
+size_t hk_read_probe_sink_words(size_t bytes) { return (size_t)read_probe_blocks(bytes); }
+
+hk_status hk_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+  if (bytes % 16 != 0) return HK_ERR_INVALID_ARGUMENT;
+  if (bytes == 0) return HK_OK;
+  if (!src || !sink) return HK_ERR_INVALID_ARGUMENT;
+  if (!aligned16(src)) return HK_ERR_UNSUPPORTED;
+  if (read_probe_blocks(bytes) > 0x7FFFFFFF) return HK_ERR_UNSUPPORTED;
+  return from_hip(launch_read_probe(src, bytes, sink, as_stream(stream)));
+}
+
+size_t hk_gather_probe_sink_words(int64_t n_idx, int rows_per_block) {
+  if (n_idx <= 0 || !gather_probe_rows_ok(rows_per_block)) return 0;
+  return (size_t)gather_probe_blocks(n_idx, rows_per_block);
+}
+
+hk_status hk_gather_probe(const void *k, const void *v, int64_t table_rows, const int32_t *idx,
+                          int64_t n_idx, int rows_per_block, uint32_t *sink, void *stream) {
+  if (n_idx < 0 || !gather_probe_rows_ok(rows_per_block)) return HK_ERR_INVALID_ARGUMENT;
+  if (n_idx == 0) return HK_OK;
+  if (!k || !v || !idx || !sink || table_rows < 1) return HK_ERR_INVALID_ARGUMENT;
+  if (!aligned16(k) || !aligned16(v)) return HK_ERR_UNSUPPORTED;
+  if (gather_probe_blocks(n_idx, rows_per_block) > 0x7FFFFFFF) return HK_ERR_UNSUPPORTED;
+  return from_hip(launch_gather_probe(k, v, table_rows, idx, n_idx, rows_per_block, sink,
+                                      as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,5 +1,6 @@
 """The C ABI without a GPU: libhk.so loads, exports every function include/hk.h
-declares, and rejects bad arguments on the host before touching HIP."""
+declares (and none of the measurement aids), libhk_probe.so exports those of
+include/hk_probe.h, and both reject bad arguments on the host before touching HIP."""
 import ctypes
 import os
 import re
@@ -8,10 +9,11 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hk.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "hk_probe.h")
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(hk_[a-z_0-9]+)\s*\(", text)))
 
@@ -20,6 +22,12 @@ def _declared():
 def hk():
     import hash_top_kv_amd
     return hash_top_kv_amd
+
+
+@pytest.fixture(scope="module")
+def hkp():
+    from hash_top_kv_amd import probe
+    return probe
 
 
 def test_header_declares_the_five_calls():
@@ -34,6 +42,19 @@ def test_every_declared_symbol_is_exported(hk):
     missing = [n for n in _declared() if not hasattr(L, n)]
     assert not missing, missing
     assert set(_declared()) <= set(hk._SIGNATURES), "binding lacks a declared call"
+
+
+def test_probes_live_in_their_own_library(hk):
+    """The measurement aids are declared in hk_probe.h and exported by libhk_probe.so
+    only; the decode path's header and library hold the method alone."""
+    from hash_top_kv_amd import probe
+    names = _declared(PROBE_HEADER)
+    assert names and not set(names) & set(_declared())
+    Lp = ctypes.CDLL(probe.PROBE_LIB_PATH)
+    assert all(hasattr(Lp, n) for n in names)
+    assert set(names) <= set(probe._SIGNATURES)
+    L = ctypes.CDLL(hk.LIB_PATH)
+    assert not any(hasattr(L, n) for n in names)
 
 
 def test_strerror_covers_every_status(hk):
@@ -163,10 +184,10 @@ def test_host_validation_without_gpu(hk):
     assert L.hk_window_indices(-1, 4, 64, P, ctypes.byref(n), P) == hk.HK_ERR_INVALID_ARGUMENT
 
 
-def test_read_probe_host_checks(hk):
+def test_read_probe_host_checks(hkp):
     """The read probe rejects sizes that are not whole 16-byte vectors and missing
     pointers on the host; zero bytes enqueue nothing."""
-    L = hk.lib()
+    L = hkp.lib()
     assert L.hk_read_probe_sink_words(1 << 30) == (1 << 30) // 32768
     assert L.hk_read_probe_sink_words(16) == 1
     assert L.hk_read_probe(None, 24, None, None) == 1          # not a multiple of 16
@@ -175,10 +196,10 @@ def test_read_probe_host_checks(hk):
     assert L.hk_read_probe(ctypes.c_void_p(0x1008), 32, ctypes.c_void_p(0x2000), None) == 2
 
 
-def test_gather_probe_host_checks(hk):
+def test_gather_probe_host_checks(hkp):
     """The gather probe rejects bad workgroup sizes, negative counts and missing pointers
     on the host; an empty list enqueues nothing."""
-    L = hk.lib()
+    L = hkp.lib()
     P = ctypes.c_void_p(0x1000)
     assert L.hk_gather_probe_sink_words(1000, 512) == 2
     assert L.hk_gather_probe_sink_words(1024, 512) == 2

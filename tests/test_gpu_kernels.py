@@ -13,15 +13,18 @@ from helpers import codes_tensor, compare_codes, np_u32, say
 pytestmark = pytest.mark.gpu
 
 hk = None
+hkp = None
 
 
 @pytest.fixture(scope="module", autouse=True)
 def _lib():
-    global hk
+    global hk, hkp
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import hash_top_kv_amd
+    from hash_top_kv_amd import probe
     hk = hash_top_kv_amd
+    hkp = probe
 
 
 # ----------------------------------------------------------------- retrieval
@@ -566,9 +569,9 @@ def test_read_probe_reads_every_byte(nbytes):
     rng = np.random.default_rng(nbytes % 1000)
     data = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
     x = torch.from_numpy(data.view(np.int32)).cuda()
-    sink = hk.read_probe(x)
+    sink = hkp.read_probe(x)
     torch.cuda.synchronize()
-    words = int(hk.lib().hk_read_probe_sink_words(nbytes))
+    words = int(hkp.lib().hk_read_probe_sink_words(nbytes))
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)[:words])
     assert got == np.bitwise_xor.reduce(data)
 
@@ -588,9 +591,9 @@ def test_gather_probe_reads_every_row(rpb):
     idx[5], idx[77], idx[-1] = -3, rows, 2 ** 31 - 1       # outside the table: row 0
     k = torch.from_numpy(Kw.view(np.int32)).cuda()
     v = torch.from_numpy(Vw.view(np.int32)).cuda()
-    sink = hk.gather_probe(k, v, torch.from_numpy(idx).cuda(), rpb)
+    sink = hkp.gather_probe(k, v, torch.from_numpy(idx).cuda(), rpb)
     torch.cuda.synchronize()
-    words = int(hk.lib().hk_gather_probe_sink_words(idx.size, rpb))
+    words = int(hkp.lib().hk_gather_probe_sink_words(idx.size, rpb))
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)[:words])
     eff = np.where((idx >= 0) & (idx < rows), idx, 0)
     want = np.bitwise_xor.reduce(Kw[eff].ravel()) ^ np.bitwise_xor.reduce(Vw[eff].ravel())
