@@ -33,7 +33,7 @@ constexpr int64_t kResidentBlocks = 768;
 
 template <int LPT, bool BF16, int G, int MAXC, int REPS>
 __device__ __forceinline__ void emit_attend_body(
-    const uint32_t *__restrict__ stash, const uint32_t *__restrict__ hist, int bins, int64_t C,
+    const uint8_t *__restrict__ stash, const uint32_t *__restrict__ hist, int bins, int64_t C,
     int keff, int32_t *__restrict__ count, int S, int CPB, int Sc, int64_t lo, int k,
     int32_t *__restrict__ idx, const void *__restrict__ q, const void *__restrict__ kc,
     const void *__restrict__ vc, int Hq, int Hkv, int64_t cap, float scale_log2,
@@ -41,7 +41,6 @@ __device__ __forceinline__ void emit_attend_body(
     float *__restrict__ part_lse, int64_t rows, const int32_t *__restrict__ ctx_len,
     int64_t n_local, int64_t max_ctx) {
   constexpr int CH = kScanThreads * LPT;
-  static_assert(CH <= kListMax, "a chunk's selection must fit the list");
   static_assert(kHistLdsWords <= kListMax, "the chunk histograms are staged in the list");
   __shared__ __attribute__((aligned(16))) int32_t sel[kListMax];
   const int c = blockIdx.x;
@@ -88,33 +87,25 @@ __device__ __forceinline__ void emit_attend_body(
     auto g0 = [&](int r) { return (c + r * Sc) * cpb; };
     auto g1 = [&](int r) { return min(Sb, g0(r) + cpb); };
     int32_t *out = idx + (int64_t)bh * k;
-    // A group's stash words are staged in LDS (indexed by chunk at run time without
-    // scratch memory).  The first group's are requested before the threshold is derived,
-    // and arrive while it is.
-    __shared__ uint32_t sw[MAXC][LPT / 4][kScanThreads];
-    __shared__ int4 smt[REPS][MAXC];
-    auto load_stash = [&](int r, uint32_t(&wl)[MAXC][LPT / 4]) {
-#pragma unroll
-      for (int i = 0; i < MAXC; ++i) {
-        int ch = g0(r) + i < g1(r) ? g0(r) + i : g0(r);
-        ch = ch < S ? ch : S - 1;                // an empty group past the last chunk
-        const uint32_t *sp = stash + ((int64_t)bh * S + ch) * stash_words_per_chunk<LPT>();
-#pragma unroll
-        for (int i4 = 0; i4 < LPT / 4; ++i4) wl[i][i4] = sp[i4 * kScanThreads + t];
-      }
+    // A group's candidates are one run of the head's distance bytes (token order); thread
+    // t holds tokens [t*TPT, (t+1)*TPT) of the run.  The first group's bytes are requested
+    // before the threshold is derived, and arrive while it is.
+    constexpr int TPT = MAXC * LPT;
+    const uint8_t *dh = stash + (int64_t)bh * S * CH;
+    auto load_group = [&](int r, uint32_t(&w)[TPT / 4]) {
+      const bool ok = (int64_t)t * TPT < (int64_t)(g1(r) - g0(r)) * CH;
+      load_run<TPT>(dh, (int64_t)g0(r) * CH + (int64_t)t * TPT, ok, w);
     };
-    auto stage_stash = [&](const uint32_t(&wl)[MAXC][LPT / 4]) {
-#pragma unroll
-      for (int i = 0; i < MAXC; ++i)
-#pragma unroll
-        for (int i4 = 0; i4 < LPT / 4; ++i4) sw[i][i4][t] = wl[i][i4];
-    };
-    // The head's threshold, tie quota and the counts before each chunk of the groups,
-    // from the chunk histograms -- the computation of the threshold kernel, done by
-    // every workgroup of the head, which saves a kernel and its dependent round trip.
-    // When the head's bin counts fit in LDS (Sb * bins <= kHistLdsWords: up to 32 chunks
-    // of 128-bit codes), they are requested together with the stash and the threshold
-    // is derived from LDS, one round trip to memory instead of two.
+    __shared__ int2 gbase[REPS];               // head counts below / at T before group r
+    __shared__ uint32_t scan_lds[kScanThreads / 64];
+    uint32_t w[TPT / 4];
+    // The head's threshold, tie quota and the counts before each group, from the chunk
+    // histograms, derived by every workgroup of the head, which saves a kernel and its
+    // dependent round trip: two reads of the histograms (superbins, then the bins of the
+    // superbin holding T) and two exchanges.  When the head's bin counts fit in LDS
+    // (Sb * bins <= kHistLdsWords: up to 32 chunks of 128-bit codes), they are requested
+    // together with the distance bytes and the threshold is derived from LDS, one round
+    // trip to memory instead of two.
     int T, quota;
     {
       const int roww = bins + bins / 8;
@@ -132,12 +123,11 @@ __device__ __forceinline__ void emit_attend_body(
                           : make_uint4(0u, 0u, 0u, 0u);
         }
       }
-      uint32_t wl[MAXC][LPT / 4];
-      load_stash(0, wl);
+      load_group(0, w);
       auto sink = [&](int cc, const int4 &m) {
 #pragma unroll
         for (int r = 0; r < REPS; ++r)
-          if (cc >= g0(r) && cc < g1(r)) smt[r][cc - g0(r)] = m;
+          if (cc == g0(r)) gbase[r] = make_int2(m.x, m.y);
       };
       if (hist_lds) {
         uint32_t *hl = reinterpret_cast<uint32_t *>(sel);
@@ -151,65 +141,57 @@ __device__ __forceinline__ void emit_attend_body(
           head_threshold_lds<128>(hl, Sb, C, CH, keff, T, quota, sink);
         else
           head_threshold_lds<64>(hl, Sb, C, CH, keff, T, quota, sink);
-      } else if (bins == 128) {
-        head_threshold<128>(hh, Sb, C, CH, keff, T, quota, sink);
       } else {
-        head_threshold<64>(hh, Sb, C, CH, keff, T, quota, sink);
+        int gs[REPS], lb[REPS], eb[REPS];
+#pragma unroll
+        for (int r = 0; r < REPS; ++r) gs[r] = g0(r);
+        if (bins == 128)
+          head_threshold_groups<128, REPS>(hh, Sb, CH, keff, gs, T, quota, lb, eb);
+        else
+          head_threshold_groups<64, REPS>(hh, Sb, CH, keff, gs, T, quota, lb, eb);
+        if (t == 0 && T >= 0) {
+#pragma unroll
+          for (int r = 0; r < REPS; ++r) gbase[r] = make_int2(lb[r], eb[r]);
+        }
       }
       if (c == 0 && t == 0) count[bh] = keff;
-      stage_stash(wl);
     }
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < REPS; ++r) {
-      if (r > 0) {
-        // Every wavefront is done with the previous group's list and stash.
+      if (T < 0 || g0(r) >= g1(r)) break;      // uniform: nothing selected, or no chunks
+      if (r > 0) load_group(r, w);
+      const int2 gb = gbase[r];
+      const int64_t tok_t = lo + (int64_t)g0(r) * CH + (int64_t)t * TPT;   // thread's first token
+      RunSelect<TPT> rs;
+      rs.build(w, T, quota, gb.x, gb.y, scan_lds);
+      const int total = rs.total, first = rs.first;
+      // The group's selected tokens occupy positions [first, first + total) of the head's
+      // list.  They go to the LDS list first and to the index list afterwards, in
+      // coalesced stores; the workgroup attends over the LDS list.
+      const int n0 = min(total, kListMax);
+      if (n0 > 0) {
+        rs.emit(0, n0, [&](int pos, int off) { sel[pos] = (int32_t)(tok_t + off); });
         __syncthreads();
-        uint32_t wl[MAXC][LPT / 4];
-        load_stash(r, wl);
-        stage_stash(wl);
+        for (int rr = t; rr < n0; rr += kScanThreads) out[first + rr] = sel[rr];
+        attend_list(n0);
+      }
+      // More than the list holds (a budget of thousands of tokens per group): further
+      // rounds of kListMax positions, each rebuilding the masks from the distance bytes
+      // so that no mask stays live through the attention.
+      for (int base = kListMax; base < total; base += kListMax) {
+        __syncthreads();                       // every wavefront is done with the list
+        uint32_t w2[TPT / 4];
+        load_group(r, w2);
+        RunSelect<TPT> rs2;
+        rs2.build(w2, T, quota, gb.x, gb.y, scan_lds);
+        const int n = min(total - base, kListMax);
+        rs2.emit(base, base + n, [&](int pos, int off) { sel[pos - base] = (int32_t)(tok_t + off); });
         __syncthreads();
+        for (int rr = t; rr < n; rr += kScanThreads) out[first + base + rr] = sel[rr];
+        attend_list(n);
       }
-      const int c0 = g0(r);
-      const int nch = g1(r) - c0;
-      const int4 *mt_r = smt[r];
-      int total = 0;
-#pragma unroll
-      for (int i = 0; i < MAXC; ++i)
-        total += (i < nch && T >= 0) ? chunk_selected(mt_r[i], quota) : 0;
-      if (total > 0 && total <= kListMax) {
-        // All chunks compacted together: the group's selected tokens occupy positions
-        // [first, first + total) of the head's list.  The list goes to LDS first and to
-        // the index list afterwards, in coalesced stores.
-        const int4 m0 = mt_r[0];
-        const int first = m0.x + min(m0.y, quota);
-        emit_chunks_lanes<LPT, MAXC>(sw, mt_r, nch, T, quota, lo + (int64_t)c0 * CH, first, sel);
-        for (int rr = t; rr < total; rr += kScanThreads) out[first + rr] = sel[rr];
-        attend_list(total);
-      } else if (total > kListMax) {
-        // Too many for the list: chunk by chunk, attending whenever the list would overflow.
-        int len = 0;
-        for (int i = 0; i < nch; ++i) {
-          const int4 mt = mt_r[i];
-          const int nsel = chunk_selected(mt, quota);
-          if (nsel == 0) continue;
-          if (len + nsel > kListMax) {
-            attend_list(len);
-            __syncthreads();                   // the list is reused
-            len = 0;
-          }
-          const int base = len - (mt.x + min(mt.y, quota));   // list slot = base + position
-          emit_chunks<LPT, 1>([&](int, int kk) { return sw[i][kk][t]; }, [&](int) { return mt; },
-                              1, T, quota, lo + (int64_t)(c0 + i) * CH,
-                              [&](int pos, int32_t tok) {
-                                out[pos] = tok;
-                                sel[base + pos] = tok;
-                              });
-          __syncthreads();
-          len += nsel;
-        }
-        if (len > 0) attend_list(len);
-      }
+      __syncthreads();                         // the list and scan_lds are reused
     }
     if (!ga_ready) ga.init(q, row0, scale_log2);
   } else {
@@ -225,7 +207,7 @@ __device__ __forceinline__ void emit_attend_body(
 }
 
 #define HK_EMIT_ATTEND_PARAMS                                                                 \
-  const uint32_t *__restrict__ stash, const uint32_t *__restrict__ hist, int bins, int64_t C, \
+  const uint8_t *__restrict__ stash, const uint32_t *__restrict__ hist, int bins, int64_t C,  \
       int keff, int32_t *__restrict__ count, int S, int CPB, int Sc, int64_t lo, int k,      \
       int32_t *__restrict__ idx, const void *__restrict__ q, const void *__restrict__ kc,    \
       const void *__restrict__ vc, int Hq, int Hkv, int64_t cap, float scale_log2,           \
@@ -239,8 +221,8 @@ __device__ __forceinline__ void emit_attend_body(
 
 // bf16 (matrix cores): held to 168 VGPRs, three workgroups per CU.  fp32 (VALU) keeps
 // the compiler's choice: its accumulators would spill under that limit.  MAXC (8, or 4
-// when the plan puts at most 4 chunks in a workgroup) sizes the staged stash and the
-// compaction, which handle all MAXC slots at once.  REPS (1 or 2) chunk groups per
+// when the plan puts at most 4 chunks in a workgroup) sizes the run of distance bytes a
+// thread holds (MAXC * LPT tokens) and selects from.  REPS (1 or 2) chunk groups per
 // chunk workgroup: 2 when one group of 8 chunks per workgroup would need more workgroups
 // than are resident at once.
 template <int LPT, int G, int MAXC, int REPS>
@@ -256,7 +238,7 @@ __global__ __launch_bounds__(kScanThreads) void emit_attend_f32_kernel(HK_EMIT_A
 #undef HK_EMIT_ATTEND_ARGS
 
 template <int LPT, bool BF16, int G, int MAXC, int REPS>
-void fused_launch_c(const FusedPlan &p, const uint32_t *stash, const uint32_t *hist,
+void fused_launch_c(const FusedPlan &p, const uint8_t *stash, const uint32_t *hist,
                   int32_t *count, int k, int32_t *idx, const void *q, const void *kc,
                   const void *vc, int Hq, int Hkv, int64_t cap, float scale_log2, float *po,
                   float *pl, int64_t rows, const int32_t *ctx_len, hipStream_t st) {
@@ -275,7 +257,7 @@ void fused_launch_c(const FusedPlan &p, const uint32_t *stash, const uint32_t *h
 }
 
 template <int LPT, bool BF16, int G>
-void fused_launch(const FusedPlan &p, const uint32_t *stash, const uint32_t *hist,
+void fused_launch(const FusedPlan &p, const uint8_t *stash, const uint32_t *hist,
                   int32_t *count, int k, int32_t *idx, const void *q, const void *kc,
                   const void *vc, int Hq, int Hkv, int64_t cap, float scale_log2, float *po,
                   float *pl, int64_t rows, const int32_t *ctx_len, hipStream_t st) {
@@ -291,7 +273,7 @@ void fused_launch(const FusedPlan &p, const uint32_t *stash, const uint32_t *his
 }
 
 template <int LPT, bool BF16>
-void fused_dispatch_g(const FusedPlan &p, const uint32_t *stash, const uint32_t *hist,
+void fused_dispatch_g(const FusedPlan &p, const uint8_t *stash, const uint32_t *hist,
                       int32_t *count, int k, int32_t *idx, const void *q, const void *kc,
                       const void *vc, int Hq, int Hkv, int64_t cap, float sl2, float *po,
                       float *pl, int64_t rows, const int32_t *ctx_len, hipStream_t st) {
@@ -379,7 +361,7 @@ hipError_t launch_fused_attend(const FusedPlan &p, const void *q, const void *kc
   float *po = reinterpret_cast<float *>(w8 + p.off_o);
   float *pl = reinterpret_cast<float *>(w8 + p.off_lse);
   if (p.parts > 0) {
-    const uint32_t *stash = reinterpret_cast<const uint32_t *>(w8 + p.r.off_stash);
+    const uint8_t *stash = w8 + p.r.off_stash;
     const uint32_t *hist = reinterpret_cast<const uint32_t *>(w8 + p.r.off_hist);
     const float sl2 = scale * kLog2e;
     const bool bf = dtype == HK_BF16;

@@ -38,7 +38,7 @@ constexpr int64_t kStashNtBytes = 8 << 20;
 template <int W, int LPT, bool NT_STASH>
 __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
     const uint32_t *__restrict__ codes, const uint32_t *__restrict__ qcodes, int64_t cap,
-    int64_t lo, int64_t C, int S, uint32_t *__restrict__ stash, uint32_t *__restrict__ hist_out,
+    int64_t lo, int64_t C, int S, uint8_t *__restrict__ stash, uint32_t *__restrict__ hist_out,
     const int32_t *__restrict__ ctx_len, int Hkv, int64_t n_local, int64_t max_ctx) {
   constexpr int BINS = 32 * W;
   constexpr int NBP = BINS + 4;
@@ -84,25 +84,20 @@ __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
   for (int w = 0; w < W; ++w) q[w] = qcodes[(int64_t)bh * W + w];
   __syncthreads();
 
-  uint32_t *st = stash + ((int64_t)bh * S + c) * stash_words_per_chunk<LPT>();
+  // Distance bytes in token order: item i of the wavefront is one 64-byte store.
+  uint8_t *st = stash + (int64_t)bh * S * CH + pw;
 #pragma unroll
-  for (int i4 = 0; i4 < LPT / 4; ++i4) {
-    uint32_t packed = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = 4 * i4 + j;
-      const int64_t p = pw + 64 * i;
-      uint32_t d = 0xFFu;                      // past the last candidate: never selected
-      if (p < C) {
-        d = CV::dist(v[i], q);
-        atomicAdd(&hist[wave][d], 1u);
-      }
-      packed |= d << (8 * j);
+  for (int i = 0; i < LPT; ++i) {
+    const int64_t p = pw + 64 * i;
+    uint32_t d = 0xFFu;                        // past the last candidate: never selected
+    if (p < C) {
+      d = CV::dist(v[i], q);
+      atomicAdd(&hist[wave][d], 1u);
     }
     if constexpr (NT_STASH)
-      __builtin_nontemporal_store(packed, st + i4 * kScanThreads + t);
+      __builtin_nontemporal_store((uint8_t)d, st + 64 * i);
     else
-      st[i4 * kScanThreads + t] = packed;
+      st[64 * i] = (uint8_t)d;
   }
   __syncthreads();
   constexpr int NSB = BINS / 8;
@@ -139,28 +134,30 @@ __global__ __launch_bounds__(kThrThreads) void topk_threshold_kernel(
   }
 }
 
-// grid (S, BH).  Same thread <-> token mapping as the scan.
+// grid (S, BH): chunk c of head bh, thread t its tokens [t*LPT, (t+1)*LPT).
 template <int LPT>
 __global__ __launch_bounds__(kScanThreads) void topk_emit_kernel(
-    const uint32_t *__restrict__ stash, const int4 *__restrict__ meta,
+    const uint8_t *__restrict__ stash, const int4 *__restrict__ meta,
     const int2 *__restrict__ params, int S, int64_t lo, int k, int32_t *__restrict__ idx) {
   constexpr int CH = kScanThreads * LPT;
+  __shared__ uint32_t lds[kScanThreads / 64];
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
   const int t = threadIdx.x;
   // Issue every load of the block before branching on any of them.
   const int2 pr = params[bh];
   const int4 mt = meta[(int64_t)bh * S + c];
-  const uint32_t *sp = stash + ((int64_t)bh * S + c) * stash_words_per_chunk<LPT>();
   uint32_t w[LPT / 4];
-#pragma unroll
-  for (int i4 = 0; i4 < LPT / 4; ++i4) w[i4] = sp[i4 * kScanThreads + t];
+  load_run<LPT>(stash + ((int64_t)bh * S + c) * CH, (int64_t)t * LPT, true, w);
   const int T = pr.x;
   const int quota = pr.y;
-  if (T < 0 || chunk_selected(mt, quota) == 0) return;
-  int32_t *out = idx + (int64_t)bh * k;
-  emit_chunks<LPT, 1>([&](int, int kk) { return w[kk]; }, [&](int) { return mt; }, 1, T, quota,
-                      lo + (int64_t)c * CH, [&](int pos, int32_t tok) { out[pos] = tok; });
+  const int ties = quota - mt.y;
+  if (T < 0 || mt.z + (ties <= 0 ? 0 : (ties < mt.w ? ties : mt.w)) == 0) return;
+  RunSelect<LPT> rs;
+  rs.build(w, T, quota, mt.x, mt.y, lds);
+  int32_t *out = idx + (int64_t)bh * k + rs.first;
+  const int32_t tok0 = (int32_t)(lo + (int64_t)c * CH) + LPT * t;
+  rs.emit(0, rs.total, [&](int pos, int off) { out[pos] = tok0 + off; });
 }
 
 __global__ void window_indices_kernel(int32_t n_sinks, int64_t local0, int32_t n,
@@ -176,7 +173,7 @@ __global__ void window_indices_kernel(int32_t n_sinks, int64_t local0, int32_t n
 template <int W, int LPT, int G, bool NT_STASH>
 __global__ __launch_bounds__(kScanThreads) void hamming_scan_group_kernel(
     const uint32_t *__restrict__ codes, const uint32_t *__restrict__ qcodes, int64_t cap,
-    int64_t lo, int64_t C, int S, uint32_t *__restrict__ stash, uint32_t *__restrict__ hist_out) {
+    int64_t lo, int64_t C, int S, uint8_t *__restrict__ stash, uint32_t *__restrict__ hist_out) {
   constexpr int BINS = 32 * W;
   constexpr int NBP = BINS + 4;
   constexpr int CH = kScanThreads * LPT;
@@ -208,25 +205,19 @@ __global__ __launch_bounds__(kScanThreads) void hamming_scan_group_kernel(
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    uint32_t *st = stash + (((int64_t)bh * G + g) * S + c) * stash_words_per_chunk<LPT>();
+    uint8_t *st = stash + ((int64_t)bh * G + g) * S * CH + pw;
 #pragma unroll
-    for (int i4 = 0; i4 < LPT / 4; ++i4) {
-      uint32_t packed = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * i4 + j;
-        const int64_t p = pw + 64 * i;
-        uint32_t d = 0xFFu;
-        if (p < C) {
-          d = CV::dist(v[i], q[g]);
-          atomicAdd(&hist[g][wave][d], 1u);
-        }
-        packed |= d << (8 * j);
+    for (int i = 0; i < LPT; ++i) {
+      const int64_t p = pw + 64 * i;
+      uint32_t d = 0xFFu;
+      if (p < C) {
+        d = CV::dist(v[i], q[g]);
+        atomicAdd(&hist[g][wave][d], 1u);
       }
       if constexpr (NT_STASH)
-        __builtin_nontemporal_store(packed, st + i4 * kScanThreads + t);
+        __builtin_nontemporal_store((uint8_t)d, st + 64 * i);
       else
-        st[i4 * kScanThreads + t] = packed;
+        st[64 * i] = (uint8_t)d;
     }
   }
   __syncthreads();
@@ -252,7 +243,7 @@ __global__ __launch_bounds__(kScanThreads) void hamming_scan_group_kernel(
 
 template <int W, int LPT>
 void scan_group_launch(const RetrievePlan &p, int G, const uint32_t *codes,
-                       const uint32_t *qcodes, int64_t cap, uint32_t *stash, uint32_t *hist,
+                       const uint32_t *qcodes, int64_t cap, uint8_t *stash, uint32_t *hist,
                        hipStream_t st) {
   const dim3 grid(p.S, p.BH / G), blk(kScanThreads);
   // p.BH counts query heads here: the distance bytes of all of them
@@ -272,7 +263,7 @@ void scan_group_launch(const RetrievePlan &p, int G, const uint32_t *codes,
 
 template <int W, int LPT>
 void scan_launch(const RetrievePlan &p, const uint32_t *codes, const uint32_t *qcodes,
-                 int64_t cap, uint32_t *stash, uint32_t *hist, const int32_t *ctx_len, int Hkv,
+                 int64_t cap, uint8_t *stash, uint32_t *hist, const int32_t *ctx_len, int Hkv,
                  int64_t n_local, int64_t max_ctx, hipStream_t st) {
   if ((int64_t)p.BH * p.S * p.ch > kStashNtBytes)
     hipLaunchKernelGGL((hamming_scan_kernel<W, LPT, true>), dim3(p.S, p.BH), dim3(kScanThreads),
@@ -323,7 +314,7 @@ hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
                                int64_t n_local, int64_t max_ctx) {
   if (p.BH == 0 || p.S == 0) return hipSuccess;
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  uint32_t *stash = reinterpret_cast<uint32_t *>(w8 + p.off_stash);
+  uint8_t *stash = w8 + p.off_stash;
   uint32_t *hist = reinterpret_cast<uint32_t *>(w8 + p.off_hist);
 #define HK_SCAN(WW, LL) \
   scan_launch<WW, LL>(p, codes, qcodes, cap, stash, hist, ctx_len, Hkv, n_local, max_ctx, st)
@@ -344,7 +335,7 @@ hipError_t launch_hamming_scan_qheads(const RetrievePlan &p, int G, const uint32
   if (G == 1) return launch_hamming_scan(p, codes, qcodes, cap, ws, st);
   if (p.BH == 0 || p.S == 0) return hipSuccess;
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  uint32_t *stash = reinterpret_cast<uint32_t *>(w8 + p.off_stash);
+  uint8_t *stash = w8 + p.off_stash;
   uint32_t *hist = reinterpret_cast<uint32_t *>(w8 + p.off_hist);
   if (p.W == 4) {
     if (p.lpt == 8) scan_group_launch<4, 8>(p, G, codes, qcodes, cap, stash, hist, st);
@@ -378,7 +369,7 @@ hipError_t launch_topk_select(const RetrievePlan &p, int k, int32_t *idx, int32_
   hipError_t e = launch_topk_threshold(p, count, ws, st);
   if (e != hipSuccess || p.S == 0 || p.keff == 0) return e;
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  const uint32_t *stash = reinterpret_cast<const uint32_t *>(w8 + p.off_stash);
+  const uint8_t *stash = w8 + p.off_stash;
   const int4 *meta = reinterpret_cast<const int4 *>(w8 + p.off_meta);
   const int2 *params = reinterpret_cast<const int2 *>(w8 + p.off_params);
   if (p.lpt == 8)

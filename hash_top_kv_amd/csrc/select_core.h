@@ -10,125 +10,190 @@ constexpr int kScanThreads = 256;
 
 // Token order within a chunk: wavefront w owns tokens [w*64*LPT, (w+1)*64*LPT), and its
 // item i covers tokens w*64*LPT + 64*i + lane, so every load instruction of a wavefront
-// reads 64 consecutive codes.  A thread's distances are stored four to a 32-bit word:
-// word (i/4)*256 + t of the chunk holds items i..i+3 of thread t (one coalesced dword
-// store per four tokens).
-template <int LPT>
-__device__ __forceinline__ int64_t stash_words_per_chunk() { return (int64_t)LPT / 4 * kScanThreads; }
+// reads 64 consecutive codes.  The distances are stored in token order: byte p of a
+// head's distance bytes is candidate p's distance (255 past the last candidate, never
+// selected), so each item is one coalesced 64-byte store per wavefront and a reader finds
+// any run of consecutive tokens in consecutive bytes.
 
-// Number of tokens a chunk contributes to the selection: all of its tokens below the
-// threshold and the ties that fall inside the quota.
-__device__ __forceinline__ int chunk_selected(const int4 &mt, int quota) {
-  const int ties = quota - mt.y;
-  return mt.z + (ties <= 0 ? 0 : (ties < mt.w ? ties : mt.w));
+// Bits 8, 9, 24, 25 of the result flag the bytes 0, 1, 2, 3 of w (four consecutive tokens)
+// whose value is >= t, for 0 <= t <= 256 given as tt = t | t << 16.  Each byte x sits in a
+// 16-bit field as 0x100 | x, from which t is subtracted: bit 8 of the field survives exactly
+// when x >= t, and no borrow leaves the field (0x100 + x - t >= 0).
+constexpr uint32_t kByteFlags = 0x03000300u;
+__device__ __forceinline__ uint32_t bytes_ge(uint32_t w, uint32_t tt) {
+  const uint32_t ev = (w & 0x00FF00FFu) | 0x01000100u;
+  const uint32_t od = ((w >> 8) & 0x00FF00FFu) | 0x01000100u;
+  return ((ev - tt) & 0x01000100u) | (((od - tt) & 0x01000100u) << 1);
 }
 
-// Number of set bits of m below this lane.
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+// Inclusive prefix sum over the 64 lanes of a wavefront: shifts within rows of 16 lanes,
+// then the row totals broadcast to the following rows (DPP row_shr, row_bcast:15/31).
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
 }
 
-// Writes the selected tokens of nch consecutive chunks (nch uniform, at most MAXC):
-// word(i, k) is this thread's k-th stash word of chunk i, meta(i) the chunk's counts below
-// / at T before it and its own, and chunk i starts at token tok0 + i*CH.  sink(position
-// in the head's list, token) is called for every selected token.  Called by all threads
-// of the workgroup.
-//
-// The tie quota splits at most one chunk of a head.  Every other chunk takes exactly its
-// tokens with D < T (the quota is used up before it) or with D <= T (its ties all fit),
-// so one ballot per item decides, and a token's position is the chunk's first position
-// plus the selected count in earlier wavefronts of the chunk (one exchange through LDS),
-// in the wavefront's earlier items (a running count) and in lower lanes (mbcnt).  The
-// chunk holding the quota boundary ranks ties and non-ties separately.
-template <int LPT, int MAXC, class Word, class Meta, class Sink>
-__device__ __forceinline__ void emit_chunks(Word word, Meta meta, int nch, int T, int quota,
-                                            int64_t tok0, Sink sink) {
-  constexpr int NW = kScanThreads / 64;
-  constexpr int CH = kScanThreads * LPT;
-  __shared__ uint32_t wcnt[2][MAXC][NW];      // per (chunk, wavefront) counts
-  const int t = threadIdx.x;
-  const int wave = t >> 6;
-  const int lane = t & 63;
-  // mode of a chunk: 0 = D < T, 1 = D <= T, 2 = split by the quota
-  auto mode_of = [&](const int4 &mt) {
-    return mt.y >= quota ? 0 : (mt.y + mt.w <= quota ? 1 : 2);
-  };
-#pragma unroll 1
-  for (int i = 0; i < nch; ++i) {
-    const int mode = mode_of(meta(i));
-    uint32_t wv[LPT / 4];
+// Exclusive prefix over the 256 threads of a workgroup: DPP scans within the wavefronts,
+// the wavefront totals through lds[4].  Returns the prefix and sets total.  Called by all
+// threads; lds may be reused after the caller's next barrier.
+__device__ __forceinline__ uint32_t block_excl_scan_dpp(uint32_t v, uint32_t *lds,
+                                                        uint32_t &total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan_dpp(v);
+  if (lane == 63) lds[wave] = inc;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
 #pragma unroll
-    for (int k = 0; k < LPT / 4; ++k) wv[k] = word(i, k);
-    uint32_t n0 = 0, n1 = 0;
-    if (mode < 2) {
-      const int lim = T + mode;               // selected: D < lim
+  for (int w = 0; w < kScanThreads / 64; ++w) {
+    const uint32_t x = lds[w];
+    off += w < wave ? x : 0u;
+    tot += x;
+  }
+  total = tot;
+  return off + inc - v;
+}
+
+// Flags at bit 7 of each byte of w (four consecutive tokens) for the bytes >= t, for
+// 0 <= t <= 127 given as t4 = t * 0x01010101: a byte of 128 or more (distance 128 of
+// 128-bit codes, 255 past the last candidate) carries bit 7 itself, and for the others
+// (x | 0x80) - t keeps bit 7 exactly when x >= t, with no borrow out of the byte.
+constexpr uint32_t kByteHigh = 0x80808080u;
+__device__ __forceinline__ uint32_t bytes_ge7(uint32_t w, uint32_t t4) {
+  return (((w | kByteHigh) - t4) | w) & kByteHigh;
+}
+// The flags (bit 7 of each byte) of two words as 8 bits in token order: byte b of fa at
+// bit b, byte b of fb at bit 4 + b.  x holds fa's flags at bits 0, 8, 16, 24 and fb's at
+// 4, 12, 20, 28; the multiply by 2^21 + 2^14 + 2^7 + 1 adds four shifted copies of x whose
+// bits differ mod 4, so no two bits meet (no carries), and bits 21 .. 28 of the product
+// are the eight flags in order.
+__device__ __forceinline__ uint32_t high_pair_to_byte(uint32_t fa, uint32_t fb) {
+  return (((fa >> 7) | (fb >> 3)) * 0x00204081u >> 21) & 0xFFu;
+}
+// Bits 8, 9, 24, 25 (the flags of bytes_ge) moved to bits 0..3.
+__device__ __forceinline__ uint32_t spread_to_nibble(uint32_t f) {
+  return ((f >> 8) & 3u) | ((f >> 22) & 0xCu);
+}
+// The lowest n set bits of m (all of them when n >= popcount(m)).
+__device__ __forceinline__ uint32_t lowest_bits(uint32_t m, int n) {
+  if (n <= 0) return 0u;
+  uint32_t rest = m;
+  for (int i = 0; i < n && rest; ++i) rest &= rest - 1u;
+  return m & ~rest;
+}
+
+// The selected tokens of a run of a head's candidates, with TPT consecutive tokens per
+// thread of a 256-thread workgroup (TPT a multiple of 4, at most 64).  Selected are the
+// tokens with D < T and the first `quota` tokens of the head with D == T in token order.
+//   build(): from this thread's distance bytes w (bytes past the run set to 255) and the
+//     head's counts below and at T before the run: one block-wide scan of the packed
+//     counts below / at T gives the counts before this thread's first token, hence its
+//     share of the tie quota; then this thread's mask of selected tokens (bit j = token j)
+//     and the number of the head's selected tokens before its first one;
+//   emit(): sink(position - first, token offset in the thread's run) for every selected
+//     token whose list position p - first lies in [lo, hi), visiting only the set bits.
+// The top-k list is written in token order, so a selected token's position is the number
+// of selected tokens before it: (below before) + min(at before, quota) for the thread,
+// plus its rank among the thread's own.
+template <int TPT>
+struct RunSelect {
+  static_assert(TPT % 4 == 0 && TPT <= 64, "4 .. 64 tokens per thread");
+  static constexpr int NWD = TPT / 4;
+  static constexpr int NH = (TPT + 31) / 32;   // 32-bit mask words
+  uint32_t sel[NH];
+  int selb, total, first;
+
+  __device__ void build(const uint32_t (&w)[NWD], int T, int quota, int lt_before, int eq_before,
+                        uint32_t *lds) {
+    uint32_t lt[NH], eq[NH];
 #pragma unroll
-      for (int j = 0; j < LPT; ++j)
-        n0 += (uint32_t)__popcll(__ballot((int)((wv[j >> 2] >> (8 * (j & 3))) & 0xFFu) < lim));
+    for (int h = 0; h < NH; ++h) lt[h] = eq[h] = 0u;
+    if (T <= 126) {                            // uniform
+      const uint32_t t0 = (uint32_t)T * 0x01010101u, t1 = t0 + 0x01010101u;
+      uint32_t fl[NWD], fe[NWD];
+#pragma unroll
+      for (int k = 0; k < NWD; ++k) {
+        const uint32_t ge0 = bytes_ge7(w[k], t0), ge1 = bytes_ge7(w[k], t1);
+        fl[k] = ~ge0 & kByteHigh;
+        fe[k] = ge0 & ~ge1;
+      }
+#pragma unroll
+      for (int k = 0; k < NWD; k += 2) {
+        const uint32_t bl = high_pair_to_byte(fl[k], k + 1 < NWD ? fl[k + 1] : 0u);
+        const uint32_t be = high_pair_to_byte(fe[k], k + 1 < NWD ? fe[k + 1] : 0u);
+        lt[k / 8] |= bl << (4 * (k % 8));
+        eq[k / 8] |= be << (4 * (k % 8));
+      }
     } else {
+      const uint32_t t0 = (uint32_t)T | ((uint32_t)T << 16), t1 = t0 + 0x00010001u;
 #pragma unroll
-      for (int j = 0; j < LPT; ++j) {
-        const int d = (int)((wv[j >> 2] >> (8 * (j & 3))) & 0xFFu);
-        n0 += (uint32_t)__popcll(__ballot(d < T));
-        n1 += (uint32_t)__popcll(__ballot(d == T));
+      for (int k = 0; k < NWD; ++k) {
+        const uint32_t ge0 = bytes_ge(w[k], t0), ge1 = bytes_ge(w[k], t1);
+        lt[k / 8] |= spread_to_nibble(~ge0 & kByteFlags) << (4 * (k % 8));
+        eq[k / 8] |= spread_to_nibble(ge0 & ~ge1) << (4 * (k % 8));
       }
     }
-    if (lane == 0) {
-      wcnt[0][i][wave] = n0;
-      wcnt[1][i][wave] = n1;
+    uint32_t n = 0;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) n += (uint32_t)__popc(lt[h]) | ((uint32_t)__popc(eq[h]) << 16);
+    uint32_t tot;
+    const uint32_t before = block_excl_scan_dpp(n, lds, tot);
+    const int ltb = lt_before + (int)(before & 0xFFFFu);
+    const int eqb = eq_before + (int)(before >> 16);
+    // this thread's ties within the quota: the first quota - eqb of them
+    int take = quota - eqb;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const int c = __popc(eq[h]);
+      sel[h] = lt[h] | (take >= c ? eq[h] : lowest_bits(eq[h], take));
+      take -= c;
+    }
+    const int tl = (int)(tot & 0xFFFFu), te = (int)(tot >> 16);
+    const int ties = quota - eq_before;
+    total = tl + (ties <= 0 ? 0 : (ties < te ? ties : te));
+    first = lt_before + min(eq_before, quota);
+    selb = ltb + min(eqb, quota) - first;      // run position of this thread's first selected
+  }
+
+  template <class Sink>
+  __device__ void emit(int lo, int hi, Sink sink) const {
+    int r = selb;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      uint32_t m = sel[h];
+      while (m) {
+        const int bb = __builtin_ctz(m);
+        const int pos = r + __popc(sel[h] & ((1u << bb) - 1u));
+        m &= m - 1u;
+        if (pos >= lo && pos < hi) sink(pos, 32 * h + bb);
+      }
+      r += __popc(sel[h]);
     }
   }
-  __syncthreads();
-#pragma unroll 1
-  for (int i = 0; i < nch; ++i) {
-    const int4 mt = meta(i);
-    const int mode = mode_of(mt);
-    uint32_t wv[LPT / 4];
+};
+
+// Loads the TPT distance bytes of tokens [p, p + TPT) from a head's distance bytes d (16-
+// byte aligned runs), or 255s when ok is false.
+template <int TPT>
+__device__ __forceinline__ void load_run(const uint8_t *d, int64_t p, bool ok,
+                                         uint32_t (&w)[TPT / 4]) {
+  if constexpr (TPT % 16 == 0) {
 #pragma unroll
-    for (int k = 0; k < LPT / 4; ++k) wv[k] = word(i, k);
-    const int64_t tw = tok0 + (int64_t)i * CH + (int64_t)wave * (64 * LPT) + lane;
-    if (mode < 2) {
-      const int lim = T + mode;
-      int run = mt.x + min(mt.y, quota);      // first position of the chunk
-#pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2)
-        if (w2 < wave) run += (int)wcnt[0][i][w2];
-#pragma unroll
-      for (int j = 0; j < LPT; ++j) {
-        const bool take = (int)((wv[j >> 2] >> (8 * (j & 3))) & 0xFFu) < lim;
-        const uint64_t m = __ballot(take);
-        if (m) {
-          if (take) sink(run + lanes_below(m), (int32_t)(tw + 64 * j));
-          run += __popcll(m);
-        }
-      }
-    } else {
-      int run_lt = mt.x, run_eq = mt.y;
-#pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) {
-        if (w2 < wave) {
-          run_lt += (int)wcnt[0][i][w2];
-          run_eq += (int)wcnt[1][i][w2];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < LPT; ++j) {
-        const int d = (int)((wv[j >> 2] >> (8 * (j & 3))) & 0xFFu);
-        const uint64_t blt = __ballot(d < T), beq = __ballot(d == T);
-        if (blt | beq) {
-          if (d <= T) {
-            const int lt_rank = run_lt + lanes_below(blt);
-            const int eq_rank = run_eq + lanes_below(beq);
-            int pos = -1;
-            if (d < T) pos = lt_rank + min(eq_rank, quota);
-            else if (eq_rank < quota) pos = lt_rank + eq_rank;
-            if (pos >= 0) sink(pos, (int32_t)(tw + 64 * j));
-          }
-          run_lt += __popcll(blt);
-          run_eq += __popcll(beq);
-        }
-      }
+    for (int i = 0; i < TPT / 16; ++i) {
+      const uint4 v = ok ? reinterpret_cast<const uint4 *>(d + p)[i]
+                         : make_uint4(~0u, ~0u, ~0u, ~0u);
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
     }
+  } else if constexpr (TPT == 8) {
+    const uint2 v = ok ? *reinterpret_cast<const uint2 *>(d + p) : make_uint2(~0u, ~0u);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    static_assert(TPT == 4, "4, 8 or a multiple of 16 tokens per thread");
+    w[0] = ok ? *reinterpret_cast<const uint32_t *>(d + p) : ~0u;
   }
 }
 
@@ -145,18 +210,6 @@ __device__ __forceinline__ void load_u32x(const uint32_t *p, uint32_t (&x)[K]) {
     x[4 * i + 2] = v.z;
     x[4 * i + 3] = v.w;
   }
-}
-
-// Inclusive prefix sum over the 64 lanes of a wavefront: shifts within rows of 16 lanes,
-// then the row totals broadcast to the following rows (DPP row_shr, row_bcast:15/31).
-__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);   // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);   // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);   // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);   // row_shr:8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return v;
 }
 
 // The threshold of one head, computed by one workgroup of kThrThreads threads, one thread
@@ -312,6 +365,135 @@ __device__ __forceinline__ void head_threshold(const uint32_t *__restrict__ hb, 
   quota_out = quota;
 }
 
+// The threshold of one head together with the counts of the head's tokens below / at it
+// before the first chunk of each of NG groups, by one workgroup of kThrThreads threads
+// (one thread per chunk, tiles of kThrThreads chunks) from the chunk histograms
+// hb[S][BINS + BINS/8].  Level 1 is head_threshold's: the superbin totals give the
+// superbin Ts holding T.  Level 2 reads that superbin's 8 bins of every chunk once and
+// reduces, in one exchange, both the 8 bin totals (which give T and the tie quota) and,
+// for every group g, the sums over the chunks c < gs[g] of (c's superbins below Ts) and of
+// its 8 bins; the counts below / at T before the group follow from prefix sums over
+// those totals, whatever bin of Ts holds T.  T = -1 when k_eff = 0 (the counts are then
+// left unset); T = BINS when the histogrammed distances hold fewer than k_eff candidates
+// (distance BINS is not in the histogram: its count is the chunk size minus the others).
+// Every thread returns the same T, quota and counts.
+template <int BINS, int NG>
+__device__ __forceinline__ void head_threshold_groups(const uint32_t *__restrict__ hb, int S,
+                                                      int CH, int keff, const int (&gs)[NG],
+                                                      int &T_out, int &quota_out,
+                                                      int (&lt_before)[NG], int (&eq_before)[NG]) {
+  constexpr int NSB = BINS / 8;
+  constexpr int ROW = BINS + NSB;
+  constexpr int NT = kThrThreads;
+  constexpr int NW = NT / 64;
+  constexpr int NV = 8 + 9 * NG;               // reduced values of level 2
+  constexpr int K = NV <= 16 ? 16 : 32;
+  static_assert(NV <= 32, "at most 2 groups");
+  __shared__ uint32_t red1[NW][16];
+  __shared__ uint32_t red2[NW][K];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  auto row = [&](int c) { return hb + (int64_t)(c < S ? c : S - 1) * ROW; };
+  int T = -1, quota = 0;
+  if (keff > 0) {
+    // level 1: superbin totals
+    uint32_t sb0[NSB], acc[NSB];
+#pragma unroll
+    for (int i = 0; i < NSB; ++i) acc[i] = 0u;
+    for (int c0 = 0; c0 < S; c0 += NT) {
+      uint32_t x[NSB];
+      load_u32x<NSB>(row(c0 + tid) + BINS, x);
+      const bool ok = c0 + tid < S;
+#pragma unroll
+      for (int i = 0; i < NSB; ++i) {
+        x[i] = ok ? x[i] : 0u;
+        acc[i] += x[i];
+        if (c0 == 0) sb0[i] = x[i];
+      }
+    }
+    const uint32_t r1 = wave_transpose_sum<NSB>(acc);
+    if (lane < NSB) red1[wave][bitrev_k<NSB>(lane)] = r1;
+    __syncthreads();
+    uint32_t tot = 0;
+    if (lane < NSB) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += red1[w][lane];
+    }
+    const uint32_t inc = wave_incl_scan_dpp(tot);                 // lanes >= NSB add 0
+    const uint64_t reach = __ballot(lane < NSB && inc >= (uint32_t)keff);
+    const int Ts = reach ? (int)__builtin_ctzll(reach) : NSB;
+    const uint32_t below = Ts == 0 ? 0u : (uint32_t)__shfl((int)inc, Ts - 1, 64);
+    // level 2: T's superbin, and the sums before every group
+    uint32_t a[K];
+#pragma unroll
+    for (int v = 0; v < K; ++v) a[v] = 0u;
+    for (int c0 = 0; c0 < S; c0 += NT) {
+      const int c = c0 + tid;
+      uint32_t sbv[NSB], bb[8];
+      if (c0 == 0) {
+#pragma unroll
+        for (int i = 0; i < NSB; ++i) sbv[i] = sb0[i];
+      } else {
+        load_u32x<NSB>(row(c) + BINS, sbv);
+      }
+      if (Ts < NSB) {
+        load_u32x<8>(row(c) + 8 * Ts, bb);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bb[j] = 0u;
+      }
+      const bool ok = c < S;
+      uint32_t sbelow = 0;
+#pragma unroll
+      for (int i = 0; i < NSB; ++i) sbelow += i < Ts ? sbv[i] : 0u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[j] += ok ? bb[j] : 0u;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const bool m = ok && c < gs[g];
+        a[8 + 9 * g] += m ? sbelow : 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[9 + 9 * g + j] += m ? bb[j] : 0u;
+      }
+    }
+    const uint32_t r2 = wave_transpose_sum<K>(a);
+    if (lane < K) red2[wave][bitrev_k<K>(lane)] = r2;
+    __syncthreads();
+    uint32_t t2 = 0;
+    if (lane < NV) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) t2 += red2[w][lane];
+    }
+    // inclusive prefix over the NV values: bins of Ts in lanes 0..7, then per group its
+    // below-superbin sum and its 8 bins
+    const uint32_t p2 = wave_incl_scan_dpp(t2);
+    auto pre = [&](int l) { return l < 0 ? 0u : (uint32_t)__shfl((int)p2, l, 64); };
+    int b = 0;
+    if (Ts < NSB) {
+      const uint64_t reach2 = __ballot(lane < 8 && p2 + below >= (uint32_t)keff);
+      b = (int)__builtin_ctzll(reach2);        // the superbin holds the k_eff-th distance
+      T = 8 * Ts + b;
+      quota = keff - (int)(below + pre(b - 1));
+    } else {
+      T = BINS;
+      quota = keff - (int)below;
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int a0 = 8 + 9 * g;                // the group's below-superbin sum
+      if (Ts < NSB) {
+        lt_before[g] = (int)(pre(a0 + b) - pre(a0 - 1));
+        eq_before[g] = (int)(pre(a0 + 1 + b) - pre(a0 + b));
+      } else {
+        lt_before[g] = (int)(pre(a0) - pre(a0 - 1));   // every histogrammed distance is below T
+        eq_before[g] = gs[g] * CH - lt_before[g];      // chunks before a group are whole
+      }
+    }
+  }
+  T_out = T;
+  quota_out = quota;
+}
+
 // Words of chunk histograms a workgroup can hold in LDS (the selection list's space,
 // which is unused while the threshold is derived).
 constexpr int kHistLdsWords = 4096;
@@ -409,99 +591,6 @@ __device__ __forceinline__ void head_threshold_lds(const uint32_t *hl, int S, in
   }
   T_out = T;
   quota_out = quota;
-}
-
-// Writes the selected tokens of nch consecutive chunks (nch uniform, at most MAXC) into
-// list[position - first], where first is the head-list position of the first chunk's
-// first selected token.  The chunks' distance stashes are in LDS (sw[chunk][word][thread]
-// as written by the scan), their counts in smt[chunk]; chunk i starts at token
-// tok0 + i*CH.  Called by all threads of the workgroup; ends with the list complete.
-//
-// Thread t takes the LPT consecutive tokens LPT*t .. LPT*t + LPT-1 of every chunk, so
-// tokens ascend with (chunk, thread, bit).  It reads their distances from the stash
-// (they were stashed by LPT different scan threads), and keeps two bit masks per chunk:
-// tokens below the threshold and tokens at it.  One block-wide exclusive scan of the
-// packed per-thread counts (below | at << 16) gives every thread the number of tokens
-// below / at the threshold before its own in the head; a token below the threshold goes
-// to position (below before) + min(at before, quota), a tie with (at before) < quota to
-// (below before) + (at before).  Each thread then visits only its set mask bits.
-template <int LPT, int MAXC>
-__device__ __forceinline__ void emit_chunks_lanes(const uint32_t (*sw)[LPT / 4][kScanThreads],
-                                                  const int4 *smt, int nch, int T, int quota,
-                                                  int64_t tok0, int first, int32_t *list) {
-  constexpr int NW = kScanThreads / 64;
-  constexpr int CH = kScanThreads * LPT;
-  constexpr int TPR = 64 / LPT;                // threads per 64-token row of a wavefront
-  __shared__ uint32_t wtot[NW][MAXC];
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  // Scan thread of this thread's first token, and the item (byte) that holds it.
-  const int s0 = (t & ~63) + LPT * (t % TPR);
-  const int item = (t / TPR) % LPT;
-  const int sh = 8 * (item & 3);
-  // All MAXC chunks of sw are read (unused ones hold a copy of a used chunk) so that the
-  // reads issue together; the masks of unused chunks are cleared.
-  uint4 wr[MAXC][LPT / 4];
-#pragma unroll
-  for (int i = 0; i < MAXC; ++i)
-#pragma unroll
-    for (int q4 = 0; q4 < LPT / 4; ++q4)
-      wr[i][q4] = *reinterpret_cast<const uint4 *>(&sw[i][item >> 2][s0 + 4 * q4]);
-  uint32_t masks[MAXC], cnt[MAXC];
-#pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
-    uint32_t mlt = 0, meq = 0;
-#pragma unroll
-    for (int q4 = 0; q4 < LPT / 4; ++q4) {
-      const uint32_t wv[4] = {wr[i][q4].x, wr[i][q4].y, wr[i][q4].z, wr[i][q4].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = (int)((wv[e] >> sh) & 0xFFu);
-        mlt |= (d < T ? 1u : 0u) << (4 * q4 + e);
-        meq |= (d == T ? 1u : 0u) << (4 * q4 + e);
-      }
-    }
-    const uint32_t live = i < nch ? 0xFFFFFFFFu : 0u;
-    mlt &= live;
-    meq &= live;
-    masks[i] = mlt | (meq << 16);
-    cnt[i] = (uint32_t)__popc(mlt) | ((uint32_t)__popc(meq) << 16);
-  }
-  // Block-wide exclusive scan of the packed counts (each half stays below 2^16).
-  uint32_t inc[MAXC];
-#pragma unroll
-  for (int i = 0; i < MAXC; ++i) inc[i] = wave_incl_scan_dpp(cnt[i]);
-  if (lane == 63) {
-#pragma unroll
-    for (int i = 0; i < MAXC; ++i) wtot[wave][i] = inc[i];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
-    if (i >= nch) break;
-    uint32_t before = inc[i] - cnt[i];
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-      if (w < wave) before += wtot[w][i];
-    const int4 mt = smt[i];
-    const int lt0 = mt.x + (int)(before & 0xFFFFu);
-    const int eq0 = mt.y + (int)(before >> 16);
-    const uint32_t mlt = masks[i] & 0xFFFFu, meq = masks[i] >> 16;
-    uint32_t all = mlt | meq;
-    const int32_t tokb = (int32_t)(tok0 + (int64_t)i * CH) + LPT * t;
-    while (all) {
-      const int j = __builtin_ctz(all);
-      all &= all - 1;
-      const uint32_t below = (1u << j) - 1u;
-      const int ltb = lt0 + __popc(mlt & below);
-      const int eqb = eq0 + __popc(meq & below);
-      int pos = -1;
-      if ((mlt >> j) & 1u) pos = ltb + min(eqb, quota);
-      else if (eqb < quota) pos = ltb + eqb;
-      if (pos >= 0) list[pos - first] = tokb + j;
-    }
-  }
-  __syncthreads();
 }
 
 }  // namespace hk
