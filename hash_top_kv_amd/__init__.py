@@ -66,6 +66,8 @@ _SIGNATURES = {
                               _P, _P, _P, _P, _P, _SZ, _P]),
     "hk_retrieve_attend": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I64, _I, _I,
                                 _I, _F, _P, _P, _P, _P, _P, _SZ, _P]),
+    "hk_retrieve_attend_noalloc": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I64,
+                                        _I, _I, _I, _F, _P, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -362,6 +364,42 @@ def retrieve_attend(codes, qcodes, bits, q, k, v, n_ctx, n_sink, n_local, topk, 
                                     B, Hq, Hkv, d, cap, n_ctx, n_sink, n_local, topk, float(scale),
                                     _ptr(idx), _ptr(count), _ptr(o), _ptr(lse), _ptr(ws),
                                     ws.numel(), _stream()), "hk_retrieve_attend")
+    return o, lse, idx, count
+
+
+def retrieve_attend_noalloc(codes, qcodes, bits, q, k, v, n_ctx, n_sink, n_local, topk,
+                            scale=None, idx=None, count=None, o=None, lse=None):
+    """hk_retrieve_attend_noalloc: hk_retrieve_attend with the library's own workspace (a
+    fixed array on each GPU), for callers that cannot allocate.  Returns (o, lse, idx,
+    count); the outputs are allocated here only when not given."""
+    _need(codes, "codes", dtype=torch.int32)
+    B, Hkv, cap, W = codes.shape
+    _need(qcodes, "qcodes", dtype=torch.int32, shape=(B, Hkv, W))
+    dt = _dtype_code(q)
+    _need(q, "q")
+    _need(k, "k", dtype=q.dtype)
+    _need(v, "v", dtype=q.dtype, shape=k.shape)
+    Hq, d = q.shape[1], q.shape[2]
+    if tuple(k.shape[:3]) != (B, Hkv, cap):
+        raise ValueError("k must be [B, Hkv, cap, d] like the codes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if idx is None:
+        idx = torch.empty((B, Hkv, max(topk, 1)), dtype=torch.int32, device=codes.device)
+    if count is None:
+        count = torch.empty((B, Hkv), dtype=torch.int32, device=codes.device)
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(idx, "idx", dtype=torch.int32)
+    _need(count, "count", dtype=torch.int32, shape=(B, Hkv))
+    _need(o, "o", dtype=torch.float32, shape=(B, Hq, d))
+    _need(lse, "lse", dtype=torch.float32, shape=(B, Hq))
+    _check(lib().hk_retrieve_attend_noalloc(
+        _ptr(codes), _ptr(qcodes), bits, _ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, d, cap, n_ctx,
+        n_sink, n_local, topk, float(scale), _ptr(idx), _ptr(count), _ptr(o), _ptr(lse),
+        _stream()), "hk_retrieve_attend_noalloc")
     return o, lse, idx, count
 
 

@@ -1,6 +1,8 @@
 // The C ABI of libhk: host-side argument checks, workspace sizing and dispatch.
 // Every entry point validates on the host before enqueueing anything, launches only on
 // the caller's stream, allocates nothing and keeps no state between calls.
+#include <mutex>
+
 #include "hk_internal.h"
 
 using namespace hk;
@@ -43,6 +45,31 @@ hk_status check_retrieve(int bits, int B, int Hkv, int64_t cap, int64_t n_ctx, i
   if (n_ctx > cap) return HK_ERR_INVALID_ARGUMENT;
   if (n_ctx > INT32_MAX) return HK_ERR_UNSUPPORTED;
   if ((int64_t)B * Hkv > 65535) return HK_ERR_UNSUPPORTED;
+  return HK_OK;
+}
+
+// Workspace of hk_retrieve_attend_noalloc: a file-scope array that each GPU holds for the
+// life of the process.  Host code never names it directly: its device address on each
+// device comes from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device (looked up on the first call made
+// with that device current, then kept).
+hk_status static_scratch(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return HK_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return HK_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HK_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return HK_OK;
 }
 
@@ -164,6 +191,29 @@ hk_status hk_retrieve_attend(const uint32_t *codes, const uint32_t *qcodes, int 
     e = launch_fused_attend(p, q, kc, vc, dtype, B, Hq, Hkv, cap, scale, topk, idx, count, o, lse,
                             ws, st);
   return from_hip(e);
+}
+
+hk_status hk_retrieve_attend_noalloc(const uint32_t *codes, const uint32_t *qcodes, int bits,
+                                     const void *q, const void *kc, const void *vc, int dtype,
+                                     int B, int Hq, int Hkv, int d, int64_t cap, int64_t n_ctx,
+                                     int n_sink, int n_local, int topk, float scale,
+                                     int32_t *idx, int32_t *count, float *o, float *lse,
+                                     void *stream) {
+  hk_status s = check_retrieve(bits, B, Hkv, cap, n_ctx, n_sink, n_local, topk);
+  if (s != HK_OK) return s;
+  if (dtype != HK_F32 && dtype != HK_BF16) return HK_ERR_UNSUPPORTED;
+  if (d != kHeadDim) return HK_ERR_UNSUPPORTED;
+  if (Hkv <= 0 || Hq < Hkv || Hq % Hkv != 0) return HK_ERR_INVALID_ARGUMENT;
+  if (Hq / Hkv > kMaxGroup) return HK_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq == 0) return HK_OK;
+  const FusedPlan p = plan_fused(bits, B, Hq, Hkv, n_ctx, n_sink, n_local, topk);
+  if (p.total > kStaticScratchBytes) return HK_ERR_WORKSPACE_TOO_SMALL;
+  void *ws = nullptr;
+  s = static_scratch(&ws);
+  if (s != HK_OK) return s;
+  return hk_retrieve_attend(codes, qcodes, bits, q, kc, vc, dtype, B, Hq, Hkv, d, cap, n_ctx,
+                            n_sink, n_local, topk, scale, idx, count, o, lse, ws, p.total,
+                            stream);
 }
 
 hk_status hk_select_attend(int bits, const void *q, const void *kc, const void *vc, int dtype,

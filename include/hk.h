@@ -164,6 +164,23 @@ hk_status hk_retrieve_attend(const uint32_t *codes, const uint32_t *qcodes, int 
                              int n_local, int topk, float scale, int32_t *idx, int32_t *count,
                              float *o, float *lse, void *ws, size_t ws_bytes, void *stream);
 
+/* hk_retrieve_attend without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops, harnesses that forbid hipMalloc).
+ * The workspace is a 64 MiB array that the library holds on each GPU it runs on until the
+ * process ends (enough for 16 sequences x 128K tokens x 8 KV heads); the call allocates
+ * nothing and frees nothing.  Arguments, results and errors are those of
+ * hk_retrieve_attend; a problem whose workspace, hk_retrieve_attend_workspace(...), exceeds
+ * 64 MiB returns HK_ERR_WORKSPACE_TOO_SMALL and enqueues nothing.  All calls on one GPU
+ * share the array: calls that overlap on one GPU (on different streams, or from different
+ * threads without ordering) race and give undefined results.  The array's contents on
+ * entry do not matter. */
+hk_status hk_retrieve_attend_noalloc(const uint32_t *codes, const uint32_t *qcodes, int bits,
+                                     const void *q, const void *kc, const void *vc, int dtype,
+                                     int B, int Hq, int Hkv, int d, int64_t cap, int64_t n_ctx,
+                                     int n_sink, int n_local, int topk, float scale,
+                                     int32_t *idx, int32_t *count, float *o, float *lse,
+                                     void *stream);
+
 /* The part of hk_retrieve_attend that follows the Hamming scan: called after
  * hk_hamming_scan(codes, qcodes, bits, B, Hkv, cap, n_ctx, n_sink, n_local, topk, ws, ...)
  * on the same stream and workspace (of hk_retrieve_attend_workspace(...) bytes), it

@@ -222,3 +222,22 @@ def test_workspace_sizes_grow_with_the_problem(hk):
     assert hk.retrieve_topk_workspace(128, 1, 8, 100000, 4, 64, 100) >= 8 * 99932   # a byte per candidate
     assert hk.sparse_decode_workspace(1, 1, 1, 0) == 0 or hk.sparse_decode_workspace(1, 1, 1, 0) >= 0
     assert hk.sparse_decode_workspace(16, 32, 8, 2622) >= hk.sparse_decode_workspace(16, 32, 8, 100)
+
+
+def test_noalloc_rejects_problems_beyond_its_array(hk):
+    """hk_retrieve_attend_noalloc checks on the host that the fused step's workspace fits
+    the library's 64 MiB array; a larger problem returns WORKSPACE_TOO_SMALL before any HIP
+    call (none is possible here)."""
+    L = hk.lib()
+    d = ctypes.c_void_p(0x1000)
+    f = ctypes.c_float(0.1)
+    big = hk.retrieve_attend_workspace(128, 64, 8, 8, 1 << 20, 0, 0, 1024)
+    assert big > (64 << 20)
+    assert L.hk_retrieve_attend_noalloc(d, d, 128, d, d, d, hk.HK_BF16, 64, 8, 8, 128, 1 << 20,
+                                        1 << 20, 0, 0, 1024, f, d, d, d, d, None) \
+        == hk.HK_ERR_WORKSPACE_TOO_SMALL
+    # argument errors come first, as for hk_retrieve_attend
+    assert L.hk_retrieve_attend_noalloc(d, d, 96, d, d, d, hk.HK_BF16, 1, 8, 8, 128, 100, 100, 0, 0,
+                                        10, f, d, d, d, d, None) == hk.HK_ERR_UNSUPPORTED
+    assert L.hk_retrieve_attend_noalloc(d, d, 128, d, d, d, hk.HK_BF16, 1, 8, 8, 128, 100, 101, 0,
+                                        0, 10, f, d, d, d, d, None) == hk.HK_ERR_INVALID_ARGUMENT
