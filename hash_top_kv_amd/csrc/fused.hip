@@ -18,6 +18,14 @@
 namespace hk {
 namespace {
 
+// An argument used where the attention needs it: the empty asm keeps the compiler from
+// hoisting its first use (and so the wait for its scalar load) into the kernel's entry.
+template <class T>
+__device__ __forceinline__ T at_use(T v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
 // grid (Sc + Sw, B*Hkv), after the Hamming scan.  Block c < Sc covers chunk group c (and
 // c + Sc when REPS = 2) of the head, a group being chunks [g*CPB, (g+1)*CPB); blocks
 // c >= Sc cover window slice c - Sc.  Block c writes the normalised partial of part c.
@@ -31,14 +39,17 @@ constexpr int kMaxCpb = 8;                 // chunks per workgroup, bounded by r
 // compaction, first gather, combine) over more rows.
 constexpr int64_t kResidentBlocks = 768;
 
+// The parameters that the first memory requests need come first (16 dwords, preloaded
+// into SGPRs at launch), so the distance bytes and histograms are requested without
+// waiting for a scalar load of the arguments.
 template <int LPT, bool BF16, int G, int MAXC, int REPS>
 __device__ __forceinline__ void emit_attend_body(
-    const uint8_t *__restrict__ stash, const uint32_t *__restrict__ hist, int bins, int64_t C,
-    int keff, int32_t *__restrict__ count, int S, int CPB, int Sc, int64_t lo, int k,
-    int32_t *__restrict__ idx, const void *__restrict__ q, const void *__restrict__ kc,
-    const void *__restrict__ vc, int Hq, int Hkv, int64_t cap, float scale_log2,
-    int win_sinks, int64_t win_local0, int n_win, int win_rows, float *__restrict__ part_o,
-    float *__restrict__ part_lse, int64_t rows, const int32_t *__restrict__ ctx_len,
+    const uint8_t *__restrict__ stash, const uint32_t *__restrict__ hist,
+    const int32_t *__restrict__ ctx_len, int keff, int bins, int S, int CPB, int Sc, int Hkv,
+    int64_t C, int64_t lo, int32_t *__restrict__ count, int k, int32_t *__restrict__ idx,
+    const void *__restrict__ q, const void *__restrict__ kc, const void *__restrict__ vc,
+    int Hq, int64_t cap, float scale_log2, int win_sinks, int64_t win_local0, int n_win,
+    int win_rows, float *__restrict__ part_o, float *__restrict__ part_lse, int64_t rows,
     int64_t n_local, int64_t max_ctx) {
   constexpr int CH = kScanThreads * LPT;
   static_assert(kHistLdsWords <= kListMax, "the chunk histograms are staged in the list");
@@ -48,20 +59,17 @@ __device__ __forceinline__ void emit_attend_body(
   const int b = bh / Hkv;
   const int hkv = bh - b * Hkv;
   const int t = threadIdx.x;
-  const int64_t row0 = (int64_t)b * Hq + (int64_t)hkv * G;
-  const size_t head_row0 = (size_t)bh * (size_t)cap;
+  // Query rows and the head's K/V rows; these use arguments past the preloaded ones and
+  // are computed where the attention needs them.
+  auto row0 = [&]() { return (int64_t)b * at_use(Hq) + (int64_t)hkv * G; };
+  auto head_row0 = [&]() { return (size_t)bh * (size_t)at_use(cap); };
   // Sequences of their own lengths: the head's candidates, chunks, budget and window
   // follow its n_b; S stays the launch's chunk stride (sized for the longest).
   int Sb = S;
   if (ctx_len) {
-    int64_t n = ctx_len[b];
-    n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
     C = head_candidates(ctx_len, b, max_ctx, lo, n_local);
     Sb = (int)((C + CH - 1) / CH);
     keff = (int)(k < C ? k : C);
-    win_sinks = (int)(lo < n ? lo : n);
-    win_local0 = (n - n_local) > lo ? (n - n_local) : lo;
-    n_win = win_sinks + (int)(n > win_local0 ? n - win_local0 : 0);
   }
 
   // The query fragment is loaded after the chunks are compacted: its load then issues
@@ -70,10 +78,10 @@ __device__ __forceinline__ void emit_attend_body(
   bool ga_ready = false;
   auto attend_list = [&](int len) {
     if (!ga_ready) {
-      ga.init(q, row0, scale_log2);
+      ga.init(at_use(q), row0(), scale_log2);
       ga_ready = true;
     }
-    ga.run_block(kc, vc, head_row0, len, [&](int r) { return sel[r]; });
+    ga.run_block(at_use(kc), at_use(vc), head_row0(), len, [&](int r) { return sel[r]; });
   };
   if (c < Sc) {
     // Chunk workgroup c covers chunk groups c and, when REPS = 2, c + Sc of its head, one
@@ -86,7 +94,6 @@ __device__ __forceinline__ void emit_attend_body(
     // chunks [g0(r), g1(r)) of group r; uniform over the workgroup
     auto g0 = [&](int r) { return (c + r * Sc) * cpb; };
     auto g1 = [&](int r) { return min(Sb, g0(r) + cpb); };
-    int32_t *out = idx + (int64_t)bh * k;
     // A group's candidates are one run of the head's distance bytes (token order); thread
     // t holds tokens [t*TPT, (t+1)*TPT) of the run.  The first group's bytes are requested
     // before the threshold is derived, and arrive while it is.
@@ -173,7 +180,8 @@ __device__ __forceinline__ void emit_attend_body(
       if (n0 > 0) {
         rs.emit(0, n0, [&](int pos, int off) { sel[pos] = (int32_t)(tok_t + off); });
         __syncthreads();
-        for (int rr = t; rr < n0; rr += kScanThreads) out[first + rr] = sel[rr];
+        int32_t *out = idx + (int64_t)bh * k + first;
+        for (int rr = t; rr < n0; rr += kScanThreads) out[rr] = sel[rr];
         attend_list(n0);
       }
       // More than the list holds (a budget of thousands of tokens per group): further
@@ -188,36 +196,44 @@ __device__ __forceinline__ void emit_attend_body(
         const int n = min(total - base, kListMax);
         rs2.emit(base, base + n, [&](int pos, int off) { sel[pos - base] = (int32_t)(tok_t + off); });
         __syncthreads();
-        for (int rr = t; rr < n; rr += kScanThreads) out[first + base + rr] = sel[rr];
+        int32_t *out = idx + (int64_t)bh * k + first + base;
+        for (int rr = t; rr < n; rr += kScanThreads) out[rr] = sel[rr];
         attend_list(n);
       }
       __syncthreads();                         // the list and scan_lds are reused
     }
-    if (!ga_ready) ga.init(q, row0, scale_log2);
+    if (!ga_ready) ga.init(at_use(q), row0(), scale_log2);
   } else {
-    ga.init(q, row0, scale_log2);
+    if (ctx_len) {                             // the sequence's own window
+      int64_t n = ctx_len[b];
+      n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
+      win_sinks = (int)(lo < n ? lo : n);
+      win_local0 = (n - n_local) > lo ? (n - n_local) : lo;
+      n_win = win_sinks + (int)(n > win_local0 ? n - win_local0 : 0);
+    }
+    ga.init(at_use(q), row0(), scale_log2);
     const int r0 = (c - Sc) * win_rows;
     const int r1 = min(n_win, r0 + win_rows);
-    ga.run_block(kc, vc, head_row0, r1 > r0 ? r1 - r0 : 0, [&](int rr) {
+    ga.run_block(at_use(kc), at_use(vc), head_row0(), r1 > r0 ? r1 - r0 : 0, [&](int rr) {
       const int r = r0 + rr;
       return r < win_sinks ? r : (int)(win_local0 + (r - win_sinks));
     });
   }
-  ga.combine_store(part_o + ((int64_t)c * rows + row0) * kHeadDim, part_lse + (int64_t)c * rows + row0);
+  ga.combine_store(part_o + ((int64_t)c * rows + row0()) * kHeadDim, part_lse + (int64_t)c * rows + row0());
 }
 
 #define HK_EMIT_ATTEND_PARAMS                                                                 \
-  const uint8_t *__restrict__ stash, const uint32_t *__restrict__ hist, int bins, int64_t C,  \
-      int keff, int32_t *__restrict__ count, int S, int CPB, int Sc, int64_t lo, int k,      \
-      int32_t *__restrict__ idx, const void *__restrict__ q, const void *__restrict__ kc,    \
-      const void *__restrict__ vc, int Hq, int Hkv, int64_t cap, float scale_log2,           \
-      int win_sinks, int64_t win_local0, int n_win, int win_rows, float *__restrict__ part_o, \
-      float *__restrict__ part_lse, int64_t rows, const int32_t *__restrict__ ctx_len,       \
+  const uint8_t *__restrict__ stash, const uint32_t *__restrict__ hist,                       \
+      const int32_t *__restrict__ ctx_len, int keff, int bins, int S, int CPB, int Sc, int Hkv, \
+      int64_t C, int64_t lo, int32_t *__restrict__ count, int k, int32_t *__restrict__ idx,   \
+      const void *__restrict__ q, const void *__restrict__ kc, const void *__restrict__ vc,   \
+      int Hq, int64_t cap, float scale_log2, int win_sinks, int64_t win_local0, int n_win,    \
+      int win_rows, float *__restrict__ part_o, float *__restrict__ part_lse, int64_t rows,   \
       int64_t n_local, int64_t max_ctx
 #define HK_EMIT_ATTEND_ARGS                                                                   \
-  stash, hist, bins, C, keff, count, S, CPB, Sc, lo, k, idx, q, kc, vc, Hq, Hkv, cap,         \
-      scale_log2, win_sinks, win_local0, n_win, win_rows, part_o, part_lse, rows, ctx_len,    \
-      n_local, max_ctx
+  stash, hist, ctx_len, keff, bins, S, CPB, Sc, Hkv, C, lo, count, k, idx, q, kc, vc, Hq, cap, \
+      scale_log2, win_sinks, win_local0, n_win, win_rows, part_o, part_lse, rows, n_local,    \
+      max_ctx
 
 // bf16 (matrix cores): held to 168 VGPRs, three workgroups per CU.  fp32 (VALU) keeps
 // the compiler's choice: its accumulators would spill under that limit.  MAXC (8, or 4
@@ -244,15 +260,15 @@ void fused_launch_c(const FusedPlan &p, const uint8_t *stash, const uint32_t *hi
                   float *pl, int64_t rows, const int32_t *ctx_len, hipStream_t st) {
   if constexpr (BF16)
     hipLaunchKernelGGL((emit_attend_bf16_kernel<LPT, G, MAXC, REPS>), dim3(p.parts, p.r.BH),
-                       dim3(kScanThreads), 0, st, stash, hist, p.r.BINS, p.r.C, p.r.keff, count,
-                       p.r.S, p.cpb, p.Sc, p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,
-                       p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows, ctx_len,
+                       dim3(kScanThreads), 0, st, stash, hist, ctx_len, p.r.keff, p.r.BINS, p.r.S,
+                       p.cpb, p.Sc, Hkv, p.r.C, p.r.lo, count, k, idx, q, kc, vc, Hq, cap,
+                       scale_log2, p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows,
                        p.n_local, p.max_ctx);
   else
     hipLaunchKernelGGL((emit_attend_f32_kernel<LPT, G, MAXC, REPS>), dim3(p.parts, p.r.BH),
-                       dim3(kScanThreads), 0, st, stash, hist, p.r.BINS, p.r.C, p.r.keff, count,
-                       p.r.S, p.cpb, p.Sc, p.r.lo, k, idx, q, kc, vc, Hq, Hkv, cap, scale_log2,
-                       p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows, ctx_len,
+                       dim3(kScanThreads), 0, st, stash, hist, ctx_len, p.r.keff, p.r.BINS, p.r.S,
+                       p.cpb, p.Sc, Hkv, p.r.C, p.r.lo, count, k, idx, q, kc, vc, Hq, cap,
+                       scale_log2, p.win_sinks, p.win_local0, p.n_win, p.win_rows, po, pl, rows,
                        p.n_local, p.max_ctx);
 }
 

@@ -35,11 +35,15 @@ namespace {
 // ordinary stores, with 4.2 MB (8 x 524288) 13.0 against 12.4 -- so the launch picks
 // non-temporal stores when the distance bytes exceed a quarter of the 32 MB of L2.
 constexpr int64_t kStashNtBytes = 8 << 20;
+// The parameters that the first memory requests need come first: the first 16 dwords of
+// the arguments are preloaded into SGPRs, so the code loads issue without waiting for a
+// scalar load of the arguments.
 template <int W, int LPT, bool NT_STASH>
 __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
-    const uint32_t *__restrict__ codes, const uint32_t *__restrict__ qcodes, int64_t cap,
-    int64_t lo, int64_t C, int S, uint8_t *__restrict__ stash, uint32_t *__restrict__ hist_out,
-    const int32_t *__restrict__ ctx_len, int Hkv, int64_t n_local, int64_t max_ctx) {
+    const uint32_t *__restrict__ codes, const uint32_t *__restrict__ qcodes,
+    const int32_t *__restrict__ ctx_len, int64_t cap, int64_t lo, int64_t C,
+    uint8_t *__restrict__ stash, int S, uint32_t *__restrict__ hist_out, int Hkv,
+    int64_t n_local, int64_t max_ctx) {
   constexpr int BINS = 32 * W;
   constexpr int NBP = BINS + 4;
   constexpr int CH = kScanThreads * LPT;
@@ -267,11 +271,11 @@ void scan_launch(const RetrievePlan &p, const uint32_t *codes, const uint32_t *q
                  int64_t n_local, int64_t max_ctx, hipStream_t st) {
   if ((int64_t)p.BH * p.S * p.ch > kStashNtBytes)
     hipLaunchKernelGGL((hamming_scan_kernel<W, LPT, true>), dim3(p.S, p.BH), dim3(kScanThreads),
-                       0, st, codes, qcodes, cap, p.lo, p.C, p.S, stash, hist, ctx_len, Hkv,
+                       0, st, codes, qcodes, ctx_len, cap, p.lo, p.C, stash, p.S, hist, Hkv,
                        n_local, max_ctx);
   else
     hipLaunchKernelGGL((hamming_scan_kernel<W, LPT, false>), dim3(p.S, p.BH), dim3(kScanThreads),
-                       0, st, codes, qcodes, cap, p.lo, p.C, p.S, stash, hist, ctx_len, Hkv,
+                       0, st, codes, qcodes, ctx_len, cap, p.lo, p.C, stash, p.S, hist, Hkv,
                        n_local, max_ctx);
 }
 
