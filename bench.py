@@ -161,11 +161,46 @@ def same_rows_gather(torch, hkp, ctx, sel_fn, n_lists=8, reps=20):
             best = (us, rpb)
     sel_us = graph_us(torch, [lambda i=i: sel_fn(i) for i in range(n_lists)], 2 * reps)
     nbytes = n * 512
+    rotated = nbytes * n_lists
     return ({"rows_256B": n, "bytes": nbytes, "us_per_launch": round(best[0], 3),
              "gbs": round(nbytes / best[0] / 1e3, 1), "rows_per_workgroup": best[1],
+             # the K/V rows of the rotated lists fit in the 256 MB last-level cache: the
+             # rate is then a cache-resident rate, not an HBM one
+             "rotated_bytes": rotated, "cache_resident": rotated <= (256 << 20),
              "how": f"hk_gather_probe: the K and V rows of {n_lists} steps' selections and "
                     "windows, HIP-graph replay, best of 256/512/1024/2048 rows per workgroup"},
             sel_us)
+
+
+def profile_tag(args, info) -> str:
+    """Workload tag of the committed profile summaries: w<n>, plus the hash for the
+    workload that runs two (w4_lsh64, w4_mlp128)."""
+    tag = f"w{args.workload}"
+    if args.workload == 4:
+        tag += "_" + info.get("hash", "").replace("-", "")
+    return tag
+
+
+def read_trace(tag: str, kernel: str):
+    """The committed rocprofv3 kernel-trace summary of this workload's step: the average
+    durations of `kernel` (over its back-to-back dispatches and over all of them), if the
+    kernel sources have not changed since it was taken (else None)."""
+    path = os.path.join(ROOT, "profiles", f"decode_step_{tag}_kernel_trace.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#") and "|" not in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != source_digest():
+        return None
+    try:
+        return {"summary": os.path.relpath(path, ROOT),
+                "back_to_back_avg_us": float(vals[f"{kernel}_back_to_back_avg_us"]),
+                "all_dispatches_avg_us": float(vals[f"{kernel}_all_avg_us"])}
+    except (KeyError, ValueError):
+        return None
 
 
 def read_traffic(name: str):
@@ -546,33 +581,105 @@ def time_exact(torch, hk, ctx, steps):
                                   "max": round(float(iou.max()), 4), "heads": int(iou.size)}}
 
 
-def cpu_baseline(args, ctx, synth):
-    """The CPU oracle on a bounded sample: whole decode steps of the same workload."""
+def _oracle_head_worker(job, barrier, results):
+    """One CPU worker: builds one (batch, KV head)'s inputs, waits for every worker to be
+    ready, then times the oracle's decode step of that head repeatedly for `seconds`: the
+    group's query hash, Hamming distances over every cached code, the stable-argsort
+    top-k, the widening of the selected and window rows from their stored form,
+    attention of the G query heads over both sets and the log-sum-exp merge.  Puts
+    (median seconds, repetitions) on `results`."""
     import oracle
-    cores, model = cpu_info()
-    if args.workload != 2:
-        return {"value": None, "unit": "us/step", "cores": cores, "kind": "oracle",
-                "sample": "not run for this workload"}
-    wl = ctx["wl"]
-    g = synth.make_given_codes(wl, replica=0)
-    kv = ctx["kv"]
-    q = oracle.widen(synth.make_q(wl, replica=0), wl.dtype)
-    scale = 1 / math.sqrt(128)
+    import synth
+    wid, hidx, sign, no_window, b, g, seconds = job
+    wl = synth.WORKLOADS[wid]
+    if no_window:
+        wl = synth.scaled(wl, n_sink=0, n_local=0)
+    G = wl.Hq // wl.Hkv
+    kv = synth.make_kv(wl, heads=[(b, g)])
+    Ks, Vs = kv["K"][b, g].copy(), kv["V"][b, g].copy()      # stored form
+    del kv
+    q = oracle.widen(synth.make_q(wl)[b, g * G:(g + 1) * G], wl.dtype)
+    qcode = hp = None
+    if sign or wl.hashes:
+        spec = synth.HashSpec("sign", 128) if sign else wl.hashes[hidx]
+        hp = oracle.prepare_hash(synth.make_hash(wl, spec, hidx))
+        codes = np.concatenate([oracle.encode(oracle.widen(Ks[r:r + 32768], wl.dtype), hp)[0]
+                                for r in range(0, wl.N, 32768)])   # the cache's codes
+    else:                                                           # codes given directly
+        gc = synth.make_given_codes(wl, heads=[(b, g)])
+        codes, qcode = gc["codes"][b, g].copy(), gc["qcodes"][b, g]
+    scale = 1.0 / math.sqrt(wl.d)
+    win = oracle.window_indices(wl.N, wl.n_sink, wl.n_local)
+
+    def step():
+        qc = qcode if hp is None else oracle.encode_query(q[None], hp, 1)[0][0, 0]
+        idx = oracle.select_topk(codes, qc, wl.N, wl.n_sink, wl.n_local, wl.k)
+        K1, V1 = oracle.widen(Ks[idx], wl.dtype), oracle.widen(Vs[idx], wl.dtype)
+        K2, V2 = oracle.widen(Ks[win], wl.dtype), oracle.widen(Vs[win], wl.dtype)
+        for h in range(G):
+            o1, l1 = oracle.attend(q[h], K1, V1, scale)
+            o2, l2 = oracle.attend(q[h], K2, V2, scale)
+            oracle.lse_merge(np.stack([o1, o2]), np.array([l1, l2]))
+
+    step()
+    barrier.wait()
     times = []
-    t_end = time.perf_counter() + args.cpu_seconds
+    t_end = time.perf_counter() + seconds
     while time.perf_counter() < t_end or not times:
         t0 = time.perf_counter()
-        for h in range(wl.Hkv):
-            idx = oracle.select_topk(g["codes"][0, h], g["qcodes"][0, h], wl.N, 0, 0, wl.k)
-            kr = oracle.widen(kv["K"][0, h][idx], wl.dtype)
-            vr = oracle.widen(kv["V"][0, h][idx], wl.dtype)
-            oracle.attend(q[0, h], kr, vr, scale)
+        step()
         times.append(time.perf_counter() - t0)
-    us = float(np.median(times)) * 1e6
-    return {"value": round(us, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
-            "sample": f"{len(times)} whole decode steps (8 heads x 524288 codes, top-1024, "
-                      f"attention over the selected rows), median; NumPy popcount and stable "
-                      f"argsort run on one thread; host has {cores} cores ({model})"}
+    results.put((float(np.median(times)), len(times)))
+
+
+def cpu_baseline_run(args):
+    """The CPU oracle on every host core (a process of its own, started with one BLAS
+    thread per worker, that never touches the GPU): P = min(cores, heads) workers each
+    time one (batch, KV head)'s oracle decode step, all at once; a whole step over all
+    B*Hkv heads on P cores takes ceil(B*Hkv / P) rounds of the median head time."""
+    import multiprocessing as mp
+    import synth
+    cores, model = cpu_info()
+    wl = synth.WORKLOADS[args.workload]
+    heads = [(b, g) for b in range(wl.B) for g in range(wl.Hkv)]
+    P = max(1, min(cores, len(heads)))
+    ctx = mp.get_context("fork")
+    barrier, results = ctx.Barrier(P), ctx.Queue()
+    procs = [ctx.Process(target=_oracle_head_worker,
+                         args=((args.workload, args.hash, args.sign, args.no_window, b, g,
+                                args.cpu_seconds), barrier, results))
+             for b, g in heads[:P]]
+    for p in procs:
+        p.start()
+    res = [results.get() for _ in procs]
+    for p in procs:
+        p.join()
+    per_head = float(np.median([r[0] for r in res]))
+    rounds = -(-len(heads) // P)
+    us = per_head * rounds * 1e6
+    return {"value": round(us, 1), "unit": "us/step", "cores": P, "kind": "oracle",
+            "sample": f"{P} of the {len(heads)} (batch, KV head) decode steps, one per core, "
+                      f"timed together for {args.cpu_seconds:g} s ({sum(r[1] for r in res)} "
+                      f"repetitions): median {per_head * 1e3:.2f} ms per head; a step is "
+                      f"{rounds} round(s) of {P} heads. NumPy float64, one BLAS thread per "
+                      f"process; host has {cores} usable cores ({model})"}
+
+
+def cpu_baseline(args):
+    """Runs cpu_baseline_run in a child process (this one has initialised the GPU)."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-only",
+           "--workload", str(args.workload), "--hash", str(args.hash),
+           "--cpu-seconds", str(args.cpu_seconds)]
+    if args.sign:
+        cmd.append("--sign")
+    if args.no_window:
+        cmd.append("--no-window")
+    r = subprocess.run(cmd, capture_output=True, text=True, env=env, timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError(f"CPU baseline failed:\n{r.stderr[-2000:]}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def main():
@@ -605,10 +712,16 @@ def main():
                     help="also time HashEvict's eviction step on the same cache (last)")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step through the separate calls instead of the fused one")
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="only time the CPU oracle on the workload (no GPU) and print its JSON")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes 10 times (calibrates "
                          "the HBM byte counters) and exit")
     args = ap.parse_args()
+
+    if args.cpu_baseline_only:
+        print(json.dumps(cpu_baseline_run(args)), flush=True)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (the step would "
@@ -769,10 +882,20 @@ def main():
     stream = None if args.no_kernel_timing else stream_read_rate(torch, hkp)
     if "gbs" in sc:
         a = sc["gbs"]
+        tag = profile_tag(args, info)
         roofline = {"kernel": "hamming_scan", "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4),
-                    "traffic": read_traffic(f"hamming_scan_w{args.workload}"),
+                    "traffic": read_traffic(f"hamming_scan_{tag}"),
                     "alg_bytes_per_launch": sc["alg_bytes"], "us_per_launch": sc["us_per_launch"]}
+        # The same kernel in the committed rocprofv3 trace of this command: under the
+        # profiler every dispatch starts from an idle GPU (the profiler leaves gaps
+        # between dispatches), so its duration includes the launch ramp that back-to-back
+        # launches overlap with the previous kernel's drain.
+        tr = read_trace(tag, "hamming_scan")
+        if tr:
+            for key in ("back_to_back_avg_us", "all_dispatches_avg_us"):
+                tr["frac_" + key[:-7]] = round(sc["alg_bytes"] / tr[key] / 1e3 / HBM_PEAK_GBS, 4)
+        roofline["trace"] = tr
         if stream:
             roofline["frac_of_measured_read"] = round(a / stream["gbs"], 4)
             same = same_size_read_rate(torch, hkp, sc["alg_bytes"])
@@ -796,7 +919,7 @@ def main():
     if args.evict and args.workload != 2:
         out["evict"] = time_evict(torch, hk, synth, ctx, min(args.steps, 200))
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(args, ctx, synth)
+        out["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(out), flush=True)
 
 

@@ -1,5 +1,7 @@
 """Parity at the five workloads' full sizes, in the launch configurations the
-benchmark uses, on sampled (batch, KV head) pairs the oracle computes one by one.
+benchmark uses: every (batch, KV head)'s selection against the oracle's top-k of the
+GPU's own codes, and the whole step on sampled (batch, KV head) pairs the oracle
+computes one by one.
 
 For each workload:
   * key codes: the whole cache is encoded on the GPU; sampled heads are compared with
@@ -95,6 +97,21 @@ def _check_head_step(gpu_idx, gpu_o, gpu_lse, qg, Kf, Vf, key_codes, qcode_ref, 
     return err_o, err_l
 
 
+def _check_all_heads(codes, qcodes, idx, count, wl, lengths=None):
+    """Every (batch, KV head) at full size: given the GPU's own key and query codes, the
+    GPU's selection (count, ascending indices, ties to the lower index) must equal the
+    oracle's top-k of those codes.  lengths: per-sequence context lengths, else wl.N."""
+    codes, qcodes = np_u32(codes), np_u32(qcodes)
+    idx, count = idx.cpu().numpy(), count.cpu().numpy()
+    for b in range(wl.B):
+        n = wl.N if lengths is None else lengths[b]
+        for g in range(wl.Hkv):
+            want = oracle.select_topk(codes[b, g, :n], qcodes[b, g], n, wl.n_sink, wl.n_local, wl.k)
+            assert count[b, g] == want.size, (b, g)
+            assert np.array_equal(idx[b, g, :want.size], want), (b, g)
+    say(f"  all {wl.B * wl.Hkv} (batch, KV head) selections equal the oracle's on the GPU's codes")
+
+
 def _encode_and_check(wl, spec, hidx, sample):
     d = _inputs(wl.wid)
     hnp = synth.make_hash(wl, spec, hidx)
@@ -126,6 +143,7 @@ def _run_workload(wid, hidx=0, spec=None, k=None):
     step = DecodeStep(d["K"], d["V"], codes, spec.bits, wl.N, wl.n_sink, wl.n_local, wl.k, wl.Hq, h)
     o, lse = step(d["Q"])
     torch.cuda.synchronize()
+    _check_all_heads(codes, step.qcodes, step.idx, step.count, wl)
     gq = np_u32(step.qcodes)
     qref, qy = oracle.encode_query(oracle.widen(d["q"], wl.dtype), hp, wl.Hkv)
     compare_codes(gq, qref, qy)
@@ -189,6 +207,7 @@ def test_workload3_per_sequence_lengths():
                             wl.n_local, wl.k, wl.Hq, h)
     o, lse = step(d["Q"])
     torch.cuda.synchronize()
+    _check_all_heads(codes, step.qcodes, step.idx, step.count, wl, lengths)
     qref, qy = oracle.encode_query(oracle.widen(d["q"], wl.dtype), hp, wl.Hkv)
     compare_codes(np_u32(step.qcodes), qref, qy)
     gidx, gcnt = step.idx.cpu().numpy(), step.count.cpu().numpy()
