@@ -473,7 +473,7 @@ def qhead_overlap(torch, hk, ctx):
 def time_prefill(torch, hk, ctx, steps):
     """MFMA key encode of the whole cache (prefill), bf16: flops per launch / duration."""
     wl, K, h, codes, spec = ctx["wl"], ctx["K"], ctx["h"], ctx["codes"], ctx["spec"]
-    for _ in range(2):
+    for _ in range(10):            # the clocks settle over the first milliseconds of work
         hk.encode_keys(h, K, codes)
     t = Timer(torch, steps)
     for _ in range(steps):
@@ -693,6 +693,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prefill", action="store_true", help="also time the key encode of the whole cache")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only time the key encode of the whole cache (workloads 0, 1, 3, 4)")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the step")
@@ -749,6 +751,14 @@ def main():
         return
     build = build_retrieval_case if args.workload == 2 else build_full_case
     parts, check, info, ctx = build(args, torch, hk, synth)
+    if args.prefill_only:
+        if args.workload == 2:
+            print("workload 2 has no key encode (its codes are given)", file=sys.stderr)
+            sys.exit(2)
+        pre = time_prefill(torch, hk, ctx, max(args.steps, 1))
+        print(json.dumps({"metric": "key encode (prefill) of the whole cache", "config": info,
+                          "prefill": pre}), flush=True)
+        return
     check()
 
     def step(i):

@@ -17,15 +17,16 @@
 //   pack    lane i (+32) holds 16 of the 32 bits of token i for each 32-bit output
 //           tile; the two halves are OR-ed across lanes i and i+32, and each lane of
 //           the pair stores half of the token's code.
-// The MLP is bound by the vector ALU (the GELU: 11 vector instructions and two
-// transcendentals per hidden unit), not by the matrix cores.
+// The GELU's vector instructions (eight per hidden unit) and the matrix-core products
+// take comparable time; two wavefronts per SIMD overlap one's GELU with the other's
+// products.
 // Weights are staged in LDS once per workgroup in fragment order (64 lanes x 16 bytes
 // per fragment), so every fragment read is one conflict-free ds_read_b128.
 // Query codes (B*Hkv rows) and fp32 keys use a plain VALU kernel, one row per
 // workgroup.
 //
-// The erf of GELU is the rational approximation of Abramowitz & Stegun 7.1.26
-// (absolute error below 1.5e-7): branch-free, one reciprocal and one exponential.
+// GELU's normal tail is one polynomial under one exponential (no reciprocal, no
+// branch), with absolute error below 4.6e-7.
 #include "hk_internal.h"
 
 namespace hk {
@@ -35,35 +36,28 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// GELU(a) = a Phi(a) = max(a, 0) - |a| Phi(-|a|), with Phi(-|a|) = erfc(|a| / sqrt 2) / 2
-// from the rational approximation of erf in Abramowitz & Stegun 7.1.26 (Hastings):
-// erfc(z) ~= t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z), for
-// z >= 0, absolute error at most 1.5e-7.  One reciprocal and one base-2 exponential;
-// exp(-a^2 / 2) / 2 = 2^(-a^2 log2(e) / 2 - 1).  For |a| > 13 the exponential underflows
-// to zero and GELU(a) is max(a, 0) to fp32 precision.
-// With x = |a| and k = p / sqrt 2, t = 1 / (1 + k x) gives x t = (1 - t) / k, so
-// x t P(t) = (1 - t) P'(t) with P' = P / k (coefficients divided by k once, here): one
-// fused multiply-add instead of two products.  1 - t is exact (t lies in (0, 1]); the
-// rounding of t then moves the result by at most about 2e-7.  max(a, 0) is an integer
-// max of the bits (a negative float, -0 included, is a negative integer): one operation
-// with no NaN canonicalisation (the inputs are finite).
-constexpr double kErfP = 0.3275911 * 0.70710678118654752;   // p / sqrt 2
+// GELU(a) = a Phi(a) = max(a, 0) - x Phi(-x) with x = |a|, and Phi(-x) = 2^R(x): R is a
+// degree-5 polynomial fitted to log2 Phi(-x) (a weighted minimax fit that bounds the
+// absolute error of x 2^R(x), not of R).  Evaluated in fp32 (Horner, then one base-2
+// exponential), |GELU - exact| <= 4.6e-7 above fp32 rounding of the result, for every
+// finite a.  R's leading coefficient is negative, so R falls without bound: from x ~ 12
+// on, 2^R is below 2^-140 and GELU(a) = max(a, 0) to fp32 precision, with no clamp; for
+// very large x the Horner sum reaches -inf and the exponential 0 (never NaN).  Five
+// fused multiply-adds, one exponential, one integer max (a negative float, -0 included,
+// is a negative integer) and one fused multiply-add: eight vector instructions, one of
+// them transcendental.  The fit is written out, with its check, in gelu_fit.py.
+constexpr float kGelu0 = -1.000037722e+00f, kGelu1 = -1.150787181e+00f,
+                kGelu2 = -4.599939130e-01f, kGelu3 = -5.182606418e-02f,
+                kGelu4 = 7.084052480e-03f, kGelu5 = -4.732408280e-04f;
 __device__ __forceinline__ float gelu(float a) {
-  constexpr float kP = (float)kErfP;
-  constexpr float kHalfLog2e = -0.72134752044448170f;       // -log2(e) / 2
-  constexpr float c1 = (float)(0.254829592 / kErfP), c2 = (float)(-0.284496736 / kErfP);
-  constexpr float c3 = (float)(1.421413741 / kErfP), c4 = (float)(-1.453152027 / kErfP);
-  constexpr float c5 = (float)(1.061405429 / kErfP);
   const float x = fabsf(a);
-  const float t = __builtin_amdgcn_rcpf(fmaf(kP, x, 1.0f));
-  float p = c5;
-  p = fmaf(p, t, c4);
-  p = fmaf(p, t, c3);
-  p = fmaf(p, t, c2);
-  p = fmaf(p, t, c1);
-  const float u = fmaf(-t, p, p);                           // x t P(t)
-  const float g = __builtin_amdgcn_exp2f(fmaf(x * kHalfLog2e, x, -1.0f));
-  return fmaf(-u, g, __int_as_float(max(__float_as_int(a), 0)));   // max(a, 0)
+  float r = fmaf(kGelu5, x, kGelu4);
+  r = fmaf(r, x, kGelu3);
+  r = fmaf(r, x, kGelu2);
+  r = fmaf(r, x, kGelu1);
+  r = fmaf(r, x, kGelu0);
+  const float g = __builtin_amdgcn_exp2f(r);
+  return fmaf(-x, g, __int_as_float(max(__float_as_int(a), 0)));   // max(a, 0)
 }
 
 // Round to the nearest bf16 (ties to even); finite inputs.
@@ -510,19 +504,29 @@ __global__ __launch_bounds__(128) void encode_query_sign_kernel(const void *__re
 }
 
 // ------------------------------------------------------------------ MFMA kernel
-template <bool MLP, int BITS> struct EncLayout {
+template <bool MLP, int BITS, bool BIAS = false> struct EncLayout {
   static constexpr int JT = BITS / 32;                // 32-bit output tiles
   static constexpr int F1 = MLP ? 8 * 8 : JT * 8;     // first-GEMM fragments
   static constexpr int F2 = MLP ? JT * 16 : 0;        // second-GEMM fragments
+  // LDS fragment order: per hidden (or bit) tile, its 8 first-GEMM k-steps, then (MLP)
+  // its 2 * JT second-GEMM fragments, so that one tile's reads share a base address
+  // and take constant offsets within the 16-bit offset field.
+  static constexpr int FB = MLP ? 8 + 2 * JT : 8;
   static constexpr int NB1 = MLP ? kHidden : 0;       // b1 floats
   static constexpr int NB2 = MLP ? BITS : 0;          // b2 floats
   // Wavefronts per workgroup.  The MLP weights fill most of LDS, so one workgroup holds
-  // a CU: 8 wavefronts (2 per SIMD) let one wavefront's GELU run beside another's
-  // matrix-core work (12 measured no faster).  The LSH projection is small; several
-  // workgroups share a CU.
-  static constexpr int WAVES = MLP ? 8 : 4;
+  // a CU.  Without biases, 12 wavefronts (3 per SIMD, at most 168 registers each) run
+  // the pipelined stages; with biases, 8 (2 per SIMD) run one hidden tile at a time.
+  // The LSH projection is small; several workgroups share a CU.
+  static constexpr int WAVES = MLP ? (BIAS ? 8 : 12) : 4;
   static constexpr int PER_CU = MLP ? 1 : 4;
 };
+
+// Vector instructions scheduled after each matrix-core product in the MLP's pipelined
+// stages (a stage holds 16 products and about 150 vector instructions).
+constexpr int kGeluGroup = 9;
+
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;   // an LDS-resident vector
 
 // Bit position, inside its 32-bit tile, of accumulator register r of lane group g.
 __device__ __forceinline__ constexpr int acc_row(int r, int g) {
@@ -534,10 +538,10 @@ __device__ __forceinline__ constexpr int acc_row(int r, int g) {
 // ks, and accumulator register r holds output row acc_row(r, g) of token i.
 // BIAS: the MLP has b1 or b2 (a null bias reads as zero).
 template <bool MLP, int BITS, bool BIAS>
-__global__ __launch_bounds__((EncLayout<MLP, BITS>::WAVES * 64)) void encode_keys_mfma_kernel(
+__global__ __launch_bounds__((EncLayout<MLP, BITS, BIAS>::WAVES * 64)) void encode_keys_mfma_kernel(
     HashPtrs hp, const uint16_t *__restrict__ K, int64_t nt, int64_t cap, int64_t t0,
     int64_t total_rows, int64_t n_tiles, uint32_t *__restrict__ codes) {
-  using L = EncLayout<MLP, BITS>;
+  using L = EncLayout<MLP, BITS, BIAS>;
   constexpr int JT = L::JT;
   constexpr int W = BITS / 32;
   constexpr int NWG = L::WAVES * 64;
@@ -556,18 +560,18 @@ __global__ __launch_bounds__((EncLayout<MLP, BITS>::WAVES * 64)) void encode_key
     const int fi = f >> 6, fl = f & 63, i = fl & 31, g = fl >> 5;
     const int tile = fi >> 3, ks = fi & 7;      // (hidden or bit tile, k-step)
     const uint16_t *src = A1 + (size_t)(32 * tile + i) * kHeadDim + 64 * g + 8 * ks;
-    frag[fi][fl] = *reinterpret_cast<const u32x4 *>(src);
+    frag[tile * L::FB + ks][fl] = *reinterpret_cast<const u32x4 *>(src);
   }
   static_assert(MLP || !BIAS, "LSH has no bias");
   if constexpr (MLP) {
     const uint16_t *A2 = static_cast<const uint16_t *>(hp.W2);
     for (int f = tid; f < L::F2 * 64; f += NWG) {
       const int fi = f >> 6, fl = f & 63, i = fl & 31, g = fl >> 5;
-      const int jt = fi >> 4, ks2 = fi & 15, ht = ks2 >> 1, half = ks2 & 1;
+      const int ks2 = fi / JT, jt = fi - ks2 * JT, ht = ks2 >> 1, half = ks2 & 1;
       const uint16_t *row = A2 + (size_t)(32 * jt + i) * kHidden + 32 * ht + 16 * half + 4 * g;
       const u32x2 lo = *reinterpret_cast<const u32x2 *>(row);
       const u32x2 hi = *reinterpret_cast<const u32x2 *>(row + 8);
-      frag[L::F1 + fi][fl] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      frag[ht * L::FB + 8 + half * JT + jt][fl] = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
     if constexpr (BIAS) {
       for (int j = tid; j < L::NB1 + L::NB2; j += NWG) {
@@ -579,41 +583,80 @@ __global__ __launch_bounds__((EncLayout<MLP, BITS>::WAVES * 64)) void encode_key
   }
   __syncthreads();
 
-  for (int64_t tile = (int64_t)blockIdx.x * L::WAVES + wave; tile < n_tiles;
-       tile += (int64_t)gridDim.x * L::WAVES) {
-    const int64_t row = tile * 32 + li;
+  // Lane li's row of the current tile, its position in the cache (head bh, token t0 +
+  // off) and its cache row mem.  Tiles advance by a fixed stride of rows, so the
+  // division by nt happens once; each step adds the stride's quotient and remainder.
+  const int64_t tstride = (int64_t)gridDim.x * L::WAVES;
+  const int64_t step = tstride * 32;
+  const int64_t q = step / nt, rem = step - q * nt;
+  const int64_t dmem = q * cap + rem;
+  int64_t tile = (int64_t)blockIdx.x * L::WAVES + wave;
+  int64_t row = tile * 32 + li;
+  int64_t off = row % nt;
+  int64_t mem = (row / nt) * cap + t0 + off;
+  // Rows past the end read row 0 instead (a token column only feeds its own outputs,
+  // and those are not stored), so every load is unconditional.
+  auto load = [&](bf16x8 (&x)[8]) {
+    const uint16_t *src = K + (size_t)(row < total_rows ? mem : 0) * kHeadDim + 64 * lg;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      x[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(src + 8 * ks));
+  };
+  // The LSH projection is bound by the key reads: each wavefront requests its next
+  // tile's keys before working on the current one.  (The MLP's registers are taken by
+  // its pipelined stages, and its products hide the reads anyway.)
+  constexpr bool PREFETCH = !MLP;
+  bf16x8 xn[8];
+  if (PREFETCH && tile < n_tiles) load(xn);
+  for (; tile < n_tiles; tile += tstride) {
     const bool ok = row < total_rows;
-    const int64_t bh = ok ? row / nt : 0;
-    const int64_t mem = ok ? bh * cap + t0 + (row - bh * nt) : 0;
     bf16x8 xf[8];
-    {
-      const uint16_t *src = K + (size_t)mem * kHeadDim + 64 * lg;
+    if constexpr (PREFETCH) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 v = ok ? *reinterpret_cast<const u32x4 *>(src + 8 * ks) : u32x4{0u, 0u, 0u, 0u};
-        xf[ks] = __builtin_bit_cast(bf16x8, v);
-      }
+      for (int ks = 0; ks < 8; ++ks) xf[ks] = xn[ks];
+    } else {
+      load(xf);
     }
+    const int64_t mem_st = mem;
+    row += step;
+    off += rem;
+    mem += dmem;
+    if (off >= nt) {
+      off -= nt;
+      mem += cap - nt;
+    }
+    if (PREFETCH && tile + tstride < n_tiles) load(xn);
 
-    f32x16 yacc[JT];
-#pragma unroll
-    for (int j = 0; j < JT; ++j) yacc[j] = f32x16{};
+    f32x16 yacc[JT];        // the first product into each starts from a zero accumulator
 
     if constexpr (MLP) {
       // H^T tile ht (hidden units 32 ht .. 32 ht + 31) of the first GEMM.
+      // Hidden tile ht's fragments are read through a base pointer the compiler cannot
+      // re-derive, so every read is that base plus a constant offset (left to itself,
+      // it shares one running base between tiles and needs an add per read for the
+      // offsets that fall outside the unsigned offset field).
+      auto block = [&](int ht) {
+        lds_u32x4 *b = (lds_u32x4 *)(&frag[ht * L::FB][lane]);
+        asm volatile("" : "+v"(b));
+        return b;
+      };
       auto gemm1 = [&](int ht) {
+        lds_u32x4 *b = block(ht);
         f32x16 h = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
-          h = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, frag[ht * 8 + ks][lane]),
-                                                      xf[ks], h, 0, 0, 0);
+          h = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b[64 * ks]), xf[ks], h,
+                                                      0, 0, 0);
         return h;
       };
-      // Bias, GELU and bf16 rounding of H^T tile ht, then its share of the second GEMM.
-      // Register r of lane group g is hidden unit 32 ht + acc_row(r, g); k-step half h
-      // of the second GEMM takes r = 8h .. 8h+7.
-      auto gelu_gemm2 = [&](int ht, const f32x16 &hacc) {
-        bf16x8 hb[2];
+      // Bias, GELU and bf16 rounding of H^T tile ht: the B operand of its two k-steps of
+      // the second GEMM.  Register r of lane group g is hidden unit 32 ht + acc_row(r, g);
+      // k-step half h of the second GEMM takes r = 8h .. 8h+7.
+      struct Hid {
+        bf16x8 h[2];
+      };
+      auto gelu_pack = [&](int ht, const f32x16 &hacc) {
+        Hid out;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           u32x4 w;
@@ -628,28 +671,74 @@ __global__ __launch_bounds__((EncLayout<MLP, BITS>::WAVES * 64)) void encode_key
             const bf16x2 pr = {(__bf16)gelu(a0), (__bf16)gelu(a1)};
             w[e] = __builtin_bit_cast(uint32_t, pr);
           }
-          hb[half] = __builtin_bit_cast(bf16x8, w);
+          out.h[half] = __builtin_bit_cast(bf16x8, w);
         }
+        return out;
+      };
+      // Hidden tile ht's share of the second GEMM (the first share starts from zero).
+      auto gemm2 = [&](int ht, const Hid &hb, bool first) {
+        lds_u32x4 *b = block(ht);
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int j = 0; j < JT; ++j)
             yacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, frag[L::F1 + j * 16 + 2 * ht + half][lane]), hb[half],
-                yacc[j], 0, 0, 0);
+                __builtin_bit_cast(bf16x8, b[64 * (8 + half * JT + j)]), hb.h[half],
+                first && half == 0 ? f32x16{} : yacc[j], 0, 0, 0);
       };
-      // Two wavefronts per SIMD overlap one's GELU with the other's products (issuing
-      // the next tile's first GEMM before this tile's GELU, or interleaving them by
-      // scheduling barriers, measured no faster).
+      if constexpr (!BIAS) {
+        // Software pipeline over the eight hidden tiles: while the vector ALU computes
+        // tile ht's GELU, the matrix cores run the second GEMM of tile ht-1 and the first
+        // GEMM of tile ht+1 (neither depends on that GELU).  Each such stage is one
+        // scheduling region whose 16 products are interleaved with the GELU's
+        // instructions, so that one wavefront keeps both units busy; the other
+        // wavefronts of the SIMD fill the gaps.
+        auto interleave = [] {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one matrix-core product
+            __builtin_amdgcn_sched_group_barrier(0x002, kGeluGroup, 0);   // vector ALU
+          }
+        };
+        f32x16 ha = gemm1(0);
+        f32x16 hb = gemm1(1);
+        Hid pa = gelu_pack(0, ha);
+        gemm2(0, pa, true);
+        ha = gemm1(2);
+        Hid pb = gelu_pack(1, hb);
+        interleave();
 #pragma unroll 1
-      for (int ht = 0; ht < 8; ++ht) gelu_gemm2(ht, gemm1(ht));
+        for (int ht = 2; ht < 6; ht += 2) {
+          gemm2(ht - 1, pb, false);
+          hb = gemm1(ht + 1);
+          pa = gelu_pack(ht, ha);
+          interleave();
+          gemm2(ht, pa, false);
+          ha = gemm1(ht + 2);
+          pb = gelu_pack(ht + 1, hb);
+          interleave();
+        }
+        gemm2(5, pb, false);
+        hb = gemm1(7);
+        pa = gelu_pack(6, ha);
+        interleave();
+        gemm2(6, pa, false);
+        pb = gelu_pack(7, hb);
+        gemm2(7, pb, false);
+      } else {
+        // With biases: one hidden tile at a time (the bias reads need the registers).
+#pragma unroll
+        for (int j = 0; j < JT; ++j) yacc[j] = f32x16{};
+#pragma unroll 1
+        for (int ht = 0; ht < 8; ++ht) gemm2(ht, gelu_pack(ht, gemm1(ht)), false);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < JT; ++j)
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
           yacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, frag[j * 8 + ks][lane]),
-                                                            xf[ks], yacc[j], 0, 0, 0);
+                                                            xf[ks], ks == 0 ? f32x16{} : yacc[j], 0, 0, 0);
     }
 
     // Sign bits.  Lanes i and i+32 hold complementary halves of each word of token i;
@@ -670,7 +759,7 @@ __global__ __launch_bounds__((EncLayout<MLP, BITS>::WAVES * 64)) void encode_key
       words[j] = w | __shfl_xor(w, 32);
     }
     if (ok) {
-      uint32_t *dst = codes + (size_t)mem * W + (W / 2) * lg;
+      uint32_t *dst = codes + (size_t)mem_st * W + (W / 2) * lg;
       if constexpr (W == 4)
         *reinterpret_cast<u32x2 *>(dst) = lg ? u32x2{words[2], words[3]} : u32x2{words[0], words[1]};
       else
@@ -682,7 +771,7 @@ __global__ __launch_bounds__((EncLayout<MLP, BITS>::WAVES * 64)) void encode_key
 template <bool MLP, int BITS, bool BIAS>
 hipError_t mfma_launch(const HashPtrs &hp, const void *k, int64_t nt, int64_t cap, int64_t t0,
                        int64_t total, uint32_t *codes, hipStream_t st) {
-  using L = EncLayout<MLP, BITS>;
+  using L = EncLayout<MLP, BITS, BIAS>;
   const int64_t n_tiles = (total + 31) / 32;
   int64_t grid = (n_tiles + L::WAVES - 1) / L::WAVES;
   if (grid > 256 * L::PER_CU) grid = 256 * L::PER_CU;

@@ -125,7 +125,7 @@ __device__ __forceinline__ void emit_attend_body(
 #pragma unroll
         for (int i = 0; i < HV; ++i) {
           const int v = t + kScanThreads * i;
-          const int cc = v / qpr;
+          const int cc = bins == 128 ? v >> 5 : v >> 4;     // v / qpr
           hv[i] = cc < Sb ? *reinterpret_cast<const uint4 *>(hh + (int64_t)cc * roww + 4 * (v - cc * qpr))
                           : make_uint4(0u, 0u, 0u, 0u);
         }
