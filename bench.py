@@ -48,7 +48,7 @@ KERNEL_SOURCES = ["include/hk.h", "hash_top_kv_amd/csrc/hk_internal.h",
                   "hash_top_kv_amd/csrc/fused.hip", "hash_top_kv_amd/csrc/encode.hip",
                   "hash_top_kv_amd/csrc/evict.hip", "hash_top_kv_amd/csrc/exact.hip",
                   "hash_top_kv_amd/csrc/probe.hip", "hash_top_kv_amd/csrc/api.hip",
-                  "include/hk_probe.h"]
+                  "include/hk_probe.h", "hash_top_kv_amd/csrc/encode_core.h"]
 
 
 def _code_only(text: str) -> str:
@@ -371,6 +371,9 @@ def build_full_case(args, torch, hk, synth):
     def scan(i):
         st(i).scan(st(i).qcodes)
 
+    def scan_query(i):
+        st(i).scan_query(Qs[i % R])
+
     def rest(i):
         st(i).select_attend(Qs[i % R])
 
@@ -428,7 +431,10 @@ def build_full_case(args, torch, hk, synth):
                      if args.qheads else
                      "hk_encode_query + hk_retrieve_attend_varlen (lengths " +
                      ",".join(map(str, lengths)) + ")"
-                     if args.varlen else "hk_encode_query + hk_hamming_scan + hk_select_attend")}
+                     if args.varlen else
+                     "hk_hamming_scan_query (the scan hashes the query) + hk_select_attend"
+                     if args.workload in (0, 1) else
+                     "hk_encode_query + hk_hamming_scan + hk_select_attend")}
     if args.unfused:
         parts = [("decode_step", unfused, None)]
     elif args.varlen:
@@ -438,6 +444,10 @@ def build_full_case(args, torch, hk, synth):
                  ("retrieve_topk_qheads", q_ret, scan_bytes),
                  ("attend_qheads+window+merge", q_att,
                   wl.B * wl.Hq * (s0.keff + s0.n_win) * 2 * 128 * esz)]
+    elif args.workload in (0, 1):
+        # latency-bound: the scan hashes the query itself (hk_hamming_scan_query)
+        parts = [("encode_query+hamming_scan", scan_query, scan_bytes),
+                 ("select+attend", rest, gather_bytes)]
     else:
         parts = [("encode_query", enc, None), ("hamming_scan", scan, scan_bytes),
                  ("select+attend", rest, gather_bytes)]

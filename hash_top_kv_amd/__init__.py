@@ -44,6 +44,8 @@ _SIGNATURES = {
     "hk_retrieve_topk": (_I, [_P, _P, _I, _I, _I, _I64, _I64, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "hk_hamming_scan": (_I, [_P, _P, _I, _I, _I, _I64, _I64, _I, _I, _I, _P, _SZ, _P]),
     "hk_topk_select": (_I, [_I, _I, _I, _I64, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "hk_hamming_scan_query": (_I, [ctypes.POINTER(_Hash), _P, _I, _I, _I, _P, _I64, _I64, _I, _I,
+                                   _I, _P, _P, _SZ, _P]),
     "hk_window_indices": (_I, [_I64, _I, _I, _P, ctypes.POINTER(ctypes.c_int32), _P]),
     "hk_sparse_decode_workspace": (_SZ, [_I, _I, _I, _I, _I]),
     "hk_sparse_decode": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _I64, _P, _I, _F,
@@ -243,6 +245,24 @@ def hamming_scan(codes, qcodes, bits, n_ctx, n_sink, n_local, k, ws):
     _need(ws, "ws", dtype=torch.uint8)
     _check(lib().hk_hamming_scan(_ptr(codes), _ptr(qcodes), bits, B, Hkv, cap, n_ctx, n_sink,
                                  n_local, k, _ptr(ws), ws.numel(), _stream()), "hk_hamming_scan")
+
+
+def hamming_scan_query(h: Hash, q, codes, n_ctx, n_sink, n_local, k, ws, qcodes=None):
+    """hk_hamming_scan_query: hk_encode_query + hk_hamming_scan in one call (the scan
+    hashes the query itself when it is small).  Returns qcodes [B, Hkv, bits/32], the
+    codes the scan used."""
+    _need(q, "q", dtype=h.dtype)
+    _need(codes, "codes", dtype=torch.int32)
+    B, Hkv, cap, W = codes.shape
+    Hq = q.shape[1]
+    if qcodes is None:
+        qcodes = torch.empty((B, Hkv, h.words), dtype=torch.int32, device=q.device)
+    _need(qcodes, "qcodes", dtype=torch.int32, shape=(B, Hkv, h.words))
+    _need(ws, "ws", dtype=torch.uint8)
+    _check(lib().hk_hamming_scan_query(ctypes.byref(h.struct()), _ptr(q), B, Hq, Hkv, _ptr(codes),
+                                       cap, n_ctx, n_sink, n_local, k, _ptr(qcodes), _ptr(ws),
+                                       ws.numel(), _stream()), "hk_hamming_scan_query")
+    return qcodes
 
 
 def topk_select(bits, B, Hkv, n_ctx, n_sink, n_local, k, idx, count, ws):

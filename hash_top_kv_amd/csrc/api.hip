@@ -104,6 +104,7 @@ hk_status hk_encode_query(const hk_hash *h, const void *q, int B, int Hq, int Hk
   hk_status s = check_hash(h);
   if (s != HK_OK) return s;
   if (B < 0 || Hq < 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq < Hkv) return HK_ERR_INVALID_ARGUMENT;
+  if (Hq / Hkv > kMaxGroup) return HK_ERR_UNSUPPORTED;
   if ((int64_t)B * Hkv == 0) return HK_OK;
   if (!q || !qcodes) return HK_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16)) return HK_ERR_UNSUPPORTED;
@@ -127,6 +128,33 @@ hk_status hk_hamming_scan(const uint32_t *codes, const uint32_t *qcodes, int bit
   if (!aligned(codes, code_align(bits))) return HK_ERR_UNSUPPORTED;
   if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
   return from_hip(launch_hamming_scan(p, codes, qcodes, cap, ws, as_stream(stream)));
+}
+
+hk_status hk_hamming_scan_query(const hk_hash *h, const void *q, int B, int Hq, int Hkv,
+                                const uint32_t *codes, int64_t cap, int64_t n_ctx, int n_sink,
+                                int n_local, int k, uint32_t *qcodes, void *ws, size_t ws_bytes,
+                                void *stream) {
+  hk_status s = check_hash(h);
+  if (s != HK_OK) return s;
+  if (B < 0 || Hq < 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq < Hkv) return HK_ERR_INVALID_ARGUMENT;
+  if (Hq / Hkv > kMaxGroup) return HK_ERR_UNSUPPORTED;
+  s = check_retrieve(h->bits, B, Hkv, cap, n_ctx, n_sink, n_local, k);
+  if (s != HK_OK) return s;
+  if ((int64_t)B * Hkv == 0) return HK_OK;
+  if (!q || !qcodes) return HK_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16)) return HK_ERR_UNSUPPORTED;
+  const RetrievePlan p = plan_retrieve(h->bits, B, Hkv, n_ctx, n_sink, n_local, k);
+  if (p.S > 0) {
+    if (!codes || !ws) return HK_ERR_INVALID_ARGUMENT;
+    if (!aligned(codes, code_align(h->bits))) return HK_ERR_UNSUPPORTED;
+    if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
+  }
+  hipStream_t st = as_stream(stream);
+  if (scan_hashes_query(p))
+    return from_hip(launch_hamming_scan_query(p, *h, q, Hq, Hkv, codes, cap, qcodes, ws, st));
+  hipError_t e = launch_encode_query(*h, q, B, Hq, Hkv, qcodes, st);
+  if (e != hipSuccess || p.S == 0) return from_hip(e);
+  return from_hip(launch_hamming_scan(p, codes, qcodes, cap, ws, st));
 }
 
 hk_status hk_topk_select(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, int n_local,

@@ -27,60 +27,15 @@
 //
 // GELU's normal tail is one polynomial under one exponential (no reciprocal, no
 // branch), with absolute error below 4.6e-7.
-#include "hk_internal.h"
+#include "encode_core.h"
 
 namespace hk {
 namespace {
+using namespace enc;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// GELU(a) = a Phi(a) = max(a, 0) - x Phi(-x) with x = |a|, and Phi(-x) = 2^R(x): R is a
-// degree-5 polynomial fitted to log2 Phi(-x) (a weighted minimax fit that bounds the
-// absolute error of x 2^R(x), not of R).  Evaluated in fp32 (Horner, then one base-2
-// exponential), |GELU - exact| <= 4.6e-7 above fp32 rounding of the result, for every
-// finite a.  R's leading coefficient is negative, so R falls without bound: from x ~ 12
-// on, 2^R is below 2^-140 and GELU(a) = max(a, 0) to fp32 precision, with no clamp; for
-// very large x the Horner sum reaches -inf and the exponential 0 (never NaN).  Five
-// fused multiply-adds, one exponential, one integer max (a negative float, -0 included,
-// is a negative integer) and one fused multiply-add: eight vector instructions, one of
-// them transcendental.  The fit is written out, with its check, in gelu_fit.py.
-constexpr float kGelu0 = -1.000037722e+00f, kGelu1 = -1.150787181e+00f,
-                kGelu2 = -4.599939130e-01f, kGelu3 = -5.182606418e-02f,
-                kGelu4 = 7.084052480e-03f, kGelu5 = -4.732408280e-04f;
-__device__ __forceinline__ float gelu(float a) {
-  const float x = fabsf(a);
-  float r = fmaf(kGelu5, x, kGelu4);
-  r = fmaf(r, x, kGelu3);
-  r = fmaf(r, x, kGelu2);
-  r = fmaf(r, x, kGelu1);
-  r = fmaf(r, x, kGelu0);
-  const float g = __builtin_amdgcn_exp2f(r);
-  return fmaf(-x, g, __int_as_float(max(__float_as_int(a), 0)));   // max(a, 0)
-}
-
-// Round to the nearest bf16 (ties to even); finite inputs.
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-__device__ __forceinline__ float round_bf16(float f) {
-  return __uint_as_float(bf16_bits(f) << 16);
-}
-
-template <bool BF16>
-__device__ __forceinline__ float elem(const void *p, size_t i) {
-  if constexpr (BF16)
-    return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
-  else
-    return static_cast<const float *>(p)[i];
-}
-
-struct HashPtrs {
-  const void *R, *W1, *b1, *W2, *b2;
-};
 
 // ------------------------------------------------------------------ VALU kernel
 // fp32 keys: row r = (bh, t0 + j) of the key cache, one workgroup per key.

@@ -67,6 +67,14 @@ hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
                                int64_t n_local = 0, int64_t max_ctx = 0);
 // Per-query-head retrieval: p planned with B*Hq heads; each code is read once and
 // compared with the G query codes of its KV head.
+// The scan with the query hash computed inside it (one code per KV head from the group
+// mean of q, fp32 arithmetic; chunk 0 writes it to qcodes), for plans that
+// scan_hashes_query accepts: at most kScanQueryMaxBlocks workgroups, ordinary stores.
+constexpr int64_t kScanQueryMaxBlocks = 512;
+bool scan_hashes_query(const RetrievePlan &p);
+hipError_t launch_hamming_scan_query(const RetrievePlan &p, const hk_hash &h, const void *q,
+                                     int Hq, int Hkv, const uint32_t *codes, int64_t cap,
+                                     uint32_t *qcodes, void *ws, hipStream_t st);
 hipError_t launch_hamming_scan_qheads(const RetrievePlan &p, int G, const uint32_t *codes,
                                       const uint32_t *qcodes, int64_t cap, void *ws,
                                       hipStream_t st);

@@ -17,6 +17,7 @@
 //   topk_emit      re-reads the one-byte distances of a chunk and writes the selected
 //                  tokens (all with D < T, and the first `quota` with D == T in index
 //                  order) at their final positions, so the output is ascending.
+#include "encode_core.h"
 #include "select_core.h"
 
 namespace hk {
@@ -102,6 +103,77 @@ __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
       __builtin_nontemporal_store((uint8_t)d, st + 64 * i);
     else
       st[64 * i] = (uint8_t)d;
+  }
+  __syncthreads();
+  constexpr int NSB = BINS / 8;
+  uint32_t *out = hist_out + ((int64_t)bh * S + c) * (BINS + NSB);
+  if (t < BINS) {
+    uint32_t sum = 0;
+#pragma unroll
+    for (int w = 0; w < kScanThreads / 64; ++w) sum += hist[w][t];
+    out[t] = sum;
+  } else if (t < BINS + NSB) {
+    const int b0 = 8 * (t - BINS);
+    uint32_t sum = 0;
+#pragma unroll
+    for (int w = 0; w < kScanThreads / 64; ++w)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += hist[w][b0 + e];
+    out[t] = sum;
+  }
+}
+
+// As hamming_scan_kernel (ordinary distance stores, every sequence at full length), with
+// the query hash computed by each workgroup from the query rows itself (enc::
+// wg_query_code), which removes the query encoder's kernel and its dependent round
+// trip from a latency-bound step; chunk 0 of every head writes the code it used to
+// qcodes.  The code loads are issued first and land while the code is computed.
+template <int W, int LPT, bool BF16, int KIND>
+__global__ __launch_bounds__(kScanThreads) void hamming_scan_query_kernel(
+    const uint32_t *__restrict__ codes, int64_t cap, int64_t lo, int64_t C,
+    uint8_t *__restrict__ stash, int S, uint32_t *__restrict__ hist_out, enc::HashPtrs hp,
+    const void *__restrict__ q, int Hq, int Hkv, uint32_t *__restrict__ qcodes) {
+  constexpr int BINS = 32 * W;
+  constexpr int NBP = BINS + 4;
+  constexpr int CH = kScanThreads * LPT;
+  using CV = CodeVec<W>;
+  using V = typename CV::T;
+  __shared__ uint32_t hist[kScanThreads / 64][NBP];
+  __shared__ float xs[kHeadDim];
+  __shared__ float hid[kHidden];
+  __shared__ uint32_t qw[W];
+
+  const int c = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int64_t p0 = (int64_t)c * CH;
+  const int64_t pw = p0 + (int64_t)wave * (64 * LPT) + (t & 63);
+  const V *base = reinterpret_cast<const V *>(codes + ((int64_t)bh * cap + lo) * W);
+  V v[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int64_t p = pw + 64 * i;
+    v[i] = (p < C) ? __builtin_nontemporal_load(base + p) : CV::zero();
+  }
+  for (int i = t; i < (kScanThreads / 64) * NBP; i += kScanThreads) (&hist[0][0])[i] = 0u;
+  const int64_t b = bh / Hkv;
+  enc::wg_query_code<BF16, KIND, 32 * W>(hp, q, b, (int)(bh - b * Hkv), Hq, Hkv, xs, hid, qw);
+  uint32_t qq[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) qq[w] = qw[w];
+  if (c == 0 && t < W) qcodes[(int64_t)bh * W + t] = qw[t];
+
+  uint8_t *st = stash + (int64_t)bh * S * CH + pw;
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int64_t p = pw + 64 * i;
+    uint32_t d = 0xFFu;
+    if (p < C) {
+      d = CV::dist(v[i], qq);
+      atomicAdd(&hist[wave][d], 1u);
+    }
+    st[64 * i] = (uint8_t)d;
   }
   __syncthreads();
   constexpr int NSB = BINS / 8;
@@ -330,6 +402,42 @@ hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
     else HK_SCAN(2, 4);
   }
 #undef HK_SCAN
+  return hipGetLastError();
+}
+
+bool scan_hashes_query(const RetrievePlan &p) {
+  // Every scan workgroup reads the hash's weight rows (up to 128 KB for an MLP): worth a
+  // kernel boundary only while the workgroups are few.
+  return p.BH > 0 && p.S > 0 && (int64_t)p.BH * p.S * p.ch <= kStashNtBytes &&
+         (int64_t)p.BH * p.S <= kScanQueryMaxBlocks;
+}
+
+hipError_t launch_hamming_scan_query(const RetrievePlan &p, const hk_hash &h, const void *q,
+                                     int Hq, int Hkv, const uint32_t *codes, int64_t cap,
+                                     uint32_t *qcodes, void *ws, hipStream_t st) {
+  if (p.BH == 0 || p.S == 0) return hipSuccess;
+  uint8_t *w8 = static_cast<uint8_t *>(ws);
+  uint8_t *stash = w8 + p.off_stash;
+  uint32_t *hist = reinterpret_cast<uint32_t *>(w8 + p.off_hist);
+  const enc::HashPtrs hp{h.R, h.W1, h.b1, h.W2, h.b2};
+  const dim3 grid(p.S, p.BH), blk(kScanThreads);
+#define HK_SQ(WW, LL, BF, KK)                                                                 \
+  hipLaunchKernelGGL((hamming_scan_query_kernel<WW, LL, BF, KK>), grid, blk, 0, st, codes, cap, \
+                     p.lo, p.C, stash, p.S, hist, hp, q, Hq, Hkv, qcodes)
+#define HK_SQ_K(WW, LL, BF)                                                                   \
+  if (h.kind == HK_HASH_MLP) HK_SQ(WW, LL, BF, enc::kMlp);                                    \
+  else if (h.kind == HK_HASH_LSH) HK_SQ(WW, LL, BF, enc::kLsh);                               \
+  else if (WW == 4) HK_SQ(4, LL, BF, enc::kSign);
+#define HK_SQ_B(WW, LL)                                                                       \
+  if (h.dtype == HK_BF16) { HK_SQ_K(WW, LL, true) } else { HK_SQ_K(WW, LL, false) }
+  if (p.W == 4) {
+    if (p.lpt == 8) { HK_SQ_B(4, 8) } else { HK_SQ_B(4, 4) }
+  } else {
+    if (p.lpt == 8) { HK_SQ_B(2, 8) } else { HK_SQ_B(2, 4) }
+  }
+#undef HK_SQ_B
+#undef HK_SQ_K
+#undef HK_SQ
   return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-"""The GELU polynomial of the key and query encoders (csrc/encode.hip), written out.
+"""The GELU polynomial of the key and query encoders (csrc/encode_core.h), written out.
 
 GELU(a) = a Phi(a) = max(a, 0) - x Phi(-x) with x = |a|.  The encoders compute
 Phi(-x) = 2^R(x) with R a degree-5 polynomial in x, so one GELU costs five fused
@@ -11,7 +11,7 @@ with R's leading coefficient negative, so that R falls without bound and 2^R
 underflows to zero for large x (no clamp is needed).  The error is that of the GELU
 itself, not of R: where x Phi(-x) is tiny, R may be far off.
 
-    python hash_top_kv_amd/gelu_fit.py          # refit, and check the constants in encode.hip
+    python hash_top_kv_amd/gelu_fit.py          # refit, and check the constants in encode_core.h
 
 `check()` evaluates the constants exactly as the kernel does (fp32 Horner with fused
 multiply-adds, fp32 exponential and result) and returns the largest absolute error
@@ -25,11 +25,11 @@ import re
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-ENCODE = os.path.join(HERE, "csrc", "encode.hip")
+ENCODE = os.path.join(HERE, "csrc", "encode_core.h")
 
 
 def constants(path: str = ENCODE) -> np.ndarray:
-    """kGelu0 .. kGelu5 as written in encode.hip (float32)."""
+    """kGelu0 .. kGelu5 as written in encode_core.h (float32)."""
     text = open(path).read()
     c = [float(re.search(rf"kGelu{k}\s*=\s*([-+0-9.eE]+)f", text).group(1)) for k in range(6)]
     return np.array(c, dtype=np.float32)
@@ -107,4 +107,4 @@ if __name__ == "__main__":
     c, d = fit()
     print("fitted R:", ", ".join(f"{v:.9e}" for v in c), f"(bound on the grid {d:.2e})")
     print(f"fitted constants, fp32 kernel arithmetic: max error {check(np.float32(c)):.2e}")
-    print(f"constants in encode.hip: max error {check():.2e}")
+    print(f"constants in encode_core.h: max error {check():.2e}")

@@ -3,7 +3,8 @@
 Sequences the C entry points with preallocated buffers (no allocation per step, so a
 step can be captured in a HIP graph):
 
-    hk_encode_query -> hk_hamming_scan -> hk_select_attend   (fused; = hk_retrieve_attend)
+    hk_hamming_scan_query -> hk_select_attend   (fused: hk_encode_query + hk_retrieve_attend;
+                                                 a small scan hashes the query itself)
 or, through the separate calls (DecodeStep.unfused):
     hk_encode_query -> hk_retrieve_topk -> hk_sparse_decode (top-k list)
                     -> hk_sparse_decode (sink + local window) -> hk_lse_merge
@@ -20,7 +21,7 @@ import math
 import torch
 
 from . import (Hash, encode_query, evict_replace, evict_select, evict_workspace, hamming_scan,
-               lse_merge, retrieve_attend_varlen, retrieve_attend_workspace, retrieve_topk_qheads,
+               hamming_scan_query, lse_merge, retrieve_attend_varlen, retrieve_attend_workspace, retrieve_topk_qheads,
                retrieve_topk_workspace,
                select_attend, sparse_decode, sparse_decode_qheads, sparse_decode_workspace,
                window_indices, workspace, _check, _ptr, _stream, lib)
@@ -62,16 +63,22 @@ class DecodeStep:
 
     def __call__(self, q: torch.Tensor, qcodes: torch.Tensor | None = None):
         """Returns (o [B, Hq, d], lse [B, Hq]); with qcodes given the query is not hashed.
-        hk_encode_query, then hk_retrieve_attend (retrieval, attention over the selected
-        tokens and the window, merge)."""
+        hk_hamming_scan_query (the query hash and the scan; a small scan hashes the query
+        itself), then hk_select_attend (selection, attention over the selected tokens and
+        the window, merge)."""
         if qcodes is None:
-            qcodes = self.encode(q)
-        self.scan(qcodes)
+            self.scan_query(q)
+        else:
+            self.scan(qcodes)
         return self.select_attend(q)
 
     # The parts of a fused step, in order (hk_retrieve_attend = scan + select_attend).
     def encode(self, q):
         return encode_query(self.hash, q, self.Hkv, self.qcodes)
+
+    def scan_query(self, q):
+        return hamming_scan_query(self.hash, q, self.codes, self.n_ctx, self.n_sink, self.n_local,
+                                  self.k, self.ws_f, self.qcodes)
 
     def scan(self, qcodes):
         hamming_scan(self.codes, qcodes, self.bits, self.n_ctx, self.n_sink, self.n_local,

@@ -98,7 +98,8 @@ hk_status hk_encode_keys(const hk_hash *h, const void *k, int B, int Hkv, int64_
  * logit), computed in fp32 without rounding the mean.
  *   q       device [B][Hq][d], element type h->dtype.
  *   qcodes  device [B][Hkv][bits/32] uint32 (written).
- * Errors: Hq % Hkv != 0, NULL pointers -> INVALID_ARGUMENT. */
+ * Errors: Hq % Hkv != 0, NULL pointers -> INVALID_ARGUMENT; G = Hq / Hkv > 8 ->
+ * UNSUPPORTED. */
 hk_status hk_encode_query(const hk_hash *h, const void *q, int B, int Hq, int Hkv,
                           uint32_t *qcodes, void *stream);
 
@@ -133,6 +134,25 @@ hk_status hk_retrieve_topk(const uint32_t *codes, const uint32_t *qcodes, int bi
 hk_status hk_hamming_scan(const uint32_t *codes, const uint32_t *qcodes, int bits, int B,
                           int Hkv, int64_t cap, int64_t n_ctx, int n_sink, int n_local,
                           int k, void *ws, size_t ws_bytes, void *stream);
+/* hk_encode_query followed by hk_hamming_scan in one call: the query code of every
+ * (b, KV head) -- the code of the group mean of its G query rows, as hk_encode_query
+ * defines it -- and the scan of the cached codes against it.  For a small scan (at most
+ * 512 scan workgroups, see hk_retrieve_topk_workspace's plan) every scan workgroup
+ * computes its head's code itself in fp32 from q and the hash weights, which saves the
+ * encoder's kernel and its dependent round trip in a latency-bound step; larger scans
+ * run the two kernels.  fp32 and sign hashes give hk_encode_query's codes bit for bit;
+ * bf16 LSH and MLP hashes computed inside the scan use the fp32 arithmetic of the fp32
+ * encoder instead of the matrix cores, so a code bit can differ from hk_encode_query's
+ * only where the pre-sign value is within fp32 rounding of zero.
+ *   h, q, B, Hq, Hkv  as hk_encode_query; codes, cap, n_ctx, n_sink, n_local, k, ws,
+ *           ws_bytes as hk_hamming_scan (bits = h->bits).
+ *   qcodes  device [B][Hkv][bits/32] uint32 (written): the codes the scan used.
+ * A following hk_topk_select or hk_select_attend continues from ws as after
+ * hk_hamming_scan.  Errors: those of hk_encode_query and hk_hamming_scan. */
+hk_status hk_hamming_scan_query(const hk_hash *h, const void *q, int B, int Hq, int Hkv,
+                                const uint32_t *codes, int64_t cap, int64_t n_ctx, int n_sink,
+                                int n_local, int k, uint32_t *qcodes, void *ws, size_t ws_bytes,
+                                void *stream);
 hk_status hk_topk_select(int bits, int B, int Hkv, int64_t n_ctx, int n_sink, int n_local,
                          int k, int32_t *idx, int32_t *count, void *ws, size_t ws_bytes,
                          void *stream);

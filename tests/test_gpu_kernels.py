@@ -363,6 +363,71 @@ def test_encode_keys_append_one_token():
             compare_codes(got[b, g], ref, y)
 
 
+# (kind, bits, dtype, biases, G, N): small scans hash the query inside the scan; the
+# last case has more than 512 scan workgroups and runs the query encoder, then the scan.
+SCANQ_CASES = [
+    ("lsh", 128, "f32", False, 1, 4096), ("mlp", 128, "f32", True, 4, 5000),
+    ("mlp", 64, "f32", False, 8, 3000), ("sign", 128, "bf16", False, 3, 4000),
+    ("sign", 128, "f32", False, 2, 2500), ("lsh", 64, "bf16", False, 2, 6000),
+    ("lsh", 128, "bf16", False, 7, 3333), ("mlp", 128, "bf16", True, 4, 7000),
+    ("mlp", 64, "bf16", False, 5, 4100), ("mlp", 128, "bf16", False, 4, 300000),
+]
+
+
+@pytest.mark.parametrize("case", SCANQ_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_hamming_scan_query_matches_encode_then_scan(case):
+    """hk_hamming_scan_query against hk_encode_query + hk_hamming_scan on the same inputs:
+    fp32 and sign hashes (and every hash on the two-kernel path) give the same query codes
+    bit for bit and the same selection; bf16 LSH/MLP codes computed inside the scan agree
+    with the oracle outside the near-zero exemption, and the selection is the oracle's
+    top-k of the codes the scan reports."""
+    kind, bits, dtype, bias, G, N = case
+    say(f"hamming_scan_query {case}")
+    B, Hkv = 2, 2
+    wl = synth.scaled(synth.WORKLOADS[1], B=B, Hkv=Hkv, Hq=Hkv * G, N=N, dtype=dtype)
+    q = synth.to_device(synth.make_q(wl), dtype)
+    if kind == "sign":
+        hnp = {"kind": "sign", "bits": 128, "dtype": dtype}
+        h = hk.Hash("sign", 128, dtype=q.dtype)
+    else:
+        hnp = _hash_case(kind, bits, dtype, 11, bias=bias)
+        h = hk.Hash(kind, bits, **synth.hash_to_device(hnp))
+    rng = np.random.default_rng(3)
+    W = bits // 32
+    codes = codes_tensor(rng.integers(0, 2 ** 32, size=(B, Hkv, N, W), dtype=np.uint32))
+    n_sink, n_local, k = 4, 64, max(1, N // 100)
+    nbytes = hk.retrieve_topk_workspace(bits, B, Hkv, N, n_sink, n_local, k)
+    ws1, ws2 = hk.workspace(nbytes), hk.workspace(nbytes)
+    idx1 = torch.zeros((B, Hkv, k), dtype=torch.int32, device="cuda")
+    idx2 = torch.zeros_like(idx1)
+    cnt1 = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+    cnt2 = torch.zeros_like(cnt1)
+    qref = hk.encode_query(h, q, Hkv)
+    hk.hamming_scan(codes, qref, bits, N, n_sink, n_local, k, ws1)
+    hk.topk_select(bits, B, Hkv, N, n_sink, n_local, k, idx1, cnt1, ws1)
+    qc = hk.hamming_scan_query(h, q, codes, N, n_sink, n_local, k, ws2)
+    hk.topk_select(bits, B, Hkv, N, n_sink, n_local, k, idx2, cnt2, ws2)
+    torch.cuda.synchronize()
+    same = dtype == "f32" or kind == "sign" or N >= 300000
+    if same:
+        assert np.array_equal(np_u32(qc), np_u32(qref))
+        assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2)
+    else:
+        ref, y = oracle.encode_query(oracle.widen(synth.make_q(wl), dtype), oracle.prepare_hash(hnp), Hkv)
+        n = compare_codes(np_u32(qc), ref, y)
+        say(f"  exempt bits that differ from the oracle: {n}")
+        _check_all_selections(codes, qc, idx2, cnt2, N, n_sink, n_local, k)
+
+
+def _check_all_selections(codes, qcodes, idx, count, N, n_sink, n_local, k):
+    codes, qcodes = np_u32(codes), np_u32(qcodes)
+    idx, count = idx.cpu().numpy(), count.cpu().numpy()
+    for b in range(codes.shape[0]):
+        for g in range(codes.shape[1]):
+            want = oracle.select_topk(codes[b, g], qcodes[b, g], N, n_sink, n_local, k)
+            assert count[b, g] == want.size and np.array_equal(idx[b, g, :want.size], want), (b, g)
+
+
 def test_invalid_arguments_enqueue_nothing():
     c = torch.zeros((1, 1, 10, 4), dtype=torch.int32, device="cuda")
     q = torch.zeros((1, 1, 4), dtype=torch.int32, device="cuda")
