@@ -1,4 +1,4 @@
-"""The encoders' GELU polynomial (the constants compiled into csrc/encode.hip), checked
+"""The encoders' GELU polynomial (the constants compiled into csrc/encode_core.h), checked
 in the kernel's own fp32 arithmetic against GELU from the normal CDF in float64."""
 import numpy as np
 from scipy.special import ndtr
