@@ -196,11 +196,15 @@ def read_trace(tag: str, kernel: str):
     if vals.get("source_digest") != source_digest():
         return None
     try:
-        return {"summary": os.path.relpath(path, ROOT),
-                "back_to_back_avg_us": float(vals[f"{kernel}_back_to_back_avg_us"]),
-                "all_dispatches_avg_us": float(vals[f"{kernel}_all_avg_us"])}
+        out = {"summary": os.path.relpath(path, ROOT),
+               "back_to_back_avg_us": float(vals[f"{kernel}_back_to_back_avg_us"]),
+               "all_dispatches_avg_us": float(vals[f"{kernel}_all_avg_us"])}
     except (KeyError, ValueError):
         return None
+    for key in (f"{kernel}_back_to_back_median_gap_us", "read_probe_same_size_avg_us"):
+        if key in vals:
+            out[key.replace(f"{kernel}_", "")] = float(vals[key])
+    return out
 
 
 def read_traffic(name: str):
@@ -922,6 +926,15 @@ def main():
             if same:
                 stream["same_size_as_scan"] = same
                 roofline["frac_of_same_size_read"] = round(a / same["gbs"], 4)
+                # Under the profiler every dispatch starts on an idle GPU (the trace
+                # shows the gap between consecutive dispatches).  The plain read of the
+                # same bytes, timed here and in the trace, shows what that costs a
+                # kernel that is nothing but the read: the scan's offset is compared
+                # with it.
+                if tr and "read_probe_same_size_avg_us" in tr:
+                    tr["isolated_minus_events_us"] = {
+                        "hamming_scan": round(tr["back_to_back_avg_us"] - sc["us_per_launch"], 3),
+                        "same_size_read": round(tr["read_probe_same_size_avg_us"] - same["us_per_launch"], 3)}
     out = {"metric": METRIC, "value": round(ms_step * 1e3, 3), "unit": "us/step", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
            "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
