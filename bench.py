@@ -282,23 +282,26 @@ def build_retrieval_case(args, torch, hk, synth):
     count = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
     o = torch.empty((B, wl.Hq, 128), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, wl.Hq), dtype=torch.float32, device="cuda")
+    # One workspace per replica: the select+attend timed back to back then rotates over
+    # the R replicas' selections instead of replaying one.
     if args.unfused:
-        ws = hk.workspace(hk.retrieve_topk_workspace(128, B, Hkv, N, 0, 0, k))
+        wss = [hk.workspace(hk.retrieve_topk_workspace(128, B, Hkv, N, 0, 0, k)) for _ in range(R)]
         wsd = hk.workspace(hk.sparse_decode_workspace(B, wl.Hq, Hkv, k))
     else:
-        ws = hk.workspace(hk.retrieve_attend_workspace(128, B, wl.Hq, Hkv, N, 0, 0, k))
+        wss = [hk.workspace(hk.retrieve_attend_workspace(128, B, wl.Hq, Hkv, N, 0, 0, k))
+               for _ in range(R)]
 
     def scan(i):
         rp = reps[i % R]
-        hk.hamming_scan(rp["codes"], rp["qcodes"], 128, N, 0, 0, k, ws)
+        hk.hamming_scan(rp["codes"], rp["qcodes"], 128, N, 0, 0, k, wss[i % R])
 
     def rest(i):
         rp = reps[i % R]
         if args.unfused:
-            hk.topk_select(128, B, Hkv, N, 0, 0, k, idx, count, ws)
+            hk.topk_select(128, B, Hkv, N, 0, 0, k, idx, count, wss[i % R])
             hk.sparse_decode(rp["Q"], K, V, idx, k, count=count, o=o, lse=lse, ws=wsd)
         else:
-            hk.select_attend(128, rp["Q"], K, V, N, 0, 0, k, idx, count, o, lse, ws)
+            hk.select_attend(128, rp["Q"], K, V, N, 0, 0, k, idx, count, o, lse, wss[i % R])
 
     def check():
         scan(0)
