@@ -48,7 +48,8 @@ KERNEL_SOURCES = ["include/hk.h", "hash_top_kv_amd/csrc/hk_internal.h",
                   "hash_top_kv_amd/csrc/fused.hip", "hash_top_kv_amd/csrc/encode.hip",
                   "hash_top_kv_amd/csrc/evict.hip", "hash_top_kv_amd/csrc/exact.hip",
                   "hash_top_kv_amd/csrc/probe.hip", "hash_top_kv_amd/csrc/api.hip",
-                  "include/hk_probe.h", "hash_top_kv_amd/csrc/encode_core.h"]
+                  "include/hk_probe.h", "hash_top_kv_amd/csrc/encode_core.h",
+                  "hash_top_kv_amd/csrc/tiny.hip"]
 
 
 def _code_only(text: str) -> str:
@@ -378,8 +379,8 @@ def build_full_case(args, torch, hk, synth):
     def scan(i):
         st(i).scan(st(i).qcodes)
 
-    def scan_query(i):
-        st(i).scan_query(Qs[i % R])
+    def whole_step(i):
+        st(i)(Qs[i % R])
 
     def rest(i):
         st(i).select_attend(Qs[i % R])
@@ -439,7 +440,7 @@ def build_full_case(args, torch, hk, synth):
                      "hk_encode_query + hk_retrieve_attend_varlen (lengths " +
                      ",".join(map(str, lengths)) + ")"
                      if args.varlen else
-                     "hk_hamming_scan_query (the scan hashes the query) + hk_select_attend"
+                     "hk_decode_step (one call: query hash, retrieval, attention)"
                      if args.workload in (0, 1) else
                      "hk_encode_query + hk_hamming_scan + hk_select_attend")}
     if args.unfused:
@@ -452,9 +453,9 @@ def build_full_case(args, torch, hk, synth):
                  ("attend_qheads+window+merge", q_att,
                   wl.B * wl.Hq * (s0.keff + s0.n_win) * 2 * 128 * esz)]
     elif args.workload in (0, 1):
-        # latency-bound: the scan hashes the query itself (hk_hamming_scan_query)
-        parts = [("encode_query+hamming_scan", scan_query, scan_bytes),
-                 ("select+attend", rest, gather_bytes)]
+        # latency-bound: hk_decode_step (c0's single head runs in one workgroup; c1's scan
+        # hashes the query itself)
+        parts = [("decode_step", whole_step, None)]
     else:
         parts = [("encode_query", enc, None), ("hamming_scan", scan, scan_bytes),
                  ("select+attend", rest, gather_bytes)]

@@ -70,6 +70,8 @@ _SIGNATURES = {
                                 _I, _F, _P, _P, _P, _P, _P, _SZ, _P]),
     "hk_retrieve_attend_noalloc": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I64,
                                         _I, _I, _I, _F, _P, _P, _P, _P, _P]),
+    "hk_decode_step": (_I, [ctypes.POINTER(_Hash), _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I64, _I,
+                            _I, _I, _F, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -354,6 +356,39 @@ def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, o=None, lse=None):
 
 def retrieve_attend_workspace(bits, B, Hq, Hkv, n_ctx, n_sink, n_local, k) -> int:
     return int(lib().hk_retrieve_attend_workspace(bits, B, Hq, Hkv, n_ctx, n_sink, n_local, k))
+
+
+def decode_step(h: Hash, q, codes, k, v, n_ctx, n_sink, n_local, topk, scale=None, qcodes=None,
+                idx=None, count=None, o=None, lse=None, ws=None):
+    """hk_decode_step: the whole step from the query (query hash, Hamming top-k, attention
+    over the selected tokens and the window).  Returns (o [B, Hq, 128], lse [B, Hq], idx,
+    count, qcodes)."""
+    _need(codes, "codes", dtype=torch.int32)
+    B, Hkv, cap, W = codes.shape
+    _need(q, "q", dtype=h.dtype)
+    _need(k, "k", dtype=h.dtype)
+    _need(v, "v", dtype=h.dtype, shape=k.shape)
+    Hq, d = q.shape[1], q.shape[2]
+    if tuple(k.shape[:3]) != (B, Hkv, cap):
+        raise ValueError("k must be [B, Hkv, cap, d] like the codes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    wsb = retrieve_attend_workspace(h.bits, B, Hq, Hkv, n_ctx, n_sink, n_local, topk)
+    idx, count, ws = _topk_buffers(B, Hkv, topk, codes.device, idx, count, ws, wsb)
+    if qcodes is None:
+        qcodes = torch.empty((B, Hkv, h.words), dtype=torch.int32, device=q.device)
+    _need(qcodes, "qcodes", dtype=torch.int32, shape=(B, Hkv, h.words))
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(o, "o", dtype=torch.float32, shape=(B, Hq, d))
+    _need(lse, "lse", dtype=torch.float32, shape=(B, Hq))
+    _check(lib().hk_decode_step(ctypes.byref(h.struct()), _ptr(q), _ptr(codes), _ptr(k), _ptr(v),
+                                B, Hq, Hkv, d, cap, n_ctx, n_sink, n_local, topk, float(scale),
+                                _ptr(qcodes), _ptr(idx), _ptr(count), _ptr(o), _ptr(lse), _ptr(ws),
+                                ws.numel(), _stream()), "hk_decode_step")
+    return o, lse, idx, count, qcodes
 
 
 def retrieve_attend(codes, qcodes, bits, q, k, v, n_ctx, n_sink, n_local, topk, scale=None,

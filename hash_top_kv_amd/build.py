@@ -21,7 +21,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhk.so")
 PROBE_LIB = os.path.join(HERE, "libhk_probe.so")
 LIB_SOURCES = ["api.hip", "retrieve.hip", "attend.hip", "fused.hip", "encode.hip", "evict.hip",
-               "exact.hip"]
+               "exact.hip", "tiny.hip"]
 PROBE_SOURCES = ["probe.hip"]
 SOURCES = LIB_SOURCES + PROBE_SOURCES
 ARCH = "gfx950"
@@ -30,6 +30,7 @@ ARCH = "gfx950"
 # costs a copy out and back per tile and a larger register footprint.
 EXTRA_FLAGS = {"attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "tiny.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "encode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

@@ -221,6 +221,46 @@ hk_status hk_retrieve_attend(const uint32_t *codes, const uint32_t *qcodes, int 
   return from_hip(e);
 }
 
+hk_status hk_decode_step(const hk_hash *h, const void *q, const uint32_t *codes,
+                         const void *kc, const void *vc, int B, int Hq, int Hkv, int d,
+                         int64_t cap, int64_t n_ctx, int n_sink, int n_local, int topk,
+                         float scale, uint32_t *qcodes, int32_t *idx, int32_t *count, float *o,
+                         float *lse, void *ws, size_t ws_bytes, void *stream) {
+  hk_status s = check_hash(h);
+  if (s != HK_OK) return s;
+  const int bits = h->bits, dtype = h->dtype;
+  s = check_retrieve(bits, B, Hkv, cap, n_ctx, n_sink, n_local, topk);
+  if (s != HK_OK) return s;
+  if (d != kHeadDim) return HK_ERR_UNSUPPORTED;
+  if (Hkv <= 0 || Hq < Hkv || Hq % Hkv != 0) return HK_ERR_INVALID_ARGUMENT;
+  if (Hq / Hkv > kMaxGroup) return HK_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq == 0) return HK_OK;
+  const FusedPlan p = plan_fused(bits, B, Hq, Hkv, n_ctx, n_sink, n_local, topk);
+  if (!q || !qcodes || !count || !o || !lse || !ws) return HK_ERR_INVALID_ARGUMENT;
+  if (p.parts > 0 && (!kc || !vc)) return HK_ERR_INVALID_ARGUMENT;
+  if (p.r.S > 0 && !codes) return HK_ERR_INVALID_ARGUMENT;
+  if (p.r.keff > 0 && !idx) return HK_ERR_INVALID_ARGUMENT;
+  if (p.r.S > 0 && !aligned(codes, code_align(bits))) return HK_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16)) return HK_ERR_UNSUPPORTED;
+  if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
+  const hipStream_t st = as_stream(stream);
+  if (tiny_step_fits(B, Hq, Hkv, p.r.C, p.r.keff, p.n_win))
+    return from_hip(launch_tiny_step(*h, p.r, q, codes, kc, vc, B, Hq, Hkv, cap, topk, scale,
+                                     p.win_sinks, p.win_local0, p.n_win, qcodes, idx, count, o,
+                                     lse, st));
+  hipError_t e;
+  if (scan_hashes_query(p.r)) {
+    e = launch_hamming_scan_query(p.r, *h, q, Hq, Hkv, codes, cap, qcodes, ws, st);
+  } else {
+    e = launch_encode_query(*h, q, B, Hq, Hkv, qcodes, st);
+    if (e == hipSuccess) e = launch_hamming_scan(p.r, codes, qcodes, cap, ws, st);
+  }
+  if (e == hipSuccess)
+    e = launch_fused_attend(p, q, kc, vc, dtype, B, Hq, Hkv, cap, scale, topk, idx, count, o, lse,
+                            ws, st);
+  return from_hip(e);
+}
+
 hk_status hk_retrieve_attend_noalloc(const uint32_t *codes, const uint32_t *qcodes, int bits,
                                      const void *q, const void *kc, const void *vc, int dtype,
                                      int B, int Hq, int Hkv, int d, int64_t cap, int64_t n_ctx,

@@ -67,6 +67,18 @@ hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
                                int64_t n_local = 0, int64_t max_ctx = 0);
 // Per-query-head retrieval: p planned with B*Hq heads; each code is read once and
 // compared with the G query codes of its KV head.
+// The whole step of small heads in one workgroup each (tiny.hip): one query head per
+// KV head, at most kTinyC candidates and kTinyList selected + window rows per head, at
+// most kTinyMaxHeads heads.
+constexpr int kTinyC = 4096;
+constexpr int kTinyList = 1024;
+constexpr int kTinyMaxHeads = 256;
+bool tiny_step_fits(int B, int Hq, int Hkv, int64_t C, int keff, int n_win);
+hipError_t launch_tiny_step(const hk_hash &h, const RetrievePlan &p, const void *q,
+                            const uint32_t *codes, const void *kc, const void *vc, int B,
+                            int Hq, int Hkv, int64_t cap, int k, float scale, int win_sinks,
+                            int64_t win_local0, int n_win, uint32_t *qcodes, int32_t *idx,
+                            int32_t *count, float *o, float *lse, hipStream_t st);
 // The scan with the query hash computed inside it (one code per KV head from the group
 // mean of q, fp32 arithmetic; chunk 0 writes it to qcodes), for plans that
 // scan_hashes_query accepts: at most kScanQueryMaxBlocks workgroups, ordinary stores.

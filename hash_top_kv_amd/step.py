@@ -3,8 +3,8 @@
 Sequences the C entry points with preallocated buffers (no allocation per step, so a
 step can be captured in a HIP graph):
 
-    hk_hamming_scan_query -> hk_select_attend   (fused: hk_encode_query + hk_retrieve_attend;
-                                                 a small scan hashes the query itself)
+    hk_decode_step   (hk_encode_query + hk_retrieve_attend in one call: a small scan hashes the
+                      query itself, and small heads run the whole step in one workgroup)
 or, through the separate calls (DecodeStep.unfused):
     hk_encode_query -> hk_retrieve_topk -> hk_sparse_decode (top-k list)
                     -> hk_sparse_decode (sink + local window) -> hk_lse_merge
@@ -20,8 +20,8 @@ import math
 
 import torch
 
-from . import (Hash, encode_query, evict_replace, evict_select, evict_workspace, hamming_scan,
-               hamming_scan_query, lse_merge, retrieve_attend_varlen, retrieve_attend_workspace, retrieve_topk_qheads,
+from . import (Hash, decode_step, encode_query, evict_replace, evict_select, evict_workspace,
+               hamming_scan, hamming_scan_query, lse_merge, retrieve_attend_varlen, retrieve_attend_workspace, retrieve_topk_qheads,
                retrieve_topk_workspace,
                select_attend, sparse_decode, sparse_decode_qheads, sparse_decode_workspace,
                window_indices, workspace, _check, _ptr, _stream, lib)
@@ -62,14 +62,17 @@ class DecodeStep:
                                   self.ws_r.numel(), _stream()), "hk_retrieve_topk")
 
     def __call__(self, q: torch.Tensor, qcodes: torch.Tensor | None = None):
-        """Returns (o [B, Hq, d], lse [B, Hq]); with qcodes given the query is not hashed.
-        hk_hamming_scan_query (the query hash and the scan; a small scan hashes the query
-        itself), then hk_select_attend (selection, attention over the selected tokens and
-        the window, merge)."""
+        """Returns (o [B, Hq, d], lse [B, Hq]).  Without qcodes: hk_decode_step (the query
+        hash and the retrieval-attention step in one call; small heads run it in one
+        workgroup each).  With qcodes given the query is not hashed: hk_hamming_scan, then
+        hk_select_attend (selection, attention over the selected tokens and the window,
+        merge)."""
         if qcodes is None:
-            self.scan_query(q)
-        else:
-            self.scan(qcodes)
+            decode_step(self.hash, q, self.codes, self.K, self.V, self.n_ctx, self.n_sink,
+                        self.n_local, self.k, scale=self.scale, qcodes=self.qcodes, idx=self.idx,
+                        count=self.count, o=self.o, lse=self.lse, ws=self.ws_f)
+            return self.o, self.lse
+        self.scan(qcodes)
         return self.select_attend(q)
 
     # The parts of a fused step, in order (hk_retrieve_attend = scan + select_attend).

@@ -344,6 +344,30 @@ hk_status hk_sparse_decode_qheads(const void *q, const void *k, const void *v, i
                                   float scale, float *o, float *lse, void *ws, size_t ws_bytes,
                                   void *stream);
 
+/* The whole decode step of one layer from the query: hk_encode_query, then
+ * hk_retrieve_attend (Spotlight Attention: Approach; RetrievalAttention, atlas summary:
+ * Approach), with the query hash computed inside the scan where the scan is small
+ * (hk_hamming_scan_query).  Heads with one query head each (Hq == Hkv), at most 4096
+ * candidates and at most 1024 selected + window rows (and at most 256 heads) run the
+ * whole step in one workgroup per head: the query hash, the scan, the selection and
+ * one attention pass over the selected and window tokens together, with no partials
+ * and no merge.  Everything else runs the kernels of hk_hamming_scan_query and
+ * hk_select_attend.
+ *   h, q         as hk_encode_query; q, kc and vc have element type h->dtype.
+ *   codes, kc, vc, B, Hq, Hkv, d, cap, n_ctx, n_sink, n_local, topk, scale, idx, count,
+ *   o, lse, ws, ws_bytes  as hk_retrieve_attend (ws of hk_retrieve_attend_workspace(
+ *                h->bits, ...) bytes).
+ *   qcodes       device [B][Hkv][bits/32] uint32 (written): the query codes used, as
+ *                hk_hamming_scan_query reports them.
+ * idx and count are those of hk_retrieve_topk for these query codes; o and lse agree
+ * with hk_retrieve_attend's to rounding (the single pass sums the two parts in another
+ * order than the merge).  Errors: those of hk_encode_query and hk_retrieve_attend. */
+hk_status hk_decode_step(const hk_hash *h, const void *q, const uint32_t *codes,
+                         const void *kc, const void *vc, int B, int Hq, int Hkv, int d,
+                         int64_t cap, int64_t n_ctx, int n_sink, int n_local, int topk,
+                         float scale, uint32_t *qcodes, int32_t *idx, int32_t *count, float *o,
+                         float *lse, void *ws, size_t ws_bytes, void *stream);
+
 /* hk_retrieve_attend for a batch of sequences of their own lengths: sequence b holds
  * ctx_len[b] cached tokens (clamped to [0, max_ctx]); its candidates, budget
  * k_eff = min(topk, candidates), window and count follow its own length, exactly as a

@@ -419,6 +419,75 @@ def test_hamming_scan_query_matches_encode_then_scan(case):
         _check_all_selections(codes, qc, idx2, cnt2, N, n_sink, n_local, k)
 
 
+# (kind, bits, dtype, G, N, n_sink, n_local, k, codes): G = 1 heads of at most 4096
+# candidates run the whole step in one workgroup; the others (G > 1, or longer heads)
+# the scan-and-select+attend kernels.  codes: "rand", or "far" (every code the complement
+# of its head's query code: all at distance bits, so T = bits with the whole quota).
+DECODE_CASES = [
+    ("lsh", 128, "f32", 1, 4096, 4, 64, 82, "rand"), ("lsh", 128, "f32", 1, 1500, 0, 0, 1500, "rand"),
+    ("mlp", 128, "bf16", 1, 3000, 4, 64, 300, "rand"), ("lsh", 64, "bf16", 1, 4164, 4, 64, 1, "rand"),
+    ("sign", 128, "f32", 1, 900, 4, 64, 0, "rand"), ("lsh", 128, "f32", 1, 100, 4, 64, 50, "rand"),
+    ("mlp", 64, "f32", 1, 2500, 4, 64, 40, "far"), ("lsh", 128, "bf16", 1, 60, 4, 64, 10, "rand"),
+    ("mlp", 128, "bf16", 4, 6000, 4, 64, 120, "rand"), ("lsh", 128, "f32", 1, 9000, 4, 64, 90, "rand"),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_decode_step_matches_scan_then_select_attend(case):
+    """hk_decode_step against hk_hamming_scan_query + hk_select_attend on the same
+    inputs: the same query codes and the same idx and count bit for bit, o and lse
+    within the dtype's bound (the one-workgroup path attends over the selection and the
+    window in one pass, the other merges two partials)."""
+    kind, bits, dtype, G, N, n_sink, n_local, k, mode = case
+    say(f"decode_step {case}")
+    B, Hkv = 2, 2
+    wl = synth.scaled(synth.WORKLOADS[1], B=B, Hkv=Hkv, Hq=Hkv * G, N=N, dtype=dtype,
+                      n_sink=n_sink, n_local=n_local, k=k)
+    q = synth.to_device(synth.make_q(wl), dtype)
+    kv = synth.make_kv(wl)
+    K, V = synth.to_device(kv["K"], dtype), synth.to_device(kv["V"], dtype)
+    if kind == "sign":
+        h = hk.Hash("sign", 128, dtype=q.dtype)
+    else:
+        h = hk.Hash(kind, bits, **synth.hash_to_device(_hash_case(kind, bits, dtype, 12)))
+    W = bits // 32
+    qc0 = hk.encode_query(h, q, Hkv)
+    torch.cuda.synchronize()
+    if mode == "far":
+        codes_np = np.broadcast_to(~np_u32(qc0)[:, :, None, :], (B, Hkv, N, W)).copy()
+    else:
+        codes_np = np.random.default_rng(5).integers(0, 2 ** 32, size=(B, Hkv, N, W), dtype=np.uint32)
+    codes = codes_tensor(codes_np)
+    nb = hk.retrieve_attend_workspace(bits, B, Hkv * G, Hkv, N, n_sink, n_local, k)
+    ws1, ws2 = hk.workspace(nb), hk.workspace(nb)
+    kk = max(k, 1)
+    idx1 = torch.full((B, Hkv, kk), -7, dtype=torch.int32, device="cuda")
+    idx2 = idx1.clone()
+    cnt1 = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+    cnt2 = cnt1.clone()
+    o1 = torch.empty((B, Hkv * G, 128), dtype=torch.float32, device="cuda")
+    l1 = torch.empty((B, Hkv * G), dtype=torch.float32, device="cuda")
+    qc1 = hk.hamming_scan_query(h, q, codes, N, n_sink, n_local, k, ws1)
+    hk.select_attend(bits, q, K, V, N, n_sink, n_local, k, idx1, cnt1, o1, l1, ws1)
+    o2, l2, _, _, qc2 = hk.decode_step(h, q, codes, K, V, N, n_sink, n_local, k, idx=idx2,
+                                       count=cnt2, ws=ws2)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_u32(qc1), np_u32(qc2))
+    assert torch.equal(cnt1, cnt2)
+    keff = int(cnt1[0, 0])
+    assert torch.equal(idx1[..., :keff], idx2[..., :keff])
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    assert float((o1 - o2).abs().max()) <= tol
+    fin = torch.isfinite(l1)
+    assert torch.equal(fin, torch.isfinite(l2))
+    if bool(fin.any()):
+        assert float((l1[fin] - l2[fin]).abs().max()) <= tol
+    if mode == "far" and keff:
+        # every candidate at distance bits: the first k_eff candidates in index order
+        want = np.arange(n_sink, n_sink + keff)
+        assert np.array_equal(idx2[0, 0, :keff].cpu().numpy(), want)
+
+
 def _check_all_selections(codes, qcodes, idx, count, N, n_sink, n_local, k):
     codes, qcodes = np_u32(codes), np_u32(qcodes)
     idx, count = idx.cpu().numpy(), count.cpu().numpy()
