@@ -14,9 +14,10 @@
 //      block scan (HashEvict: Abstract; Spotlight Attention: Key results);
 //   5. selects with RunSelect over each thread's run of consecutive tokens, writing the
 //      ascending index list to idx and to an LDS list;
-//   6. appends the sink + local window to the LDS list (RetrievalAttention: the static
-//      tokens kept beside the retrieved ones) and attends over the whole list in one
-//      online softmax, storing the final o and lse (no partials, no merge).
+//   6. attends in one online softmax over the sink + local window (RetrievalAttention:
+//      the static tokens kept beside the retrieved ones; their rows are known at once, so
+//      the attention starts with them while the codes load) and then over the selection,
+//      storing the final o and lse (no partials, no merge).
 // The selection is the same set as hk_retrieve_topk's for the same code; attention over
 // the union in one pass equals the log-sum-exp merge of the two partial attentions up to
 // rounding (RetrievalAttention, atlas summary: Approach).
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kScanThreads) void tiny_step_kernel(
   using V = typename CV::T;
   __shared__ __attribute__((aligned(16))) uint8_t dist[kTinyC];
   __shared__ uint32_t hist[kScanThreads / 64][NBP];
-  __shared__ int32_t sel[kTinyList];
+  __shared__ int32_t sel[kTinyList];                   // the selected tokens
   __shared__ float xs[kHeadDim];
   __shared__ float hid[kHidden];
   __shared__ uint32_t qw[W];
@@ -66,6 +67,15 @@ __global__ __launch_bounds__(kScanThreads) void tiny_step_kernel(
     v[i] = p < C ? base[p] : CV::zero();
   }
   for (int i = t; i < (kScanThreads / 64) * NBP; i += kScanThreads) (&hist[0][0])[i] = 0u;
+  // The window's rows are known before the scan: the attention starts with them, so their
+  // gather overlaps the code loads and the query hash.
+  typename AttentionCore<BF16, 1>::type ga;
+  const int64_t row0 = b * Hq + hg;                    // G = 1: query head = KV head
+  const size_t head_row0 = (size_t)bh * (size_t)cap;
+  ga.init(q, row0, scale_log2);
+  ga.run_block(kc, vc, head_row0, n_win, [&](int r) {
+    return r < win_sinks ? r : (int32_t)(win_local0 + (r - win_sinks));
+  });
   enc::wg_query_code<BF16, KIND, BINS>(hp, q, b, hg, Hq, Hkv, xs, hid, qw);
   uint32_t qq[W];
 #pragma unroll
@@ -122,15 +132,8 @@ __global__ __launch_bounds__(kScanThreads) void tiny_step_kernel(
     });
   }
   if (t == 0) count[bh] = keff;
-  const int ns = keff > 0 ? keff : 0;
-  for (int r = t; r < n_win; r += kScanThreads)
-    sel[ns + r] = r < win_sinks ? r : (int32_t)(win_local0 + (r - win_sinks));
   __syncthreads();
-
-  typename AttentionCore<BF16, 1>::type ga;
-  const int64_t row0 = b * Hq + hg;                    // G = 1: query head = KV head
-  ga.init(q, row0, scale_log2);
-  ga.run_block(kc, vc, (size_t)bh * (size_t)cap, ns + n_win, [&](int rr) { return sel[rr]; });
+  ga.run_block(kc, vc, head_row0, keff > 0 ? keff : 0, [&](int rr) { return sel[rr]; });
   ga.combine_store(o + row0 * kHeadDim, lse + row0);
 }
 
