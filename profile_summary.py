@@ -27,7 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # short names of the decode path's kernels, by a substring of the kernel's name
-SHORT = [("hamming_scan_query_kernel", "hamming_scan"), ("hamming_scan_group_kernel", "hamming_scan_group"),
+SHORT = [("tiny_step_kernel", "decode_step_tiny"), ("hamming_scan_query_kernel", "hamming_scan"), ("hamming_scan_group_kernel", "hamming_scan_group"),
          ("hamming_scan_kernel", "hamming_scan"), ("emit_attend", "select_attend"),
          ("lse_merge", "lse_merge"), ("encode_query", "encode_query"),
          ("encode_keys_mfma", "encode_keys"), ("read_probe", "read_probe"),
@@ -70,7 +70,7 @@ def trace(args):
             runs.append(cur)
             cur = [x]
     runs.append(cur)
-    for k in ("hamming_scan", "select_attend", "lse_merge", "encode_query"):
+    for k in ("decode_step_tiny", "hamming_scan", "select_attend", "lse_merge", "encode_query"):
         d = [(e - s) / 1e3 for n, s, e, _ in seq if n == k]
         if d:
             vals[f"{k}_all_avg_us"] = f"{statistics.mean(d):.3f}"
