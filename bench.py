@@ -175,10 +175,13 @@ def same_rows_gather(torch, hkp, ctx, sel_fn, n_lists=8, reps=20):
 
 def profile_tag(args, info) -> str:
     """Workload tag of the committed profile summaries: w<n>, plus the hash for the
-    workload that runs two (w4_lsh64, w4_mlp128)."""
+    workload that runs two (w4_lsh64, w4_mlp128) and for sign codes (w3_sign128), and
+    _nowin without the window, so that a variant never reads another command's figures."""
     tag = f"w{args.workload}"
-    if args.workload == 4:
+    if args.workload == 4 or args.sign:
         tag += "_" + info.get("hash", "").replace("-", "")
+    if args.no_window:
+        tag += "_nowin"
     return tag
 
 
