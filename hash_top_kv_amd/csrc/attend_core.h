@@ -106,6 +106,78 @@ template <int G> struct QueryFrag<false, G> {
   }
 };
 
+// The last step of both cores' combine_store.  s_m, s_l and s_o hold each wavefront's
+// running maximum (base 2), normaliser and unnormalised output per query head.  For each
+// output element: M = max over wavefronts, weights 2^(m_w - M), o = (sum over
+// wavefronts, in order, of weight * o_w) / L, lse = (M + log2 L) ln 2; an empty set
+// gives o = 0, lse = -inf.  When the G x D outputs fit in one pass of the workgroup
+// (G <= 2) each thread takes one element; for larger groups each thread takes four
+// consecutive dims of one head, read from LDS and stored to out_o 16 bytes at a time
+// (element by element when out_o is not 16-byte aligned), which needs a quarter of the
+// passes and of the LDS reads of the weights.  Both give the same values.
+template <int G>
+__device__ __forceinline__ void combine_waves(const float (*s_m)[G], const float (*s_l)[G],
+                                              const float (*s_o)[G][kHeadDim], float *out_o,
+                                              float *out_lse) {
+  constexpr int D = kHeadDim, NW = kAttThreads / 64, V = D / 4;
+  if constexpr (G * D <= kAttThreads) {
+    const int i = threadIdx.x;
+    if (i < G * D) {
+      const int h = i / D, e = i - h * D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
+      float L = 0.f, O = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float f = __builtin_amdgcn_exp2f(s_m[w][h] - M);
+          L += s_l[w][h] * f;
+          O += s_o[w][h][e] * f;
+        }
+      }
+      const bool empty = !(L > 0.f);
+      out_o[(size_t)h * D + e] = empty ? 0.f : O / L;
+      if (e == 0) out_lse[h] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
+    }
+  } else {
+    const bool vec = (reinterpret_cast<uintptr_t>(out_o) & 15u) == 0;
+    for (int i = threadIdx.x; i < G * V; i += kAttThreads) {
+      const int h = i / V, e = 4 * (i - h * V);
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
+      float L = 0.f;
+      float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float f = __builtin_amdgcn_exp2f(s_m[w][h] - M);
+          L += s_l[w][h] * f;
+          const float4 v = *reinterpret_cast<const float4 *>(&s_o[w][h][e]);
+          O.x += v.x * f;
+          O.y += v.y * f;
+          O.z += v.z * f;
+          O.w += v.w * f;
+        }
+      }
+      const bool empty = !(L > 0.f);
+      const float4 r = empty ? make_float4(0.f, 0.f, 0.f, 0.f)
+                             : make_float4(O.x / L, O.y / L, O.z / L, O.w / L);
+      float *dst = out_o + (size_t)h * D + e;
+      if (vec) {
+        *reinterpret_cast<float4 *>(dst) = r;
+      } else {
+        dst[0] = r.x;
+        dst[1] = r.y;
+        dst[2] = r.z;
+        dst[3] = r.w;
+      }
+      if (e == 0) out_lse[h] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
+    }
+  }
+}
+
 // Per-lane state of the G query heads of one group.
 template <bool BF16, int G>
 struct GroupAttention {
@@ -226,7 +298,7 @@ struct GroupAttention {
   __device__ void combine_store(float *out_o, float *out_lse) {
     __shared__ float s_m[kAttThreads / 64][G];
     __shared__ float s_l[kAttThreads / 64][G];
-    __shared__ float s_o[kAttThreads / 64][G][D];
+    __shared__ __attribute__((aligned(16))) float s_o[kAttThreads / 64][G][D];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int col = lane & 15;
@@ -246,8 +318,9 @@ struct GroupAttention {
         acc[g][e] = a;
       }
       if (lane < 16) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s_o[wave][g][col * 8 + e] = acc[g][e];
+        float4 *dst = reinterpret_cast<float4 *>(&s_o[wave][g][col * 8]);
+        dst[0] = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
+        dst[1] = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
       }
       if (lane == 0) {
         s_m[wave][g] = mw;
@@ -255,24 +328,7 @@ struct GroupAttention {
       }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < G * D; i += kAttThreads) {
-      const int g = i / D, e = i - g * D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kAttThreads / 64; ++w) M = fmaxf(M, s_m[w][g]);
-      float L = 0.f, O = 0.f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < kAttThreads / 64; ++w) {
-          const float f = __builtin_amdgcn_exp2f(s_m[w][g] - M);
-          L += s_l[w][g] * f;
-          O += s_o[w][g][e] * f;
-        }
-      }
-      const bool empty = !(L > 0.f);
-      out_o[(size_t)g * D + e] = empty ? 0.f : O / L;
-      if (e == 0) out_lse[g] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
-    }
+    combine_waves<G>(s_m, s_l, s_o, out_o, out_lse);
   }
 };
 
@@ -403,7 +459,7 @@ struct GroupAttentionMfma {
   __device__ void combine_store(float *out_o, float *out_lse) {
     __shared__ float s_m[kAttThreads / 64][G];
     __shared__ float s_l[kAttThreads / 64][G];
-    __shared__ float s_o[kAttThreads / 64][G][D];
+    __shared__ __attribute__((aligned(16))) float s_o[kAttThreads / 64][G][D];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
@@ -417,29 +473,13 @@ struct GroupAttentionMfma {
     for (int j = 0; j < 4; ++j) {
       const int h = 4 * g + j;
       if (h < G) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) s_o[wave][h][8 * n + t] = o[t][j];
+        float4 *dst = reinterpret_cast<float4 *>(&s_o[wave][h][8 * n]);
+        dst[0] = make_float4(o[0][j], o[1][j], o[2][j], o[3][j]);
+        dst[1] = make_float4(o[4][j], o[5][j], o[6][j], o[7][j]);
       }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < G * D; i += kAttThreads) {
-      const int h = i / D, e = i - h * D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kAttThreads / 64; ++w) M = fmaxf(M, s_m[w][h]);
-      float L = 0.f, O = 0.f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < kAttThreads / 64; ++w) {
-          const float f = __builtin_amdgcn_exp2f(s_m[w][h] - M);
-          L += s_l[w][h] * f;
-          O += s_o[w][h][e] * f;
-        }
-      }
-      const bool empty = !(L > 0.f);
-      out_o[(size_t)h * D + e] = empty ? 0.f : O / L;
-      if (e == 0) out_lse[h] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
-    }
+    combine_waves<G>(s_m, s_l, s_o, out_o, out_lse);
   }
 };
 
