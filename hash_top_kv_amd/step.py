@@ -21,8 +21,8 @@ import math
 import torch
 
 from . import (Hash, decode_step, encode_query, evict_replace, evict_select, evict_workspace,
-               hamming_scan, hamming_scan_query, lse_merge, retrieve_attend_varlen, retrieve_attend_workspace, retrieve_topk_qheads,
-               retrieve_topk_workspace,
+               hamming_scan, hamming_scan_query, lse_merge, retrieve_attend_varlen,
+               retrieve_attend_workspace, retrieve_topk_qheads, retrieve_topk_workspace,
                select_attend, sparse_decode, sparse_decode_qheads, sparse_decode_workspace,
                window_indices, workspace, _check, _ptr, _stream, lib)
 

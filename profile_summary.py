@@ -1,4 +1,4 @@
-"""Short text summaries of rocprofv3 output for profiles/ (the figures bench.py and the design doc use).
+"""Short text summaries of rocprofv3 output for profiles/ (the figures that bench.py reads and the design notes quote).
 
     python profile_summary.py trace  --dir D --tag w2 --json BENCH_OUT --title T --cmd C
         kernel-trace summary -> profiles/decode_step_<tag>_kernel_trace.txt
