@@ -90,7 +90,28 @@ __device__ __forceinline__ void wg_query_code(const HashPtrs &hp, const void *__
       f[3] = __uint_as_float(v.w);
     }
   };
-  // Weight rows first, so that their round trip to memory overlaps the mean's.
+  // The group's query rows and the MLP biases are requested first, all at once, and the
+  // weight rows right after them: memory waits count requests in issue order, so the mean
+  // then waits for the query rows alone and its round trip overlaps the stream of weight
+  // rows.  None of these loads sits under a branch (the compiler waits for a load at the
+  // end of the branch that holds it): every thread reads column t mod D of the rows,
+  // rows past the group read the group's last row and add zero to the mean, and a
+  // missing bias reads a weight instead and is replaced by zero.  (Workgroups of 256
+  // threads: t indexes the 256 hidden units.)
+  const int G = Hq / Hkv;
+  float qv[kMaxGroup];
+  {
+    const size_t r0 = (size_t)(b * Hq + (int64_t)hg * G) * D + (size_t)(t & (D - 1));
+#pragma unroll
+    for (int j = 0; j < kMaxGroup; ++j) qv[j] = elem<BF16>(q, r0 + (size_t)(j < G ? j : G - 1) * D);
+  }
+  float bias1 = 0.f, bias2 = 0.f;
+  if constexpr (KIND == kMlp) {
+    const float v1 = elem<BF16>(hp.b1 ? hp.b1 : hp.W1, (size_t)t);
+    const float v2 = elem<BF16>(hp.b2 ? hp.b2 : hp.W2, (size_t)((t >> 1) & (BITS - 1)));
+    bias1 = hp.b1 ? v1 : 0.f;
+    bias2 = (hp.b2 && t < 2 * BITS) ? v2 : 0.f;
+  }
   const bool has1 = KIND == kMlp || (KIND == kLsh && t < BITS);
   uint4 w1[KIND == kSign ? 1 : V1];
   if (has1) {
@@ -106,15 +127,10 @@ __device__ __forceinline__ void wg_query_code(const HashPtrs &hp, const void *__
 #pragma unroll
     for (int i = 0; i < V2; ++i) w2[i] = p[i];
   }
-  const int G = Hq / Hkv;
   if (t < D) {
-    float v[kMaxGroup];
-#pragma unroll
-    for (int j = 0; j < kMaxGroup; ++j)
-      v[j] = j < G ? elem<BF16>(q, (size_t)((b * Hq + (int64_t)hg * G + j) * D + t)) : 0.f;
     float sum = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxGroup; ++j) sum += v[j];
+    for (int j = 0; j < kMaxGroup; ++j) sum += j < G ? qv[j] : 0.f;
     xs[t] = sum / (float)G;
   }
   __syncthreads();
@@ -133,7 +149,6 @@ __device__ __forceinline__ void wg_query_code(const HashPtrs &hp, const void *__
       }
     }
     if constexpr (KIND == kMlp) {
-      const float bias1 = hp.b1 ? elem<BF16>(hp.b1, t) : 0.f;
       float h = gelu(a + bias1);
       if constexpr (BF16) h = round_bf16(h);
       hid[t] = h;
@@ -149,7 +164,6 @@ __device__ __forceinline__ void wg_query_code(const HashPtrs &hp, const void *__
           for (int k = 0; k < EPV; ++k) y = fmaf(f[k], hid[e0 + i * EPV + k], y);
         }
       }
-      const float bias2 = (hp.b2 && t < 2 * BITS) ? elem<BF16>(hp.b2, t >> 1) : 0.f;
       y += __shfl_xor(y, 1) + bias2;
       m = __ballot(t < 2 * BITS && y > 0.f);
     } else {
