@@ -289,12 +289,18 @@ __global__ __launch_bounds__(1024) void encode_query_mfma_kernel(HashPtrs hp,
                   ? *reinterpret_cast<const uint32_t *>(q + (size_t)((b * Hq + hg * G + j) * D + e0))
                   : 0u;
   }
-  // The MLP's biases for this lane's columns, requested with the rest.
+  // The MLP's biases for this lane's columns, requested with the rest and without a
+  // branch (the compiler waits for a load at the end of the branch that holds it, which
+  // would put two round trips before the weights are requested): a missing bias reads a
+  // weight instead and is replaced by zero.  col < 256 = kHidden; the second product's
+  // columns are below BITS where they are used.
   float bias1 = 0.f, bias2 = 0.f;
   if constexpr (MLP) {
     const int col = 16 * wave + n;
-    if (has1 && hp.b1) bias1 = elem<true>(hp.b1, col);
-    if (has2 && hp.b2) bias2 = elem<true>(hp.b2, col);
+    const float v1 = elem<true>(hp.b1 ? hp.b1 : hp.W1, (size_t)col);
+    const float v2 = elem<true>(hp.b2 ? hp.b2 : hp.W2, (size_t)(col & (BITS - 1)));
+    bias1 = (has1 && hp.b1) ? v1 : 0.f;
+    bias2 = (has2 && hp.b2) ? v2 : 0.f;
   }
   {
     constexpr int C1 = N1 * D / 8, C2 = MLP ? BITS * NH / 8 : 0;   // 16-byte vectors
