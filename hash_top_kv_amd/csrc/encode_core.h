@@ -114,26 +114,70 @@ __device__ __forceinline__ void wg_query_code(const HashPtrs &hp, const void *__
   }
   const bool has1 = KIND == kMlp || (KIND == kLsh && t < BITS);
   uint4 w1[KIND == kSign ? 1 : V1];
-  if (has1) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(
-        static_cast<const char *>(KIND == kMlp ? hp.W1 : hp.R) + (size_t)t * D * ES);
-#pragma unroll
-    for (int i = 0; i < V1; ++i) w1[i] = p[i];
-  }
   uint4 w2[KIND == kMlp ? V2 : 1];
-  if (KIND == kMlp && t < 2 * BITS) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(
-        static_cast<const char *>(hp.W2) + ((size_t)(t >> 1) * NH + (NH / 2) * (t & 1)) * ES);
+  // bf16 MLP weights are copied into LDS by direct-to-LDS 16-byte loads, each wavefront
+  // instruction moving 64 consecutive vectors of a padded row layout (rows of D + 8 and
+  // NH + 8 elements, against bank conflicts; a pad slot reads its row's last vector
+  // again), and each thread then reads its own row from LDS.  Reading the rows straight
+  // from memory (every load instruction touching 64 rows) keeps one CU's load path busy
+  // several times longer, and these loads hold no registers while in flight.  The
+  // products are the same either way.
+  constexpr bool kStage = BF16 && KIND == kMlp;
+  constexpr int R1 = D / 8 + 1, R2 = NH / 8 + 1;     // padded row lengths in 16-byte vectors
+  if constexpr (kStage) {
+    __shared__ __attribute__((aligned(16))) uint4 w1s[NH * R1];
+    __shared__ __attribute__((aligned(16))) uint4 w2s[BITS * R2];
+    typedef const __attribute__((address_space(1))) void *gvp;
+    typedef __attribute__((address_space(3))) void *lvp;
+    const uint4 *s1 = static_cast<const uint4 *>(hp.W1);
+    const uint4 *s2 = static_cast<const uint4 *>(hp.W2);
+    constexpr int N1 = NH * R1 / 64, N2 = BITS * R2 / 64;   // instructions (64 vectors each)
+    static_assert(NH * R1 % 64 == 0 && BITS * R2 % 64 == 0, "whole instructions");
+    for (int k = wave; k < N1; k += 4) {
+      const int v = 64 * k + lane, row = v / R1, pc = v - row * R1;
+      __builtin_amdgcn_global_load_lds((gvp)(s1 + row * (D / 8) + (pc < D / 8 ? pc : D / 8 - 1)),
+                                       (lvp)&w1s[64 * k], 16, 0, 0);
+    }
+    for (int k = wave; k < N2; k += 4) {
+      const int v = 64 * k + lane, row = v / R2, pc = v - row * R2;
+      __builtin_amdgcn_global_load_lds((gvp)(s2 + row * (NH / 8) + (pc < NH / 8 ? pc : NH / 8 - 1)),
+                                       (lvp)&w2s[64 * k], 16, 0, 0);
+    }
+    if (t < D) {
+      float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < V2; ++i) w2[i] = p[i];
-  }
-  if (t < D) {
-    float sum = 0.f;
+      for (int j = 0; j < kMaxGroup; ++j) sum += j < G ? qv[j] : 0.f;
+      xs[t] = sum / (float)G;
+    }
+    __builtin_amdgcn_s_waitcnt(0);             // this wavefront's copies have landed
+    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kMaxGroup; ++j) sum += j < G ? qv[j] : 0.f;
-    xs[t] = sum / (float)G;
+    for (int i = 0; i < V1; ++i) w1[i] = w1s[t * R1 + i];
+    if (t < 2 * BITS) {
+#pragma unroll
+      for (int i = 0; i < V2; ++i) w2[i] = w2s[(t >> 1) * R2 + (NH / 16) * (t & 1) + i];
+    }
+  } else {
+    if (has1) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(
+          static_cast<const char *>(KIND == kMlp ? hp.W1 : hp.R) + (size_t)t * D * ES);
+#pragma unroll
+      for (int i = 0; i < V1; ++i) w1[i] = p[i];
+    }
+    if (KIND == kMlp && t < 2 * BITS) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(
+          static_cast<const char *>(hp.W2) + ((size_t)(t >> 1) * NH + (NH / 2) * (t & 1)) * ES);
+#pragma unroll
+      for (int i = 0; i < V2; ++i) w2[i] = p[i];
+    }
+    if (t < D) {
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < kMaxGroup; ++j) sum += j < G ? qv[j] : 0.f;
+      xs[t] = sum / (float)G;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   uint64_t m = 0;
   if constexpr (KIND == kSign) {
     m = __ballot(t < BITS && xs[t < D ? t : 0] > 0.f);
