@@ -240,17 +240,6 @@ constexpr int kQTile = 16;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ bf16x8 split_bf16(const float (&x)[8], float (&rest)[8]) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t b = bf16_bits(x[i]);
-    r[i] = __builtin_bit_cast(__bf16, (uint16_t)b);
-    rest[i] = x[i] - __uint_as_float(b << 16);           // exact
-  }
-  return r;
-}
-
 template <bool MLP, int BITS>
 __global__ __launch_bounds__(1024) void encode_query_mfma_kernel(HashPtrs hp,
                                                                  const uint16_t *__restrict__ q,
@@ -267,7 +256,12 @@ __global__ __launch_bounds__(1024) void encode_query_mfma_kernel(HashPtrs hp,
   constexpr int P1 = D + 8, P2 = NH + 8;
   __shared__ __attribute__((aligned(16))) uint16_t w1s[N1 * P1];
   __shared__ __attribute__((aligned(16))) uint16_t w2s[MLP ? BITS * P2 : 8];
-  __shared__ float xs[kQTile][D];
+  // The group means as three bf16 parts (x = p0 + p1 + p2 exactly), split once per
+  // element by the thread that sums it and read by every wavefront as its A fragments
+  // (splitting in each wavefront repeated the same work sixteen times).  Rows padded by
+  // 16 bytes.
+  constexpr int PX = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t xb[3][kQTile][PX];
   __shared__ __attribute__((aligned(16))) uint16_t hs[MLP ? kQTile : 1][MLP ? P2 : 8];
   __shared__ uint32_t words[kQTile][W];
   const int64_t r0 = (int64_t)blockIdx.x * kQTile;
@@ -346,8 +340,14 @@ __global__ __launch_bounds__(1024) void encode_query_mfma_kernel(HashPtrs hp,
       acc0 = acc0 / (float)G;
       acc1 = acc1 / (float)G;
     }
-    xs[rr][e0] = acc0;
-    xs[rr][e0 + 1] = acc1;
+    float x0 = acc0, x1 = acc1;
+#pragma unroll
+    for (int part = 0; part < 3; ++part) {
+      const uint32_t b0 = bf16_bits(x0), b1 = bf16_bits(x1);
+      *reinterpret_cast<uint32_t *>(&xb[part][rr][e0]) = b0 | (b1 << 16);
+      x0 -= __uint_as_float(b0 << 16);                 // exact
+      x1 -= __uint_as_float(b1 << 16);
+    }
   }
   __syncthreads();
   f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -357,10 +357,9 @@ __global__ __launch_bounds__(1024) void encode_query_mfma_kernel(HashPtrs hp,
     const int col = 16 * wave + n;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      float x[8], r1[8], r2[8], r3[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = xs[n][32 * ks + 8 * g + i];
-      const bf16x8 p0 = split_bf16(x, r1), p1 = split_bf16(r1, r2), p2 = split_bf16(r2, r3);
+      const bf16x8 p0 = *reinterpret_cast<const bf16x8 *>(&xb[0][n][32 * ks + 8 * g]);
+      const bf16x8 p1 = *reinterpret_cast<const bf16x8 *>(&xb[1][n][32 * ks + 8 * g]);
+      const bf16x8 p2 = *reinterpret_cast<const bf16x8 *>(&xb[2][n][32 * ks + 8 * g]);
       const bf16x8 bw = *reinterpret_cast<const bf16x8 *>(&w1s[col * P1 + 32 * ks + 8 * g]);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p0, bw, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p1, bw, acc, 0, 0, 0);
