@@ -75,6 +75,15 @@ def trace(args):
         if d:
             vals[f"{k}_all_avg_us"] = f"{statistics.mean(d):.3f}"
             vals[f"{k}_all_dispatches"] = str(len(d))
+    # dispatches that start within 1 us of the previous dispatch's end (graph replays):
+    # launched while the GPU was still busy, as in back-to-back execution without the
+    # profiler, so they are the ones to set beside back-to-back event timing
+    for k in ("hamming_scan", "select_attend", "lse_merge"):
+        d = [(seq[i][2] - seq[i][1]) / 1e3 for i in range(1, len(seq))
+             if seq[i][0] == k and seq[i][1] - seq[i - 1][2] < 1000]
+        if d:
+            vals[f"{k}_tight_avg_us"] = f"{statistics.mean(d):.3f}"
+            vals[f"{k}_tight_dispatches"] = str(len(d))
     long = [r for r in runs if r[0][0] == "hamming_scan" and len(r) >= 20]
     if long:
         d = [(e - s) / 1e3 for r in long for _, s, e, _ in r]
@@ -108,6 +117,8 @@ NOTES_TRACE = [
     "and the read probe over exactly the scan's bytes; under the profiler consecutive",
     "dispatches are separated by the gap given below, so each one starts on an idle GPU.",
     "*_all_*: every dispatch of the kernel (the step loop, the graph replays, the separate timings).",
+    "*_tight_*: the dispatches that start within 1 us of the previous dispatch's end (graph replays),",
+    "as launches run back to back without the profiler; bench.py's event timing is compared with these.",
 ]
 
 
