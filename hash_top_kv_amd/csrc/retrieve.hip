@@ -14,7 +14,7 @@
 //                  threshold T = min{t : #(D <= t) >= k_eff} and the tie quota
 //                  k_eff - #(D < T), and an exclusive prefix over chunks of the counts
 //                  below and at T.  No sort is needed: the histogram select replaces it.
-//   topk_emit      re-reads the one-byte distances of a chunk and writes the selected
+//   topk_emit      re-reads the one-byte distances of a group of chunks and writes the selected
 //                  tokens (all with D < T, and the first `quota` with D == T in index
 //                  order) at their final positions, so the output is ascending.
 #include "encode_core.h"
@@ -210,30 +210,59 @@ __global__ __launch_bounds__(kThrThreads) void topk_threshold_kernel(
   }
 }
 
-// grid (S, BH): chunk c of head bh, thread t its tokens [t*LPT, (t+1)*LPT).
-template <int LPT>
+// grid (ceil(S / CPE), BH): group g of head bh covers chunks [g*CPE, min(S, (g+1)*CPE)),
+// one run of the head's distance bytes; thread t takes its tokens [t*TPT, (t+1)*TPT) with
+// TPT = CPE*LPT.  The group's counts below / at T before it are its first chunk's meta,
+// and its own counts follow from its last chunk's.
+template <int LPT, int CPE>
 __global__ __launch_bounds__(kScanThreads) void topk_emit_kernel(
     const uint8_t *__restrict__ stash, const int4 *__restrict__ meta,
     const int2 *__restrict__ params, int S, int64_t lo, int k, int32_t *__restrict__ idx) {
   constexpr int CH = kScanThreads * LPT;
+  constexpr int TPT = CPE * LPT;
   __shared__ uint32_t lds[kScanThreads / 64];
-  const int c = blockIdx.x;
+  const int c0 = blockIdx.x * CPE;
+  const int c1 = min(S, c0 + CPE);
   const int bh = blockIdx.y;
   const int t = threadIdx.x;
   // Issue every load of the block before branching on any of them.
   const int2 pr = params[bh];
-  const int4 mt = meta[(int64_t)bh * S + c];
-  uint32_t w[LPT / 4];
-  load_run<LPT>(stash + ((int64_t)bh * S + c) * CH, (int64_t)t * LPT, true, w);
+  const int4 mf = meta[(int64_t)bh * S + c0];
+  const int4 ml = meta[(int64_t)bh * S + c1 - 1];
+  uint32_t w[TPT / 4];
+  load_run<TPT>(stash + ((int64_t)bh * S + c0) * CH, (int64_t)t * TPT,
+                (int64_t)t * TPT < (int64_t)(c1 - c0) * CH, w);
   const int T = pr.x;
   const int quota = pr.y;
-  const int ties = quota - mt.y;
-  if (T < 0 || mt.z + (ties <= 0 ? 0 : (ties < mt.w ? ties : mt.w)) == 0) return;
-  RunSelect<LPT> rs;
-  rs.build(w, T, quota, mt.x, mt.y, lds);
+  const int lt = ml.x + ml.z - mf.x;           // the group's tokens below T
+  const int eq = ml.y + ml.w - mf.y;           // and at T
+  const int ties = quota - mf.y;
+  if (T < 0 || lt + (ties <= 0 ? 0 : (ties < eq ? ties : eq)) == 0) return;
+  RunSelect<TPT> rs;
+  rs.build(w, T, quota, mf.x, mf.y, lds);
   int32_t *out = idx + (int64_t)bh * k + rs.first;
-  const int32_t tok0 = (int32_t)(lo + (int64_t)c * CH) + LPT * t;
+  const int32_t tok0 = (int32_t)(lo + (int64_t)c0 * CH) + TPT * t;
   rs.emit(0, rs.total, [&](int pos, int off) { out[pos] = tok0 + off; });
+}
+
+// Chunks per emit workgroup: the fewest (a power of two, at most 8) with which the grid
+// fits in one round of resident workgroups (8 per CU).  One chunk per workgroup leaves
+// the emit a chain of short rounds on many chunks (16384 chunks of the 112 query heads of
+// 4 sequences x 262144 tokens: seven rounds), each paying a load round trip and a scan.
+constexpr int64_t kEmitResident = 2048;
+template <int LPT>
+void emit_launch(const RetrievePlan &p, const uint8_t *stash, const int4 *meta,
+                 const int2 *params, int k, int32_t *idx, hipStream_t st) {
+  int cpe = 1;
+  while (cpe < 8 && (int64_t)((p.S + cpe - 1) / cpe) * p.BH > kEmitResident) cpe *= 2;
+  const dim3 grid((unsigned)((p.S + cpe - 1) / cpe), (unsigned)p.BH), blk(kScanThreads);
+#define HK_EMIT(CC)                                                                          \
+  case CC:                                                                                   \
+    hipLaunchKernelGGL((topk_emit_kernel<LPT, CC>), grid, blk, 0, st, stash, meta, params,  \
+                       p.S, p.lo, k, idx);                                                   \
+    break;
+  switch (cpe) { HK_EMIT(1) HK_EMIT(2) HK_EMIT(4) HK_EMIT(8) default: break; }
+#undef HK_EMIT
 }
 
 __global__ void window_indices_kernel(int32_t n_sinks, int64_t local0, int32_t n,
@@ -485,11 +514,9 @@ hipError_t launch_topk_select(const RetrievePlan &p, int k, int32_t *idx, int32_
   const int4 *meta = reinterpret_cast<const int4 *>(w8 + p.off_meta);
   const int2 *params = reinterpret_cast<const int2 *>(w8 + p.off_params);
   if (p.lpt == 8)
-    hipLaunchKernelGGL((topk_emit_kernel<8>), dim3(p.S, p.BH), dim3(kScanThreads), 0, st,
-                       stash, meta, params, p.S, p.lo, k, idx);
+    emit_launch<8>(p, stash, meta, params, k, idx, st);
   else
-    hipLaunchKernelGGL((topk_emit_kernel<4>), dim3(p.S, p.BH), dim3(kScanThreads), 0, st,
-                       stash, meta, params, p.S, p.lo, k, idx);
+    emit_launch<4>(p, stash, meta, params, k, idx, st);
   return hipGetLastError();
 }
 

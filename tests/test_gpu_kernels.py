@@ -45,6 +45,9 @@ RETRIEVE_CASES = [
     (128, 1, 8, 540000, 0, 0, 1024, 9),     # > 256 chunks per head (second threshold
                                             # window for 128-bit codes), heavy ties
     (64, 1, 2, 1100000, 0, 0, 500, 0),      # > 512 chunks per head (64-bit codes)
+    (64, 16, 8, 70000, 4, 64, 700, 0),      # 4480 chunks: 4 chunks per emit workgroup,
+                                            # the last group of each head 3 chunks
+    (64, 32, 8, 70000, 0, 0, 1400, 5),      # 8960 chunks: 8 per emit workgroup, ties
 ]
 
 
