@@ -150,7 +150,7 @@ hk_status hk_hamming_scan_query(const hk_hash *h, const void *q, int B, int Hq, 
     if (ws_bytes < p.total) return HK_ERR_WORKSPACE_TOO_SMALL;
   }
   hipStream_t st = as_stream(stream);
-  if (scan_hashes_query(p))
+  if (scan_hashes_query(p, *h))
     return from_hip(launch_hamming_scan_query(p, *h, q, Hq, Hkv, codes, cap, qcodes, ws, st));
   hipError_t e = launch_encode_query(*h, q, B, Hq, Hkv, qcodes, st);
   if (e != hipSuccess || p.S == 0) return from_hip(e);
@@ -249,7 +249,7 @@ hk_status hk_decode_step(const hk_hash *h, const void *q, const uint32_t *codes,
                                      p.win_sinks, p.win_local0, p.n_win, qcodes, idx, count, o,
                                      lse, st));
   hipError_t e;
-  if (scan_hashes_query(p.r)) {
+  if (scan_hashes_query(p.r, *h)) {
     e = launch_hamming_scan_query(p.r, *h, q, Hq, Hkv, codes, cap, qcodes, ws, st);
   } else {
     e = launch_encode_query(*h, q, B, Hq, Hkv, qcodes, st);

@@ -81,9 +81,10 @@ hipError_t launch_tiny_step(const hk_hash &h, const RetrievePlan &p, const void 
                             int32_t *count, float *o, float *lse, hipStream_t st);
 // The scan with the query hash computed inside it (one code per KV head from the group
 // mean of q, fp32 arithmetic; chunk 0 writes it to qcodes), for plans that
-// scan_hashes_query accepts: at most kScanQueryMaxBlocks workgroups, ordinary stores.
+// scan_hashes_query accepts: sign codes, and hashes with weights at most
+// kScanQueryMaxBlocks workgroups with ordinary stores.
 constexpr int64_t kScanQueryMaxBlocks = 512;
-bool scan_hashes_query(const RetrievePlan &p);
+bool scan_hashes_query(const RetrievePlan &p, const hk_hash &h);
 hipError_t launch_hamming_scan_query(const RetrievePlan &p, const hk_hash &h, const void *q,
                                      int Hq, int Hkv, const uint32_t *codes, int64_t cap,
                                      uint32_t *qcodes, void *ws, hipStream_t st);

@@ -458,11 +458,16 @@ hipError_t launch_hamming_scan(const RetrievePlan &p, const uint32_t *codes,
   return hipGetLastError();
 }
 
-bool scan_hashes_query(const RetrievePlan &p) {
-  // Every scan workgroup reads the hash's weight rows (up to 128 KB for an MLP): worth a
-  // kernel boundary only while the workgroups are few.
-  return p.BH > 0 && p.S > 0 && (int64_t)p.BH * p.S * p.ch <= kStashNtBytes &&
-         (int64_t)p.BH * p.S <= kScanQueryMaxBlocks;
+bool scan_hashes_query(const RetrievePlan &p, const hk_hash &h) {
+  if (p.BH == 0 || p.S == 0) return false;
+  // Sign codes need no weights: every scan workgroup only averages its group's query
+  // rows, which costs less than the query encoder's kernel and its boundary (4 x 262144
+  // tokens, 4 KV heads: 35.1 against 38.4 us per step).
+  if (h.kind == HK_HASH_SIGN) return true;
+  // Every scan workgroup reads the hash's weight rows (128 KB for a bf16 MLP, 16 KB for
+  // bf16 LSH-64): worth a kernel boundary only while the workgroups are few (on the same
+  // workload LSH-64 in 2048 workgroups took 35.8 against 33.4 us per step).
+  return (int64_t)p.BH * p.S * p.ch <= kStashNtBytes && (int64_t)p.BH * p.S <= kScanQueryMaxBlocks;
 }
 
 hipError_t launch_hamming_scan_query(const RetrievePlan &p, const hk_hash &h, const void *q,
