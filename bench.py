@@ -788,11 +788,11 @@ def main():
         return
     check()
 
-    whole = ctx.get("step")
+    one_call = ctx.get("step")
 
     def step(i):
-        if whole is not None:
-            whole(i)
+        if one_call is not None:
+            one_call(i)
             return
         for _, fn, _ in parts:
             fn(i)
