@@ -46,8 +46,9 @@ constexpr int64_t kStashNtBytes = 8 << 20;
 // workgroup one chunk (Sx = S): four chunks per workgroup, one round of 2048 workgroups
 // on 16 x 8 heads of 131072 tokens, measured 51.9 us against 47.1 with a workgroup per
 // chunk, while this form of the kernel at one chunk per workgroup measured 1.5-1.7%
-// faster than the earlier straight-line one (c2 12.12 against 12.32 us, 67.1 MB; c3
-// 46.9 against 47.1), with the same loads in the same order.
+// faster than the earlier straight-line one (8 heads x 524288 128-bit codes: 12.12
+// against 12.32 us; 16 x 8 heads of 131072: 46.9 against 47.1), with the same loads in
+// the same order.
 template <int W, int LPT, bool NT_STASH>
 __global__ __launch_bounds__(kScanThreads) void hamming_scan_kernel(
     const uint32_t *__restrict__ codes, const uint32_t *__restrict__ qcodes,
